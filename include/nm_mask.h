@@ -1,0 +1,157 @@
+/*
+ * nm_mask.h -- C ABI of the MI355X (gfx950) library for learnable N:M semi-structured sparsity:
+ * the differentiable Gumbel-softmax mask layer, its backward pass to the logits, hard-mask
+ * extraction and the compressed N:M storage format.
+ *
+ * Method (MaskLLM project page, "MaskLLM: Learnable Semi-Structured Sparsity for Large Language
+ * Models", Fig. 3 caption): each run of M consecutive weights owns a learnable categorical
+ * distribution over the C(M,N) candidate masks that keep N of the M weights.  A Gumbel-softmax
+ * sample of that distribution, weighted-averaged over the candidates, is a differentiable soft
+ * mask.  Fig. 5 caption: a scaling factor kappa sets the randomness of the sampling.  Abstract:
+ * the weights stay frozen and only the masks are learned.
+ * Compressed storage ("Accelerating Sparse Deep Neural Networks" summary page, section 3.1):
+ * only the kept values are stored, plus the position of each kept value inside its group as
+ * separate metadata (2 bits per kept value for groups of four).
+ *
+ * Conventions used by every entry point
+ *   W          [rows, cols] row-major, element type shape->wtype (NM_F32 or NM_BF16); groups of
+ *              m consecutive elements run along cols (the contiguous, input dimension), so group
+ *              g = r*(cols/m) + q holds W[r, q*m .. q*m+m-1].
+ *   candidates the K = C(m,n) subsets of n kept positions, in lexicographic order of their
+ *              ascending position lists (2:4: {0,1},{0,2},{0,3},{1,2},{1,3},{2,3}); see
+ *              nm_candidate_table.
+ *   logits     fp32 [rows, cols/m, K], K contiguous: logit k of group g is logits[g*K + k].
+ *   noise      candidate slot i = g*K + k uses word (i & 3) of the Philox4x32-10 block (Salmon et
+ *              al., SC'11) with key (seed lo, seed hi) and counter ((i>>2) lo, (i>>2) hi,
+ *              offset lo, offset hi).  Its top 24 bits j give u = (j + 1/2) / 2^24 and the
+ *              Gumbel sample g = -ln(-ln u).  offset is the training step: forward and backward
+ *              of one step pass the same (seed, offset), and the backward regenerates the noise
+ *              instead of reading it from memory.
+ *   sample     y_k = softmax_k((kappa*l_k + g_k) / tau); soft mask m_j = sum of y_k over the
+ *              candidates k that keep position j (so m_j is in [0,1] and sums to n per group).
+ *   hard mask  the candidate with the largest logit (no noise; the first one on exact ties).
+ *   packed     values [rows, cols*n/m] in wtype: the kept weights of each group in ascending
+ *              position order.  indices: per row, a little-endian stream of 32-bit words holding
+ *              b = ceil(log2 m) bits per kept value (2 for m = 4, 3 for m = 8); field
+ *              f = q*n + t of a row (kept value t of group q) sits at bit f*b.  Each row starts
+ *              on a new word; unused bits of its last word are zero.  Words per row:
+ *              nm_index_words_per_row.
+ *
+ * Supported: m in {4, 8}, 1 <= n < m (K = 4, 6, 4 for m = 4; 8, 28, 56, 70, 56, 28, 8 for
+ * m = 8); wtype NM_F32 or NM_BF16; all arithmetic is fp32.
+ *
+ * Ownership and execution: every pointer is device memory owned by the caller (a torch tensor,
+ * a hipMalloc buffer).  The library allocates nothing, keeps no mutable global state and may be
+ * called from several host threads.  Calls are asynchronous and ordered on `stream` (a
+ * hipStream_t passed as void*; NULL is the default stream).  The return value reports argument
+ * validation and launch only; execution errors surface at the caller's next synchronisation.
+ *
+ * Errors: arguments are checked on the host before any HIP call; on an error nothing is
+ * launched and no output is touched.  An empty matrix (rows == 0 or cols == 0) is valid and
+ * launches nothing.  Outputs are unspecified for non-finite weights, logits or gradients, except
+ * that the hard mask and the packed data are always well formed (a NaN logit never wins over
+ * logit 0 of its group).
+ *   NM_EINVAL       null shape/sample/required pointer, rows or cols < 0, cols % m != 0,
+ *                   kappa < 0 or non-finite, tau <= 0 or non-finite, size overflow
+ *   NM_EUNSUPPORTED (n, m) or wtype outside the supported set
+ *   NM_EALIGN       a data pointer that is not 16-byte aligned
+ *   NM_EHIP         the HIP launch failed (hipGetLastError is consumed)
+ */
+#ifndef NM_MASK_H
+#define NM_MASK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NM_OK = 0,
+    NM_EINVAL = 1,
+    NM_EALIGN = 2,
+    NM_EUNSUPPORTED = 3,
+    NM_EHIP = 4
+} nm_status;
+
+enum { NM_F32 = 0, NM_BF16 = 1 };
+
+typedef struct {
+    int64_t rows, cols; /* W is [rows, cols] row-major */
+    int32_t n, m;       /* keep n of every m consecutive weights along cols */
+    int32_t wtype;      /* NM_F32 or NM_BF16: type of W, of its gradient and of packed values */
+} nm_shape;
+
+typedef struct {
+    float kappa;     /* logit scale (MaskLLM project page, Fig. 5 caption), >= 0 */
+    float tau;       /* Gumbel-softmax temperature, > 0 */
+    uint64_t seed;   /* Philox key */
+    uint64_t offset; /* Philox counter high half: the training step */
+} nm_sample;
+
+/* Forward of the differentiable mask (MaskLLM project page, Fig. 3 caption; frozen weights per
+ * its Abstract): w_masked = W * m, rounded to wtype, with m the soft mask of the sample.
+ *   w         [rows, cols] wtype, read
+ *   logits    [rows, cols/m, K] fp32, read
+ *   w_masked  [rows, cols] wtype, written (may not alias the inputs) */
+nm_status nm_mask_forward(const nm_shape *shape, const nm_sample *sample, const void *w,
+                          const float *logits, void *w_masked, void *stream);
+
+/* Backward to the logits (Fig. 3 caption: every step is differentiable).  With the upstream
+ * gradient G = dL/dw_masked, d_k = sum over positions j kept by candidate k of G_j * w_j,
+ * s = sum_k y_k d_k and grad_logits_k = (kappa/tau) * y_k * (d_k - s).  The noise is
+ * regenerated from (seed, offset), so pass the sample of the matching forward.  The weights
+ * are frozen and get no gradient.
+ *   w, grad_w_masked  [rows, cols] wtype, read
+ *   logits            [rows, cols/m, K] fp32, read
+ *   grad_logits       [rows, cols/m, K] fp32, overwritten (not accumulated) */
+nm_status nm_mask_backward(const nm_shape *shape, const nm_sample *sample, const void *w,
+                           const float *logits, const void *grad_w_masked, float *grad_logits,
+                           void *stream);
+
+/* Hard mask and compressed storage ("Accelerating Sparse Deep Neural Networks" summary page,
+ * section 3.1).  Per group: k* = first argmax of its logits; the kept weights of candidate k*
+ * go to `values` and their positions to `indices` (layout above).
+ *   w        [rows, cols] wtype, read;  logits [rows, cols/m, K] fp32, read
+ *   values   [rows, cols*n/m] wtype, written (bit copies of the kept weights)
+ *   indices  [rows, nm_index_words_per_row] uint32, written
+ *   hard_idx [rows, cols/m] uint8, written with k*; may be NULL */
+nm_status nm_mask_harden_pack(const nm_shape *shape, const void *w, const float *logits,
+                              void *values, uint32_t *indices, uint8_t *hard_idx, void *stream);
+
+/* Decompression: w_dense = +0.0 everywhere except the kept values at their positions.
+ * Positions >= m in malformed metadata are skipped.
+ *   values  [rows, cols*n/m] wtype, read;  indices [rows, nm_index_words_per_row] uint32, read
+ *   w_dense [rows, cols] wtype, written */
+nm_status nm_unpack(const nm_shape *shape, const void *values, const uint32_t *indices,
+                    void *w_dense, void *stream);
+
+/* ---- host-only helpers (no device work, no HIP call) ---------------------------------- */
+/* K = C(m, n) for a supported (n, m), else -1. */
+int32_t nm_num_candidates(int32_t n, int32_t m);
+/* out_bits[k] (K bytes, caller-owned host memory): bit j set iff candidate k keeps j. */
+nm_status nm_candidate_table(int32_t n, int32_t m, uint8_t *out_bits);
+/* rows * cols * n / m, or -1 for an invalid shape. */
+int64_t nm_packed_value_elems(const nm_shape *shape);
+/* ceil((cols/m) * n * ceil(log2 m) / 32), or -1 for an invalid shape. */
+int64_t nm_index_words_per_row(const nm_shape *shape);
+/* rows * nm_index_words_per_row, or -1. */
+int64_t nm_packed_index_words(const nm_shape *shape);
+/* Static description of a status code. */
+const char *nm_status_str(nm_status status);
+
+/* ---- diagnostic exports: the same device functions the kernels use ------------------- */
+/* Raw noise words [rows*cols/m, K] (uint32) of a sample; kappa and tau are not used. */
+nm_status nm_debug_noise(const nm_shape *shape, const nm_sample *sample, uint32_t *words,
+                         void *stream);
+/* Base-2 Gumbel exponent of noise words: h = log2(-log2(u)), u = ((x >> 8) + 1/2) / 2^24, so
+ * that the Gumbel sample is g = -ln(2) * (h + log2(ln 2)).  words and h hold count elements. */
+nm_status nm_debug_gumbel_log2(const uint32_t *words, float *h, int64_t count, void *stream);
+/* Soft mask [rows, cols] fp32 of a sample (the forward's m before the multiply). */
+nm_status nm_debug_soft_mask(const nm_shape *shape, const nm_sample *sample,
+                             const float *logits, float *soft_mask, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NM_MASK_H */

@@ -34,15 +34,16 @@ def layer_weights(layer):
     return sum(r * c for _, r, c in layer)
 
 
-def _gen(seed):
-    g = torch.Generator(device="cpu")
+def _gen(seed, device="cpu"):
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
 
-def normal(shape, std, seed, dtype=torch.float32):
-    """N(0, std^2) samples (std is the standard deviation), rounded to `dtype`."""
-    t = torch.randn(shape, generator=_gen(seed), dtype=torch.float32)
+def normal(shape, std, seed, dtype=torch.float32, device="cpu"):
+    """N(0, std^2) samples (std is the standard deviation), rounded to `dtype`.  The same seed
+    gives different values on different device types (each has its own generator)."""
+    t = torch.randn(shape, generator=_gen(seed, device), dtype=torch.float32, device=device)
     if std != 1.0:
         t.mul_(std)
     return t.to(dtype)
@@ -61,25 +62,25 @@ def magnitude_prior_index(w, n, m):
     # stable sort of -|w|: equal magnitudes keep their original (lower-first) order
     order = torch.sort(-a, dim=-1, stable=True).indices[..., :n]
     code = (torch.ones_like(order) << order).sum(-1)
-    lut = torch.full((1 << m,), -1, dtype=torch.int64)
+    lut = torch.full((1 << m,), -1, dtype=torch.int64, device=w.device)
     for k, pos in enumerate(itertools.combinations(range(m), n)):
         lut[sum(1 << p for p in pos)] = k
     return lut[code]
 
 
 def prior_logits(w, n, m, seed, alpha=3.0, noise_std=0.1):
-    """fp32 logits [rows, cols/m, K]: alpha on the magnitude-prior candidate, 0 elsewhere,
-    plus N(0, noise_std^2)."""
+    """fp32 logits [rows, cols/m, K] on w's device: alpha on the magnitude-prior candidate,
+    0 elsewhere, plus N(0, noise_std^2)."""
     rows, cols = w.shape
     K = num_candidates(n, m)
     idx = magnitude_prior_index(w, n, m)
-    L = normal((rows, cols // m, K), noise_std, seed)
-    L.scatter_add_(-1, idx.unsqueeze(-1), torch.full(idx.shape + (1,), alpha))
+    L = normal((rows, cols // m, K), noise_std, seed, device=w.device)
+    L.scatter_add_(-1, idx.unsqueeze(-1), torch.full(idx.shape + (1,), alpha, device=w.device))
     return L
 
 
-def gaussian_logits(rows, cols, n, m, seed, std=1.0):
-    return normal((rows, cols // m, num_candidates(n, m)), std, seed)
+def gaussian_logits(rows, cols, n, m, seed, std=1.0, device="cpu"):
+    return normal((rows, cols // m, num_candidates(n, m)), std, seed, device=device)
 
 
 def input_seed(config, layer, matrix):
@@ -87,12 +88,13 @@ def input_seed(config, layer, matrix):
     return 1000 * config + 10 * layer + matrix
 
 
-def matrix_inputs(rows, cols, n, m, wtype, w_std, seed, logits="gaussian", with_grad=True):
+def matrix_inputs(rows, cols, n, m, wtype, w_std, seed, logits="gaussian", with_grad=True,
+                  device="cpu"):
     """(w, logits, grad) for one weight matrix; grad ~ N(0,1) in the weight type."""
-    w = normal((rows, cols), w_std, 3 * seed + 0, wtype)
+    w = normal((rows, cols), w_std, 3 * seed + 0, wtype, device)
     if logits == "prior":
         L = prior_logits(w, n, m, 3 * seed + 1)
     else:
-        L = gaussian_logits(rows, cols, n, m, 3 * seed + 1)
-    G = normal((rows, cols), 1.0, 3 * seed + 2, wtype) if with_grad else None
+        L = gaussian_logits(rows, cols, n, m, 3 * seed + 1, device=device)
+    G = normal((rows, cols), 1.0, 3 * seed + 2, wtype, device) if with_grad else None
     return w, L, G

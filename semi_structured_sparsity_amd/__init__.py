@@ -1,0 +1,295 @@
+"""Learnable N:M semi-structured sparsity on MI355X: Python binding of libnm_mask.so.
+
+The binding only marshals arguments: every step of the layer runs in the HIP kernels of
+libnm_mask.so (include/nm_mask.h documents the contract).  PyTorch provides device memory and
+the current stream.  Importing the package does not touch the GPU; the first call loads the
+library and fails loudly if it has not been built (python -m semi_structured_sparsity_amd.build)
+or if a tensor is not on a ROCm device.
+
+Entry points, named as in the C ABI:
+    nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset)        -> w_masked
+    nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset) -> grad_logits
+    nm_mask_harden_pack(w, logits, n, m, with_hard=False)             -> values, indices[, hard]
+    nm_unpack(values, indices, cols, n, m)                            -> w_dense
+and `mask(...)`, the autograd function whose backward is nm_mask_backward (the weights are frozen
+and get no gradient).
+"""
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+NM_OK, NM_EINVAL, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(5)
+NM_F32, NM_BF16 = 0, 1
+
+_lib = None
+
+
+class NMError(RuntimeError):
+    """A non-zero nm_status from the library."""
+
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {lib().nm_status_str(status).decode()} (status {status})")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("n", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("wtype", ctypes.c_int32)]
+
+
+class _Sample(ctypes.Structure):
+    _fields_ = [("kappa", ctypes.c_float), ("tau", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "nm_mask_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "nm_mask_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
+    "nm_candidate_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P]),
+    "nm_packed_value_elems": (ctypes.c_int64, [_P]),
+    "nm_index_words_per_row": (ctypes.c_int64, [_P]),
+    "nm_packed_index_words": (ctypes.c_int64, [_P]),
+    "nm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "nm_debug_noise": (ctypes.c_int, [_P, _P, _P, _P]),
+    "nm_debug_gumbel_log2": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "nm_debug_soft_mask": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+
+def library_path():
+    return os.environ.get("NM_MASK_LIB", _build.LIB)
+
+
+def lib():
+    """The loaded libnm_mask.so (never rebuilt here: build() does that explicitly)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -m semi_structured_sparsity_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------------------------
+# marshalling helpers
+
+def _wtype(dtype):
+    if dtype == torch.float32:
+        return NM_F32
+    if dtype == torch.bfloat16:
+        return NM_BF16
+    raise TypeError(f"weights must be float32 or bfloat16, got {dtype}")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(rows, cols, n, m, wtype):
+    return _Shape(int(rows), int(cols), int(n), int(m), int(wtype))
+
+
+def _sample(kappa, tau, seed, offset):
+    return _Sample(float(kappa), float(tau), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1))
+
+
+def _check(status, what):
+    if status != NM_OK:
+        raise NMError(status, what)
+
+
+def num_candidates(n, m):
+    """K = C(m, n) for a supported n:m, else -1."""
+    return lib().nm_num_candidates(n, m)
+
+
+def candidate_table(n, m):
+    """Host list of K bytes: bit j of entry k set iff candidate k keeps position j."""
+    K = num_candidates(n, m)
+    if K < 0:
+        raise NMError(NM_EUNSUPPORTED, "nm_candidate_table")
+    buf = (ctypes.c_uint8 * K)()
+    _check(lib().nm_candidate_table(n, m, buf), "nm_candidate_table")
+    return list(buf)
+
+
+def index_words_per_row(cols, n, m):
+    return lib().nm_index_words_per_row(ctypes.byref(_shape(1, cols, n, m, NM_F32)))
+
+
+def _logit_shape(rows, cols, n, m):
+    K = num_candidates(n, m)
+    if K < 0:
+        raise NMError(NM_EUNSUPPORTED, "n:m")
+    return (rows, cols // m, K)
+
+
+# ---------------------------------------------------------------------------------------------
+# the four entry points of the layer
+
+def nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset, out=None):
+    """Masked frozen weights w * m (MaskLLM project page, Fig. 3 caption)."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    out = torch.empty_like(w) if out is None else out
+    st = lib().nm_mask_forward(ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)),
+                               _dev(w, "w"), _dev(logits, "logits", torch.float32,
+                                                  _logit_shape(rows, cols, n, m)),
+                               _dev(out, "out", w.dtype, w.shape), _stream(w.device))
+    _check(st, "nm_mask_forward")
+    return out
+
+
+def nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset, out=None):
+    """Gradient of the loss with respect to the logits (overwrites `out` if given)."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    lshape = _logit_shape(rows, cols, n, m)
+    out = torch.empty(lshape, dtype=torch.float32, device=w.device) if out is None else out
+    st = lib().nm_mask_backward(ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)),
+                                _dev(w, "w"), _dev(logits, "logits", torch.float32, lshape),
+                                _dev(grad, "grad", w.dtype, w.shape),
+                                _dev(out, "out", torch.float32, lshape), _stream(w.device))
+    _check(st, "nm_mask_backward")
+    return out
+
+
+def nm_mask_harden_pack(w, logits, n, m, with_hard=False, out=None):
+    """Hard argmax mask packed as (values, indices[, hard]) ("Accelerating Sparse Deep Neural
+    Networks" summary page, section 3.1)."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    wpr = lib().nm_index_words_per_row(ctypes.byref(sh))
+    if wpr < 0:
+        raise NMError(NM_EINVAL, "nm_mask_harden_pack")
+    if out is None:
+        values = torch.empty((rows, cols // m * n), dtype=w.dtype, device=w.device)
+        indices = torch.empty((rows, wpr), dtype=torch.int32, device=w.device)
+        hard = torch.empty((rows, cols // m), dtype=torch.uint8, device=w.device) if with_hard else None
+    else:
+        values, indices, hard = out
+    st = lib().nm_mask_harden_pack(
+        ctypes.byref(sh), _dev(w, "w"),
+        _dev(logits, "logits", torch.float32, _logit_shape(rows, cols, n, m)),
+        _dev(values, "values", w.dtype, (rows, cols // m * n)),
+        _dev(indices, "indices", torch.int32, (rows, wpr)),
+        None if hard is None else _dev(hard, "hard", torch.uint8, (rows, cols // m)),
+        _stream(w.device))
+    _check(st, "nm_mask_harden_pack")
+    return (values, indices, hard) if with_hard else (values, indices)
+
+
+def nm_unpack(values, indices, cols, n, m, out=None):
+    """Dense weights with +0.0 at dropped positions."""
+    rows = values.shape[0]
+    sh = _shape(rows, cols, n, m, _wtype(values.dtype))
+    wpr = lib().nm_index_words_per_row(ctypes.byref(sh))
+    if wpr < 0:
+        raise NMError(NM_EINVAL, "nm_unpack")
+    out = torch.empty((rows, cols), dtype=values.dtype, device=values.device) if out is None else out
+    st = lib().nm_unpack(ctypes.byref(sh), _dev(values, "values", None, (rows, cols // m * n)),
+                         _dev(indices, "indices", torch.int32, (rows, wpr)),
+                         _dev(out, "out", values.dtype, (rows, cols)), _stream(values.device))
+    _check(st, "nm_unpack")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# diagnostics (same device functions as the kernels)
+
+def nm_debug_noise(rows, cols, n, m, seed, offset, device="cuda"):
+    """Raw Philox words [rows, cols/m, K] as int32 (bit patterns of the uint32 words)."""
+    shape = _logit_shape(rows, cols, n, m)
+    out = torch.empty(shape, dtype=torch.int32, device=device)
+    sh = _shape(rows, cols, n, m, NM_F32)
+    st = lib().nm_debug_noise(ctypes.byref(sh), ctypes.byref(_sample(1.0, 1.0, seed, offset)),
+                              _dev(out, "out"), _stream(out.device))
+    _check(st, "nm_debug_noise")
+    return out
+
+
+def nm_debug_gumbel_log2(words):
+    """h = log2(-log2(u)) for int32 tensors holding uint32 noise words."""
+    out = torch.empty(words.shape, dtype=torch.float32, device=words.device)
+    st = lib().nm_debug_gumbel_log2(_dev(words, "words", torch.int32), _dev(out, "out"),
+                                    words.numel(), _stream(words.device))
+    _check(st, "nm_debug_gumbel_log2")
+    return out
+
+
+def nm_debug_soft_mask(logits, n, m, kappa, tau, seed, offset):
+    """fp32 soft mask [rows, cols] of a sample."""
+    rows, gpr, K = logits.shape
+    cols = gpr * m
+    out = torch.empty((rows, cols), dtype=torch.float32, device=logits.device)
+    sh = _shape(rows, cols, n, m, NM_F32)
+    st = lib().nm_debug_soft_mask(ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)),
+                                  _dev(logits, "logits", torch.float32, _logit_shape(rows, cols, n, m)),
+                                  _dev(out, "out"), _stream(logits.device))
+    _check(st, "nm_debug_soft_mask")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# autograd
+
+class NMMask(torch.autograd.Function):
+    """w_masked = w * softmask(logits); gradient to the logits only (frozen weights)."""
+
+    @staticmethod
+    def forward(ctx, w, logits, n, m, kappa, tau, seed, offset):
+        ctx.save_for_backward(w, logits)
+        ctx.params = (n, m, kappa, tau, seed, offset)
+        return nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset)
+
+    @staticmethod
+    def backward(ctx, grad):
+        w, logits = ctx.saved_tensors
+        n, m, kappa, tau, seed, offset = ctx.params
+        dl = nm_mask_backward(w, logits, grad.contiguous(), n, m, kappa, tau, seed, offset)
+        return None, dl, None, None, None, None, None, None
+
+
+def mask(w, logits, n, m, kappa, tau, seed, offset):
+    """Differentiable N:M mask layer; `offset` is the training step (fresh noise per step)."""
+    return NMMask.apply(w, logits, n, m, kappa, tau, seed, offset)
+
+
+def packed_bytes(rows, cols, n, m, elem_bytes):
+    """Bytes of the compressed form: kept values plus index words."""
+    return rows * cols // m * n * elem_bytes + rows * index_words_per_row(cols, n, m) * 4
+
+
+__all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
+           "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
+           "NMError", "EXPORTS", "library_path", "math"]

@@ -1,0 +1,218 @@
+// nm_abi.hip -- the extern "C" entry points declared in include/nm_mask.h.
+//
+// Each entry point validates its arguments on the host, derives the fp32 launch constants
+// (A = kappa*log2(e)/tau, B = 1/tau, C = kappa/tau, computed in double and rounded once), and
+// launches one kernel on the caller's stream.  No HIP call is made before validation passes,
+// so every argument error is reported without touching the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/nm_mask.h"
+#include "nm_kernels.hpp"
+
+namespace {
+
+bool supported_nm(int32_t n, int32_t m) { return (m == 4 || m == 8) && n >= 1 && n < m; }
+
+int32_t binom_host(int32_t m, int32_t n) {
+    int64_t c = 1;
+    for (int32_t i = 0; i < n; ++i) c = c * (m - i) / (i + 1);
+    return (int32_t)c;
+}
+
+int32_t index_bits(int32_t m) { return m <= 4 ? 2 : 3; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest flat thread count a launch may need: the grid's x dimension is at most 2^31 - 1
+// blocks of 256 threads.
+constexpr int64_t kMaxThreads = ((int64_t)1 << 31) * 256 - 256;
+
+// Shape checks shared by all entry points; on success *groups = rows*cols/m and *K = C(m,n).
+nm_status check_shape(const nm_shape* s, int64_t* groups, int32_t* K) {
+    if (!s) return NM_EINVAL;
+    if (s->rows < 0 || s->cols < 0) return NM_EINVAL;
+    if (!supported_nm(s->n, s->m)) return NM_EUNSUPPORTED;
+    if (s->wtype != NM_F32 && s->wtype != NM_BF16) return NM_EUNSUPPORTED;
+    if (s->cols % s->m != 0) return NM_EINVAL;
+    *K = binom_host(s->m, s->n);
+    if (s->rows > 0 && s->cols > INT64_MAX / 16 / s->rows) return NM_EINVAL;
+    const int64_t g = s->rows * (s->cols / s->m);
+    if (g > INT64_MAX / 8 / *K) return NM_EINVAL;  // logit byte offsets stay in int64
+    if (g > kMaxThreads) return NM_EINVAL;         // one group or more per thread
+    *groups = g;
+    return NM_OK;
+}
+
+nm_status check_sample(const nm_sample* smp, float* A, float* B, float* C) {
+    if (!smp) return NM_EINVAL;
+    const double kappa = smp->kappa, tau = smp->tau;
+    if (!(isfinite(kappa) && kappa >= 0.0)) return NM_EINVAL;
+    if (!(isfinite(tau) && tau > 0.0)) return NM_EINVAL;
+    const double log2e = 1.4426950408889634074;
+    *A = (float)(kappa * log2e / tau);
+    *B = (float)(1.0 / tau);
+    *C = (float)(kappa / tau);
+    if (!isfinite(*A) || !isfinite(*B) || !isfinite(*C)) return NM_EINVAL;
+    return NM_OK;
+}
+
+nm::NoiseKey noise_key(const nm_sample* smp) {
+    return nm::NoiseKey{(uint32_t)smp->seed, (uint32_t)(smp->seed >> 32), (uint32_t)smp->offset,
+                        (uint32_t)(smp->offset >> 32)};
+}
+
+nm_status launched(hipError_t e) { return e == hipSuccess ? NM_OK : NM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t nm_num_candidates(int32_t n, int32_t m) { return supported_nm(n, m) ? binom_host(m, n) : -1; }
+
+nm_status nm_candidate_table(int32_t n, int32_t m, uint8_t* out_bits) {
+    if (!supported_nm(n, m)) return NM_EUNSUPPORTED;
+    if (!out_bits) return NM_EINVAL;
+    // lexicographic order of the ascending kept-position lists
+    int32_t k = 0;
+    for (int32_t r = (1 << m) - 1; r >= 0; --r) {
+        if (__builtin_popcount((unsigned)r) != n) continue;
+        uint32_t bits = 0;
+        for (int32_t j = 0; j < m; ++j)
+            if (r >> (m - 1 - j) & 1) bits |= 1u << j;
+        out_bits[k++] = (uint8_t)bits;
+    }
+    return NM_OK;
+}
+
+int64_t nm_packed_value_elems(const nm_shape* s) {
+    int64_t g;
+    int32_t K;
+    if (check_shape(s, &g, &K) != NM_OK) return -1;
+    return g * s->n;
+}
+
+int64_t nm_index_words_per_row(const nm_shape* s) {
+    int64_t g;
+    int32_t K;
+    if (check_shape(s, &g, &K) != NM_OK) return -1;
+    const int64_t bits = s->cols / s->m * s->n * index_bits(s->m);
+    return (bits + 31) / 32;
+}
+
+int64_t nm_packed_index_words(const nm_shape* s) {
+    const int64_t wpr = nm_index_words_per_row(s);
+    return wpr < 0 ? -1 : wpr * s->rows;
+}
+
+const char* nm_status_str(nm_status st) {
+    switch (st) {
+    case NM_OK: return "ok";
+    case NM_EINVAL: return "invalid argument";
+    case NM_EALIGN: return "pointer not 16-byte aligned";
+    case NM_EUNSUPPORTED: return "unsupported n:m or element type";
+    case NM_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+nm_status nm_mask_forward(const nm_shape* shape, const nm_sample* sample, const void* w,
+                          const float* logits, void* w_masked, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !w_masked) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked)) return NM_EALIGN;
+    nm::FwdArgs a{w, logits, w_masked, groups, A, B, noise_key(sample)};
+    return launched(nm::launch_forward(shape->n, shape->m, shape->wtype, a, false, (hipStream_t)stream));
+}
+
+nm_status nm_debug_soft_mask(const nm_shape* shape, const nm_sample* sample, const float* logits,
+                             float* soft_mask, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!logits || !soft_mask) return NM_EINVAL;
+    if (!aligned16(logits) || !aligned16(soft_mask)) return NM_EALIGN;
+    nm::FwdArgs a{nullptr, logits, soft_mask, groups, A, B, noise_key(sample)};
+    return launched(nm::launch_forward(shape->n, shape->m, shape->wtype, a, true, (hipStream_t)stream));
+}
+
+nm_status nm_mask_backward(const nm_shape* shape, const nm_sample* sample, const void* w,
+                           const float* logits, const void* grad_w_masked, float* grad_logits,
+                           void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !grad_w_masked || !grad_logits) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(grad_w_masked) || !aligned16(grad_logits))
+        return NM_EALIGN;
+    nm::BwdArgs a{w, logits, grad_w_masked, grad_logits, groups, A, B, C, noise_key(sample)};
+    return launched(nm::launch_backward(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
+nm_status nm_mask_harden_pack(const nm_shape* shape, const void* w, const float* logits, void* values,
+                              uint32_t* indices, uint8_t* hard_idx, void* stream) {
+    int64_t groups;
+    int32_t K;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !values || !indices) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(values) || !aligned16(indices) ||
+        (hard_idx && !aligned16(hard_idx)))
+        return NM_EALIGN;
+    nm::PackArgs a{w, logits, values, indices, hard_idx, shape->rows, shape->cols / shape->m,
+                   nm_index_words_per_row(shape), 0};
+    return launched(nm::launch_pack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
+nm_status nm_unpack(const nm_shape* shape, const void* values, const uint32_t* indices, void* w_dense,
+                    void* stream) {
+    int64_t groups;
+    int32_t K;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!values || !indices || !w_dense) return NM_EINVAL;
+    if (!aligned16(values) || !aligned16(indices) || !aligned16(w_dense)) return NM_EALIGN;
+    nm::UnpackArgs a{values, indices, w_dense, shape->rows, shape->cols / shape->m,
+                     nm_index_words_per_row(shape), 0};
+    return launched(nm::launch_unpack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
+nm_status nm_debug_noise(const nm_shape* shape, const nm_sample* sample, uint32_t* words, void* stream) {
+    int64_t groups;
+    int32_t K;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if (!sample) return NM_EINVAL;
+    if (groups == 0) return NM_OK;
+    if (!words) return NM_EINVAL;
+    if (!aligned16(words)) return NM_EALIGN;
+    nm::NoiseArgs a{words, groups * K, noise_key(sample)};
+    return launched(nm::launch_debug_noise(a, (hipStream_t)stream));
+}
+
+nm_status nm_debug_gumbel_log2(const uint32_t* words, float* h, int64_t count, void* stream) {
+    if (count < 0 || count > kMaxThreads) return NM_EINVAL;
+    if (count == 0) return NM_OK;
+    if (!words || !h) return NM_EINVAL;
+    if (!aligned16(words) || !aligned16(h)) return NM_EALIGN;
+    nm::GumbelArgs a{words, h, count};
+    return launched(nm::launch_debug_gumbel(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// nm_device.hpp -- device building blocks of the N:M mask kernels for gfx950 (MI355X):
+// compile-time candidate tables, Philox4x32-10 noise, the Gumbel transform in base 2, and
+// vector load/store helpers.  Everything here is header-only and inlined into the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nm_kernels.hpp"
+
+namespace nm {
+
+// ------------------------------------------------------------------------------------------
+// Candidate masks (MaskLLM project page, Fig. 3 caption: each group of M weights has a
+// categorical distribution over the masks that keep N of them).  Order: lexicographic in the
+// ascending list of kept positions.  With position j mapped to bit M-1-j, that order is the
+// descending numeric order of the bit patterns, which is how the table is generated.
+
+constexpr int binom(int m, int n) {
+    int c = 1;
+    for (int i = 0; i < n; ++i) c = c * (m - i) / (i + 1);
+    return c;
+}
+
+constexpr int popcount_c(unsigned v) {
+    int c = 0;
+    for (; v; v &= v - 1) ++c;
+    return c;
+}
+
+template <int N, int M>
+struct Candidates {
+    static constexpr int K = binom(M, N);
+    uint8_t keep[K];  // bit j set: position j kept
+    constexpr Candidates() : keep{} {
+        int k = 0;
+        for (int r = (1 << M) - 1; r >= 0; --r) {
+            if (popcount_c((unsigned)r) != N) continue;
+            unsigned bits = 0;
+            for (int j = 0; j < M; ++j)
+                if (r >> (M - 1 - j) & 1) bits |= 1u << j;
+            keep[k++] = (uint8_t)bits;
+        }
+    }
+    constexpr bool kept(int k, int j) const { return (keep[k] >> j & 1) != 0; }
+    // t-th kept position of candidate k
+    constexpr int pos(int k, int t) const {
+        int seen = 0;
+        for (int j = 0; j < M; ++j)
+            if (kept(k, j)) {
+                if (seen == t) return j;
+                ++seen;
+            }
+        return -1;
+    }
+};
+
+// Groups per thread in the sampling kernels: enough for the thread's candidate slots to fill
+// whole Philox blocks when K is not a multiple of 4 (K = 6 -> 2 groups = 3 blocks).  K = 70 is
+// handled with one group per thread and a 0-or-2 word phase instead (2 groups would keep 280
+// values live per thread).
+template <int K>
+struct SlotTiling {
+    static constexpr int P = (K % 4 == 0 || K == 70) ? 1 : (K % 2 == 0 ? 2 : 4);
+    static constexpr bool phased = (P * K) % 4 != 0;  // block boundary may fall inside a group
+};
+
+// ------------------------------------------------------------------------------------------
+// Philox4x32 (Salmon, Moraes, Dror, Shaw, SC'11, section 3.3): 10 rounds; each multiplies words
+// 0 and 2 by fixed odd constants, the high halves are xored into the other two words with the
+// round key, and the key is advanced by two Weyl increments between rounds.  The key (the seed)
+// and the high counter half (the offset) are uniform across a launch and stay in SGPRs.
+
+struct Philox4 {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// Block b of the noise stream: slots 4b .. 4b+3.
+__device__ __forceinline__ Philox4 noise_block(const NoiseKey& nk, uint64_t b) {
+    return philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), nk.off0, nk.off1, nk.k0, nk.k1);
+}
+
+// ------------------------------------------------------------------------------------------
+// Gumbel noise in base 2.  The sample is g = -ln(-ln u) with u = (j + 1/2) 2^-24, j = x >> 8.
+// Writing a = -log2(u) gives g = -ln2 * (log2(a) + log2(ln2)); the constant cancels in the
+// softmax, so the kernels work with h = log2(a) and z' = z * log2(e) = A*l - B*h + const, with
+// A = kappa*log2(e)/tau and B = 1/tau.
+//
+// u needs 25 significant bits when u >= 1/2, so fp32 cannot hold it; rounding it would put an
+// absolute error of 2^-25 into u, which near u = 1 is a large relative error of a (and an
+// unbounded one at u = 1 - 2^-25, which rounds to 1).  The transform therefore keeps
+// u = u_hi + r exactly (u_hi = fl32(u), r in {0, +-2^-25}) and uses
+//     -log2(u) = -log2(u_hi) - log2(1 + r/u_hi) ~= -log2(u_hi) - r*log2(e)*(2 - u_hi),
+// where 2 - u_hi stands in for 1/u_hi on [1/2, 1] (r = 0 below 1/2).  v_log_f32 is within
+// 1 ulp (relative) for the normal inputs used here.
+__device__ __forceinline__ float gumbel_log2(uint32_t x) {
+    const float jf = (float)(x >> 8);                           // exact: j < 2^24
+    const float u_hi = fmaf(jf, 0x1p-24f, 0x1p-25f);            // fl32(u)
+    const float r = fmaf(jf, 0x1p-24f, -u_hi) + 0x1p-25f;       // u - u_hi, exact
+    const float corr = (r * 1.4426950408889634f) * (2.0f - u_hi);
+    const float a = -(__builtin_amdgcn_logf(u_hi) + corr);      // -log2(u) > 0
+    return __builtin_amdgcn_logf(a);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------------------------------
+// Element types: W and its gradient are fp32 or bf16; arithmetic is fp32.
+
+struct F32 {
+    using storage = float;
+    static constexpr int bytes = 4;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Load CNT consecutive elements of type T (F32/BF16) as floats.  `vec` selects 16-byte vector
+// loads (the caller guarantees alignment and that all CNT elements exist); otherwise only the
+// first `valid` elements are read and the rest are zero.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_as_float(const typename T::storage* __restrict__ p, bool vec,
+                                              int valid, float (&out)[CNT]) {
+    if constexpr (T::bytes == 4) {
+        if (vec && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i) {
+                const float4 v = reinterpret_cast<const float4*>(p)[i];
+                out[4 * i + 0] = v.x;
+                out[4 * i + 1] = v.y;
+                out[4 * i + 2] = v.z;
+                out[4 * i + 3] = v.w;
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < CNT; ++i) out[i] = (vec || i < valid) ? p[i] : 0.0f;
+    } else {
+        if (vec && CNT % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 8; ++i) {
+                const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    out[8 * i + 2 * q] = bf16_lo(w[q]);
+                    out[8 * i + 2 * q + 1] = bf16_hi(w[q]);
+                }
+            }
+            return;
+        }
+        if (vec && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i) {
+                const uint2 v = reinterpret_cast<const uint2*>(p)[i];
+                out[4 * i + 0] = bf16_lo(v.x);
+                out[4 * i + 1] = bf16_hi(v.x);
+                out[4 * i + 2] = bf16_lo(v.y);
+                out[4 * i + 3] = bf16_hi(v.y);
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < CNT; ++i) out[i] = (vec || i < valid) ? __uint_as_float((uint32_t)p[i] << 16) : 0.0f;
+    }
+}
+
+// Store CNT floats rounded to T.  Same `vec` / `valid` contract as load_as_float.
+template <typename T, int CNT>
+__device__ __forceinline__ void store_from_float(typename T::storage* __restrict__ p, bool vec,
+                                                 int valid, const float (&in)[CNT]) {
+    if constexpr (T::bytes == 4) {
+        if (vec && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i)
+                reinterpret_cast<float4*>(p)[i] = make_float4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < CNT; ++i)
+            if (vec || i < valid) p[i] = in[i];
+    } else {
+        if (vec && CNT % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 8; ++i)
+                reinterpret_cast<uint4*>(p)[i] =
+                    make_uint4(pack_bf16x2(in[8 * i], in[8 * i + 1]), pack_bf16x2(in[8 * i + 2], in[8 * i + 3]),
+                               pack_bf16x2(in[8 * i + 4], in[8 * i + 5]), pack_bf16x2(in[8 * i + 6], in[8 * i + 7]));
+            return;
+        }
+        if (vec && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i)
+                reinterpret_cast<uint2*>(p)[i] =
+                    make_uint2(pack_bf16x2(in[4 * i], in[4 * i + 1]), pack_bf16x2(in[4 * i + 2], in[4 * i + 3]));
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < CNT; ++i)
+            if (vec || i < valid) p[i] = __builtin_bit_cast(uint16_t, (__bf16)in[i]);
+    }
+}
+
+}  // namespace nm

@@ -1,0 +1,74 @@
+// nm_kernels.hpp -- kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nm {
+
+// Philox key (the seed) and counter high half (the offset) of one launch.
+struct NoiseKey {
+    uint32_t k0, k1;      // seed lo, hi
+    uint32_t off0, off1;  // offset lo, hi
+};
+
+struct FwdArgs {
+    const void* w;
+    const float* logits;
+    void* out;           // w_masked (wtype) or soft mask (fp32)
+    int64_t groups;      // rows * cols / m
+    float A, B;          // kappa*log2(e)/tau, 1/tau
+    NoiseKey nk;
+};
+
+struct BwdArgs {
+    const void* w;
+    const float* logits;
+    const void* grad;
+    float* dlogits;
+    int64_t groups;
+    float A, B, C;       // C = kappa/tau
+    NoiseKey nk;
+};
+
+struct PackArgs {
+    const void* w;
+    const float* logits;
+    void* values;
+    uint32_t* indices;
+    uint8_t* hard;       // may be null
+    int64_t rows, gpr;   // groups per row
+    int64_t words_per_row;
+    int64_t chunks_per_row;  // set by the launcher
+};
+
+struct UnpackArgs {
+    const void* values;
+    const uint32_t* indices;
+    void* dense;
+    int64_t rows, gpr, words_per_row;
+    int64_t chunks_per_row;  // set by the launcher
+};
+
+struct NoiseArgs {
+    uint32_t* words;
+    int64_t slots;       // groups * K
+    NoiseKey nk;
+};
+
+struct GumbelArgs {
+    const uint32_t* words;
+    float* h;
+    int64_t count;
+};
+
+hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_mask, hipStream_t s);
+hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
+hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);
+hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
+hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
+hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s);
+int pack_groups_per_chunk(int n, int m);
+int groups_per_thread(int n, int m);
+
+}  // namespace nm

@@ -1,0 +1,71 @@
+"""Parity criteria between the HIP path (fp32 arithmetic) and the binary64 oracle.
+
+Tolerances (stated as 1e-5 relative for fp32 soft masks and logit gradients, 1e-2 for bf16
+outputs), with "relative" made precise for each quantity:
+
+* soft mask (fp32): per group of m, max_j |gpu_j - ref_j| <= tol * max_j |ref_j|.  Values far
+  below the group's maximum carry errors relative to the maximum, not to themselves (a
+  probability of 1e-30 is computed from an exponent of -69, whose rounding is relative to 69).
+* masked weights: |gpu_j - ref_j| <= tol * max(soft mask of the group) * |w_j| + rounding of
+  the output type (2^-24 |ref_j| for fp32, 1e-2 |ref_j| for bf16).
+* logit gradient: grad_k = c y_k (d_k - s) is a difference, so its error is measured against the
+  magnitude of the terms that form it: |gpu_k - ref_k| <= tol * c y_k (|d_k| + sum_i y_i |d_i|)
+  plus an underflow floor.
+
+tol = 1e-5 for tau >= 1/2.  Below that the fp32 noise itself limits agreement: the Gumbel
+exponent is an fp32 number of magnitude up to ~25, whose rounding (~2^-24 * 25) is amplified by
+1/tau; tol_for_tau scales the bound by 0.5/tau there.
+"""
+import numpy as np
+
+TOL_FP32 = 1e-5
+TOL_BF16 = 1e-2
+
+
+def tol_for_tau(tau):
+    return TOL_FP32 * max(1.0, 0.5 / float(tau))
+
+
+def to_f64(t):
+    """float64 numpy copy of a (GPU or CPU) torch tensor."""
+    return t.detach().double().cpu().numpy()
+
+
+def soft_mask_check(gpu, ref, m, tol):
+    """Returns (worst relative group error, number of groups over tol)."""
+    g = np.asarray(gpu, np.float64).reshape(-1, m)
+    r = np.asarray(ref, np.float64).reshape(-1, m)
+    err = np.abs(g - r).max(1)
+    scale = np.abs(r).max(1)
+    rel = err / np.maximum(scale, 1e-300)
+    return float(rel.max(initial=0.0)), int((err > tol * scale).sum())
+
+
+def forward_check(gpu, ref, w, soft_ref, m, tol, bf16):
+    """gpu: float64 array of the GPU output; ref: oracle float64; w: float64 weights."""
+    gpu = np.asarray(gpu, np.float64)
+    mmax = np.repeat(np.abs(soft_ref).reshape(-1, m).max(1), m).reshape(ref.shape)
+    out_round = (TOL_BF16 if bf16 else 2.0**-24) * np.abs(ref)
+    bound = tol * mmax * np.abs(w) + out_round
+    err = np.abs(gpu - ref)
+    scale = mmax * np.abs(w) + np.abs(ref)
+    rel = err / np.maximum(scale, 1e-300)
+    return float(rel.max(initial=0.0)), int((err > bound).sum())
+
+
+def backward_check(gpu, ref, y, d, c, tol):
+    """gpu, ref, y, d: [..., K] float64 (y = probabilities, d = candidate sums of G*w)."""
+    gpu = np.asarray(gpu, np.float64)
+    ad = np.abs(d)
+    terms = c * y * (ad + (y * ad).sum(-1, keepdims=True))
+    floor = c * 1e-36 * ad.max(-1, keepdims=True)
+    err = np.abs(gpu - ref)
+    rel = err / np.maximum(terms + floor, 1e-300)
+    return float(rel.max(initial=0.0)), int((err > tol * terms + floor).sum())
+
+
+def candidate_sums(w, grad, n, m, cand_matrix):
+    """d[..., k] = sum over positions j kept by candidate k of grad_j * w_j (float64)."""
+    a = (np.asarray(grad, np.float64) * np.asarray(w, np.float64))
+    rows, cols = a.shape
+    return a.reshape(rows, cols // m, m) @ cand_matrix.T

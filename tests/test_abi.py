@@ -1,0 +1,146 @@
+"""Host-side tests of the C ABI (no GPU): exported symbols, argument validation before any HIP
+call, and the host helpers, which are compared with the oracle's independent versions."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import semi_structured_sparsity_amd as S
+from semi_structured_sparsity_amd import NM_EALIGN, NM_EINVAL, NM_EUNSUPPORTED, NM_OK
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SUPPORTED = [(n, m) for m in (4, 8) for n in range(1, m)]
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "nm_mask.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    declared = _declared()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(S.EXPORTS)
+
+
+def _shape(rows=4, cols=16, n=2, m=4, wtype=0):
+    return ctypes.byref(S._Shape(rows, cols, n, m, wtype))
+
+
+def _sample(kappa=1.0, tau=1.0):
+    return ctypes.byref(S._Sample(kappa, tau, 0, 0))
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p((1 << 20) + 4)     # misaligned
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), NM_EINVAL), (dict(cols=-4), NM_EINVAL), (dict(cols=6), NM_EINVAL),
+    (dict(n=0), NM_EUNSUPPORTED), (dict(n=4), NM_EUNSUPPORTED), (dict(m=6, n=2, cols=12), NM_EUNSUPPORTED),
+    (dict(m=16, n=2), NM_EUNSUPPORTED), (dict(wtype=2), NM_EUNSUPPORTED),
+    (dict(rows=2**40, cols=2**40), NM_EINVAL),
+])
+def test_bad_shapes_are_rejected_on_the_host(kw, status):
+    L = S.lib()
+    sh = _shape(**kw)
+    assert L.nm_mask_forward(sh, _sample(), FAKE, FAKE, FAKE, None) == status
+    assert L.nm_mask_backward(sh, _sample(), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert L.nm_mask_harden_pack(sh, FAKE, FAKE, FAKE, FAKE, None, None) == status
+    assert L.nm_unpack(sh, FAKE, FAKE, FAKE, None) == status
+    assert L.nm_debug_noise(sh, _sample(), FAKE, None) == status
+    assert L.nm_debug_soft_mask(sh, _sample(), FAKE, FAKE, None) == status
+    assert L.nm_packed_value_elems(sh) == -1 and L.nm_index_words_per_row(sh) == -1
+
+
+@pytest.mark.parametrize("kappa,tau", [(-1.0, 1.0), (float("nan"), 1.0), (float("inf"), 1.0),
+                                       (1.0, 0.0), (1.0, -2.0), (1.0, float("nan")),
+                                       (1.0, float("inf")), (3e38, 1e-3)])
+def test_bad_samples_are_rejected_on_the_host(kappa, tau):
+    L = S.lib()
+    assert L.nm_mask_forward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_backward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_debug_soft_mask(_shape(), _sample(kappa, tau), FAKE, FAKE, None) == NM_EINVAL
+
+
+def test_null_and_misaligned_pointers_are_rejected_on_the_host():
+    L = S.lib()
+    sh, sm = _shape(), _sample()
+    assert L.nm_mask_forward(None, sm, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_forward(sh, None, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    for i in range(3):
+        args = [FAKE] * 3
+        args[i] = None
+        assert L.nm_mask_forward(sh, sm, *args, None) == NM_EINVAL
+        args[i] = ODD
+        assert L.nm_mask_forward(sh, sm, *args, None) == NM_EALIGN
+    for i in range(4):
+        args = [FAKE] * 4
+        args[i] = None
+        assert L.nm_mask_backward(sh, sm, *args, None) == NM_EINVAL
+        args[i] = ODD
+        assert L.nm_mask_backward(sh, sm, *args, None) == NM_EALIGN
+    for i in range(4):
+        args = [FAKE] * 4
+        args[i] = None
+        assert L.nm_mask_harden_pack(sh, *args, None, None) == NM_EINVAL
+        args[i] = ODD
+        assert L.nm_mask_harden_pack(sh, *args, None, None) == NM_EALIGN
+    assert L.nm_mask_harden_pack(sh, FAKE, FAKE, FAKE, FAKE, ODD, None) == NM_EALIGN
+    for i in range(3):
+        args = [FAKE] * 3
+        args[i] = None
+        assert L.nm_unpack(sh, *args, None) == NM_EINVAL
+        args[i] = ODD
+        assert L.nm_unpack(sh, *args, None) == NM_EALIGN
+    assert L.nm_debug_gumbel_log2(FAKE, FAKE, -1, None) == NM_EINVAL
+    assert L.nm_debug_gumbel_log2(None, FAKE, 5, None) == NM_EINVAL
+    assert L.nm_debug_gumbel_log2(ODD, FAKE, 5, None) == NM_EALIGN
+
+
+@pytest.mark.parametrize("rows,cols", [(0, 16), (4, 0), (0, 0)])
+def test_empty_matrices_are_valid_and_launch_nothing(rows, cols):
+    """No pointer is touched (they may be null) and no HIP call is made."""
+    L = S.lib()
+    sh, sm = _shape(rows=rows, cols=cols), _sample()
+    assert L.nm_mask_forward(sh, sm, None, None, None, None) == NM_OK
+    assert L.nm_mask_backward(sh, sm, None, None, None, None, None) == NM_OK
+    assert L.nm_mask_harden_pack(sh, None, None, None, None, None, None) == NM_OK
+    assert L.nm_unpack(sh, None, None, None, None) == NM_OK
+    assert L.nm_debug_noise(sh, sm, None, None) == NM_OK
+    assert L.nm_debug_soft_mask(sh, sm, None, None, None) == NM_OK
+    assert L.nm_debug_gumbel_log2(None, None, 0, None) == NM_OK
+    assert L.nm_packed_value_elems(sh) == 0
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+def test_candidate_table_and_sizes_agree_with_the_oracle(n, m):
+    assert S.num_candidates(n, m) == oracle.num_candidates(n, m)
+    assert S.candidate_table(n, m) == list(oracle.candidate_bits(n, m))
+    for cols in (m, 8 * m, 13 * m, 4096):
+        assert S.index_words_per_row(cols, n, m) == oracle.index_words_per_row(cols, n, m)
+        sh = S._Shape(5, cols, n, m, 1)
+        assert S.lib().nm_packed_value_elems(ctypes.byref(sh)) == 5 * cols // m * n
+        assert S.lib().nm_packed_index_words(ctypes.byref(sh)) == 5 * oracle.index_words_per_row(cols, n, m)
+
+
+def test_unsupported_helpers():
+    assert S.num_candidates(2, 6) == -1 and S.num_candidates(4, 4) == -1
+    assert S.lib().nm_candidate_table(2, 6, None) == NM_EUNSUPPORTED
+    assert S.lib().nm_candidate_table(2, 4, None) == NM_EINVAL
+    assert S.lib().nm_status_str(NM_EALIGN) == b"pointer not 16-byte aligned"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(4, 16)
+    L = torch.zeros(4, 4, 6)
+    with pytest.raises(ValueError):
+        S.nm_mask_forward(w, L, 2, 4, 1.0, 1.0, 0, 0)

@@ -1,0 +1,238 @@
+"""GPU parity of the HIP path against the oracle on small and ragged shapes, every supported
+n:m, both weight types, and the edge cases (empty, one group per row, odd group counts, ties,
+NaN logits, signed zeros).  Every call goes through the C ABI (semi_structured_sparsity_amd)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nm_synth
+import oracle
+import semi_structured_sparsity_amd as S
+from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, soft_mask_check,
+                    to_f64, tol_for_tau)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SUPPORTED = [(n, m) for m in (4, 8) for n in range(1, m)]
+# (rows, cols/m): ragged shapes that span several thread tiles and end in a partial tile
+SHAPES = [(1, 1), (3, 5), (37, 23), (64, 64)]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(rows, cols, n, m, wtype, seed, w_std=0.5):
+    w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, wtype, w_std, seed)
+    return w, L, G, w.to(DEV), L.to(DEV), G.to(DEV)
+
+
+def _u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+# ---------------------------------------------------------------------------------------------
+# noise
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("rows,gpr", SHAPES)
+def test_noise_words_are_bit_exact(n, m, rows, gpr):
+    seed, offset = 0x1234_5678_9ABC_DEF0 + n, 2**40 + 7 * m
+    _say("noise", n, m, rows, gpr)
+    got = _u32(S.nm_debug_noise(rows, gpr * m, n, m, seed, offset)).reshape(-1)
+    want = oracle.noise_words(seed, offset, 0, got.size)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_noise_beyond_2_31_slots():
+    """A matrix with more than 2^31 candidate slots (64-bit slot and block arithmetic), on a few
+    sampled slots."""
+    rows, gpr, n, m = 22000, 16384, 2, 4  # 3.6e8 groups, 2.16e9 slots
+    _say("noise large", rows * gpr)
+    got = S.nm_debug_noise(rows, gpr * m, n, m, 99, 5).reshape(-1)
+    last = rows * gpr * 6 - 1
+    idx = [0, 1, 2**31 - 1, 2**31, 2**31 + 5, last]
+    sample = got[torch.tensor(idx, device=DEV)].cpu().numpy().view(np.uint32)
+    want = [oracle.noise_words(99, 5, i, 1)[0] for i in idx]
+    np.testing.assert_array_equal(sample, want)
+    del got
+    torch.cuda.empty_cache()
+
+
+def test_gumbel_transform_over_all_2_24_uniforms():
+    """h = log2(-log2 u) for every 24-bit uniform, against the oracle's binary64 Gumbel sample
+    g = -ln(-ln u) (h = -g log2(e) - log2(ln 2))."""
+    j = np.arange(1 << 24, dtype=np.uint32)
+    x = (j << np.uint32(8)) | (j & np.uint32(0xFF))  # low byte must not matter
+    h = S.nm_debug_gumbel_log2(torch.from_numpy(x.view(np.int32)).to(DEV)).double().cpu().numpy()
+    g = oracle.gumbel(x)
+    h_ref = -g / math.log(2) - math.log2(math.log(2))
+    err = np.abs(h - h_ref)
+    ulp = np.spacing(np.abs(h_ref).astype(np.float32)).astype(np.float64)
+    _say("gumbel max abs err", err.max(), "max err/ulp(h)", (err / ulp).max())
+    # -log2(u) to ~2 ulp relative plus the rounding of h itself
+    assert np.all(err <= 2.0**-21 + 2 * ulp)
+
+
+# ---------------------------------------------------------------------------------------------
+# soft mask, forward, backward
+
+SAMPLES = [(100.0, 4.0), (100.0, 1.0), (1.0, 1.0), (0.0, 2.0), (30.0, 0.5), (5.0, 0.1)]
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("kappa,tau", SAMPLES)
+def test_soft_mask_matches_oracle(n, m, kappa, tau):
+    rows, gpr = 37, 23
+    _say("soft", n, m, kappa, tau)
+    _, L, _, _, Ld, _ = _inputs(rows, gpr * m, n, m, torch.float32, 1)
+    got = to_f64(S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed=11, offset=3))
+    want = oracle.soft_mask(L, n, m, kappa, tau, 11, 3)
+    rel, bad = soft_mask_check(got, want, m, tol_for_tau(tau))
+    _say("  worst group rel err", rel)
+    assert bad == 0
+    # invariants hold on the GPU too: sum to n, within [0, 1]
+    np.testing.assert_allclose(got.reshape(-1, m).sum(1), n, atol=1e-5 * n)
+    assert got.min() >= 0.0 and got.max() <= 1.0 + 1e-6
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("wtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,gpr", SHAPES)
+def test_forward_matches_oracle(n, m, wtype, rows, gpr):
+    kappa, tau, seed, off = 100.0, 1.0, 5, 9
+    _say("fwd", n, m, wtype, rows, gpr)
+    w, L, _, wd, Ld, _ = _inputs(rows, gpr * m, n, m, wtype, 2)
+    got = to_f64(S.nm_mask_forward(wd, Ld, n, m, kappa, tau, seed, off))
+    want = oracle.forward(w, L, n, m, kappa, tau, seed, off)
+    soft = oracle.soft_mask(L, n, m, kappa, tau, seed, off)
+    rel, bad = forward_check(got, want, w.double().numpy(), soft, m, TOL_FP32,
+                             wtype == torch.bfloat16)
+    _say("  worst rel err", rel)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("wtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,gpr", SHAPES)
+def test_backward_matches_oracle(n, m, wtype, rows, gpr):
+    kappa, tau, seed, off = 100.0, 1.0, 6, 2
+    _say("bwd", n, m, wtype, rows, gpr)
+    w, L, G, wd, Ld, Gd = _inputs(rows, gpr * m, n, m, wtype, 3)
+    got = to_f64(S.nm_mask_backward(wd, Ld, Gd, n, m, kappa, tau, seed, off))
+    want = oracle.backward(w, L, G, n, m, kappa, tau, seed, off)
+    y = oracle.probs(L, n, m, kappa, tau, seed, off)
+    d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
+    rel, bad = backward_check(got, want, y, d, kappa / tau, TOL_FP32)
+    _say("  worst rel err", rel)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("kappa,tau", SAMPLES)
+def test_backward_over_sample_parameters(kappa, tau):
+    n, m, rows, gpr = 2, 4, 16, 64
+    _say("bwd sample", kappa, tau)
+    w, L, G, wd, Ld, Gd = _inputs(rows, gpr * m, n, m, torch.bfloat16, 4)
+    got = to_f64(S.nm_mask_backward(wd, Ld, Gd, n, m, kappa, tau, 1, 1))
+    want = oracle.backward(w, L, G, n, m, kappa, tau, 1, 1)
+    y = oracle.probs(L, n, m, kappa, tau, 1, 1)
+    d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
+    rel, bad = backward_check(got, want, y, d, kappa / tau, tol_for_tau(tau))
+    _say("  worst rel err", rel)
+    assert bad == 0
+
+
+def test_autograd_function_uses_the_same_kernels():
+    n, m, rows, gpr = 2, 4, 8, 16
+    w, L, G, wd, Ld, Gd = _inputs(rows, gpr * m, n, m, torch.bfloat16, 5)
+    Lp = Ld.clone().requires_grad_(True)
+    out = S.mask(wd, Lp, n, m, 100.0, 4.0, 3, 7)
+    out.backward(Gd)
+    assert torch.equal(out, S.nm_mask_forward(wd, Ld, n, m, 100.0, 4.0, 3, 7))
+    assert torch.equal(Lp.grad, S.nm_mask_backward(wd, Ld, Gd, n, m, 100.0, 4.0, 3, 7))
+
+
+def test_forward_and_backward_are_deterministic_and_fresh_per_step():
+    n, m = 2, 4
+    _, _, _, wd, Ld, Gd = _inputs(32, 256, n, m, torch.bfloat16, 6)
+    a = S.nm_mask_forward(wd, Ld, n, m, 1.0, 1.0, 3, 0)
+    b = S.nm_mask_forward(wd, Ld, n, m, 1.0, 1.0, 3, 0)
+    c = S.nm_mask_forward(wd, Ld, n, m, 1.0, 1.0, 3, 1)
+    assert torch.equal(a, b) and not torch.equal(a, c)
+
+
+# ---------------------------------------------------------------------------------------------
+# hard mask, pack, unpack: bit-exact
+
+def _bits(t):
+    return t.cpu().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy()
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("wtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,gpr", SHAPES + [(5, 41)])
+def test_harden_pack_unpack_are_bit_exact(n, m, wtype, rows, gpr):
+    _say("pack", n, m, wtype, rows, gpr)
+    w, L, _, wd, Ld, _ = _inputs(rows, gpr * m, n, m, wtype, 7)
+    w[0, :m] = -0.0
+    L[0, 0, :] = 1.0                      # all tied: candidate 0
+    if gpr > 1:
+        L[0, 1, 0] = float("nan")         # NaN at 0: stays candidate 0
+    if gpr > 2:
+        L[0, 2, -1] = float("nan")        # NaN elsewhere: skipped
+    wd, Ld = w.to(DEV), L.to(DEV)
+    values, indices, hard = S.nm_mask_harden_pack(wd, Ld, n, m, with_hard=True)
+    rv, ri, rh = oracle.pack(w, L, n, m)
+    np.testing.assert_array_equal(hard.cpu().numpy(), rh)
+    np.testing.assert_array_equal(indices.cpu().numpy().view(np.uint32), ri)
+    np.testing.assert_array_equal(_bits(values), oracle._np(rv).view(_bits(values).dtype))
+    dense = S.nm_unpack(values, indices, gpr * m, n, m)
+    rd = oracle.unpack(rv, ri, gpr * m, n, m)
+    np.testing.assert_array_equal(_bits(dense), rd.view(_bits(dense).dtype))
+    # without the optional hard-index output the packed data is the same
+    v2, i2 = S.nm_mask_harden_pack(wd, Ld, n, m)
+    assert torch.equal(_bits_t(v2), _bits_t(values)) and torch.equal(i2, indices)
+
+
+def _bits_t(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (3, 8)])
+def test_unpack_of_malformed_metadata_matches_oracle(n, m):
+    rows, gpr = 6, 19
+    wpr = S.index_words_per_row(gpr * m, n, m)
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 2**32, size=(rows, wpr), dtype=np.uint64).astype(np.uint32)
+    vals = nm_synth.normal((rows, gpr * n), 1.0, 8, torch.bfloat16)
+    got = S.nm_unpack(vals.to(DEV), torch.from_numpy(idx.view(np.int32)).to(DEV), gpr * m, n, m)
+    want = oracle.unpack(vals, idx, gpr * m, n, m)
+    np.testing.assert_array_equal(_bits(got), want.view(np.int16))
+
+
+# ---------------------------------------------------------------------------------------------
+# edge cases of the binding
+
+def test_empty_matrices():
+    for n, m in [(2, 4), (4, 8)]:
+        K = S.num_candidates(n, m)
+        w = torch.empty((0, 8 * m), dtype=torch.bfloat16, device=DEV)
+        L = torch.empty((0, 8, K), device=DEV)
+        assert S.nm_mask_forward(w, L, n, m, 1.0, 1.0, 0, 0).shape == (0, 8 * m)
+        assert S.nm_mask_backward(w, L, w, n, m, 1.0, 1.0, 0, 0).shape == (0, 8, K)
+        v, i = S.nm_mask_harden_pack(w, L, n, m)
+        assert v.numel() == 0 and i.numel() == 0
+
+
+def test_misaligned_views_are_refused():
+    n, m = 2, 4
+    base = torch.zeros(4 * 64 + 2, dtype=torch.bfloat16, device=DEV)
+    w = base[2:].view(4, 64)              # 4-byte offset
+    L = torch.zeros(4, 16, 6, device=DEV)
+    with pytest.raises(S.NMError) as e:
+        S.nm_mask_forward(w, L, n, m, 1.0, 1.0, 0, 0)
+    assert e.value.status == S.NM_EALIGN
