@@ -23,10 +23,10 @@
  *   logits     fp32 [rows, cols/m, K], K contiguous: logit k of group g is logits[g*K + k].
  *   noise      candidate slot i = g*K + k uses word (i & 3) of the Philox4x32-10 block (Salmon et
  *              al., SC'11) with key (seed lo, seed hi) and counter ((i>>2) lo, (i>>2) hi,
- *              offset lo, offset hi).  Its top 24 bits j give u = (j + 1/2) / 2^24 and the
- *              Gumbel sample g = -ln(-ln u).  offset is the training step: forward and backward
- *              of one step pass the same (seed, offset), and the backward regenerates the noise
- *              instead of reading it from memory.
+ *              offset lo, offset hi).  Its top 23 bits j give u = (j + 1/2) / 2^23 (exact in
+ *              fp32) and the Gumbel sample g = -ln(-ln u).  offset is the training step:
+ *              forward and backward of one step pass the same (seed, offset), and the backward
+ *              regenerates the noise instead of reading it from memory.
  *   sample     y_k = softmax_k((kappa*l_k + g_k) / tau); soft mask m_j = sum of y_k over the
  *              candidates k that keep position j (so m_j is in [0,1] and sums to n per group).
  *   hard mask  the candidate with the largest logit (no noise; the first one on exact ties).
@@ -144,7 +144,7 @@ const char *nm_status_str(nm_status status);
 /* Raw noise words [rows*cols/m, K] (uint32) of a sample; kappa and tau are not used. */
 nm_status nm_debug_noise(const nm_shape *shape, const nm_sample *sample, uint32_t *words,
                          void *stream);
-/* Base-2 Gumbel exponent of noise words: h = log2(-log2(u)), u = ((x >> 8) + 1/2) / 2^24, so
+/* Base-2 Gumbel exponent of noise words: h = log2(-log2(u)), u = ((x >> 9) + 1/2) / 2^23, so
  * that the Gumbel sample is g = -ln(2) * (h + log2(ln 2)).  words and h hold count elements. */
 nm_status nm_debug_gumbel_log2(const uint32_t *words, float *h, int64_t count, void *stream);
 /* Soft mask [rows, cols] fp32 of a sample (the forward's m before the multiply). */

@@ -105,9 +105,10 @@ void ref_noise_words(uint64_t seed, uint64_t offset, uint64_t first, int64_t cou
     for (int64_t j = 0; j < count; ++j) words[j] = ref_noise_word(seed, offset, first + (uint64_t)j);
 }
 
-/* Uniform in (0,1) from the top 24 bits of a word, at the midpoint of its 2^-24 cell (a
- * reading): never 0 or 1, so both logarithms below are finite. */
-double ref_uniform(uint32_t x) { return ((double)(x >> 8) + 0.5) * 0x1p-24; }
+/* Uniform in (0,1) from the top 23 bits j of a word, at the midpoint of its 2^-23 cell:
+ * u = (2j + 1) / 2^24 (a reading: the pages fix no bit width; 23 bits make every u exactly
+ * representable in binary32 as well).  Never 0 or 1, so both logarithms below are finite. */
+double ref_uniform(uint32_t x) { return ((double)(x >> 9) + 0.5) * 0x1p-23; }
 
 /* Gumbel(0,1) by inverting its CDF F(g) = exp(-exp(-g)). */
 double ref_gumbel(uint32_t x) {

@@ -24,7 +24,7 @@
  *
  * Readings of points the pages leave open (N = number kept; groups along the contiguous input
  * dimension; lexicographic candidate order; fp32 logits [rows, cols/M, K]; z = (kappa*l+g)/tau;
- * Philox counter map; 24-bit midpoint uniforms; argmax of the logits for the hard mask with the
+ * Philox counter map; 23-bit midpoint uniforms; argmax of the logits for the hard mask with the
  * first maximum winning; little-endian per-row index bitstream) are listed with each function.
  *
  * Parity pins: every function below is pinned by tests/test_oracle_*.py against library
@@ -67,7 +67,7 @@ uint32_t ref_noise_word(uint64_t seed, uint64_t offset, uint64_t i);
 /* words[j] = ref_noise_word(seed, offset, first + j) for j < count */
 void ref_noise_words(uint64_t seed, uint64_t offset, uint64_t first, int64_t count,
                      uint32_t *words);
-/* u = ((x >> 8) + 1/2) / 2^24, exact in binary64, in (0, 1). */
+/* u = ((x >> 9) + 1/2) / 2^23, exact in binary64 (and in binary32), in (0, 1). */
 double ref_uniform(uint32_t x);
 /* Standard Gumbel(0,1) sample by the inverse CDF: g = -ln(-ln u). */
 double ref_gumbel(uint32_t x);

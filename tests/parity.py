@@ -31,26 +31,25 @@ def to_f64(t):
     return t.detach().double().cpu().numpy()
 
 
+def _verdict(err, bound):
+    """(largest err/bound, number of elements over their bound); a ratio <= 1 passes."""
+    ratio = err / np.maximum(bound, 1e-300)
+    return float(ratio.max(initial=0.0)), int((err > bound).sum())
+
+
 def soft_mask_check(gpu, ref, m, tol):
-    """Returns (worst relative group error, number of groups over tol)."""
     g = np.asarray(gpu, np.float64).reshape(-1, m)
     r = np.asarray(ref, np.float64).reshape(-1, m)
-    err = np.abs(g - r).max(1)
-    scale = np.abs(r).max(1)
-    rel = err / np.maximum(scale, 1e-300)
-    return float(rel.max(initial=0.0)), int((err > tol * scale).sum())
+    return _verdict(np.abs(g - r).max(1), tol * np.abs(r).max(1))
 
 
 def forward_check(gpu, ref, w, soft_ref, m, tol, bf16):
-    """gpu: float64 array of the GPU output; ref: oracle float64; w: float64 weights."""
+    """gpu: float64 array of the GPU output; ref: oracle float64; w: float64 weights.
+    Returns (largest error / allowed error, number of elements over it)."""
     gpu = np.asarray(gpu, np.float64)
     mmax = np.repeat(np.abs(soft_ref).reshape(-1, m).max(1), m).reshape(ref.shape)
     out_round = (TOL_BF16 if bf16 else 2.0**-24) * np.abs(ref)
-    bound = tol * mmax * np.abs(w) + out_round
-    err = np.abs(gpu - ref)
-    scale = mmax * np.abs(w) + np.abs(ref)
-    rel = err / np.maximum(scale, 1e-300)
-    return float(rel.max(initial=0.0)), int((err > bound).sum())
+    return _verdict(np.abs(gpu - ref), tol * mmax * np.abs(w) + out_round)
 
 
 def backward_check(gpu, ref, y, d, c, tol):
@@ -58,10 +57,8 @@ def backward_check(gpu, ref, y, d, c, tol):
     gpu = np.asarray(gpu, np.float64)
     ad = np.abs(d)
     terms = c * y * (ad + (y * ad).sum(-1, keepdims=True))
-    floor = c * 1e-36 * ad.max(-1, keepdims=True)
-    err = np.abs(gpu - ref)
-    rel = err / np.maximum(terms + floor, 1e-300)
-    return float(rel.max(initial=0.0)), int((err > tol * terms + floor).sum())
+    floor = c * 1e-36 * ad.max(-1, keepdims=True)  # probabilities near the fp32 underflow
+    return _verdict(np.abs(gpu - ref), tol * terms + floor)
 
 
 def candidate_sums(w, grad, n, m, cand_matrix):

@@ -93,7 +93,7 @@ def test_soft_mask_matches_oracle(n, m, kappa, tau):
     got = to_f64(S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed=11, offset=3))
     want = oracle.soft_mask(L, n, m, kappa, tau, 11, 3)
     rel, bad = soft_mask_check(got, want, m, tol_for_tau(tau))
-    _say("  worst group rel err", rel)
+    _say("  worst err/bound", rel)
     assert bad == 0
     # invariants hold on the GPU too: sum to n, within [0, 1]
     np.testing.assert_allclose(got.reshape(-1, m).sum(1), n, atol=1e-5 * n)
@@ -112,7 +112,7 @@ def test_forward_matches_oracle(n, m, wtype, rows, gpr):
     soft = oracle.soft_mask(L, n, m, kappa, tau, seed, off)
     rel, bad = forward_check(got, want, w.double().numpy(), soft, m, TOL_FP32,
                              wtype == torch.bfloat16)
-    _say("  worst rel err", rel)
+    _say("  worst err/bound", rel)
     assert bad == 0
 
 
@@ -128,7 +128,7 @@ def test_backward_matches_oracle(n, m, wtype, rows, gpr):
     y = oracle.probs(L, n, m, kappa, tau, seed, off)
     d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
     rel, bad = backward_check(got, want, y, d, kappa / tau, TOL_FP32)
-    _say("  worst rel err", rel)
+    _say("  worst err/bound", rel)
     assert bad == 0
 
 
@@ -142,7 +142,7 @@ def test_backward_over_sample_parameters(kappa, tau):
     y = oracle.probs(L, n, m, kappa, tau, 1, 1)
     d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
     rel, bad = backward_check(got, want, y, d, kappa / tau, tol_for_tau(tau))
-    _say("  worst rel err", rel)
+    _say("  worst err/bound", rel)
     assert bad == 0
 
 

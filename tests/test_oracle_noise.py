@@ -105,23 +105,27 @@ def test_noise_streams_differ_by_seed_and_offset():
 
 # --- uniform and Gumbel ----------------------------------------------------------------------
 
-def test_uniform_uses_top_24_bits_at_cell_midpoints():
-    for hi in [0, 1, 2**23, 2**24 - 1]:
-        for lo in [0, 1, 0x7F, 0xFF]:
-            assert oracle.uniform((hi << 8) | lo) == (hi + 0.5) / 2**24
+def test_uniform_uses_top_23_bits_at_cell_midpoints():
+    for hi in [0, 1, 2**22, 2**23 - 1]:
+        for lo in [0, 1, 0xFF, 0x1FF]:
+            assert oracle.uniform((hi << 9) | lo) == (hi + 0.5) / 2**23
     assert 0.0 < oracle.uniform(0) and oracle.uniform(0xFFFFFFFF) < 1.0
+    # every uniform is a binary32 number: 2j+1 < 2^24
+    for x in [0, 0x7FFFFE00, 0xFFFFFE00, 0xFFFFFFFF]:
+        u = oracle.uniform(x)
+        assert float(np.float32(u)) == u
 
 
 @pytest.fixture(scope="module")
 def gumbel_grid():
-    j = np.arange(1 << 24, dtype=np.uint32)
-    return j, oracle.gumbel(j << np.uint32(8))
+    j = np.arange(1 << 23, dtype=np.uint32)
+    return j, oracle.gumbel(j << np.uint32(9))
 
 
 def test_gumbel_is_the_inverse_cdf_exhaustively(gumbel_grid):
-    """All 2^24 uniforms: g equals scipy's Gumbel(0,1) quantile of u."""
+    """All 2^23 uniforms: g equals scipy's Gumbel(0,1) quantile of u."""
     j, g = gumbel_grid
-    u = (j.astype(np.float64) + 0.5) / 2**24
+    u = (j.astype(np.float64) + 0.5) / 2**23
     want = scipy.stats.gumbel_r.ppf(u)
     np.testing.assert_allclose(g, want, rtol=2e-15, atol=2e-15)
 
@@ -130,13 +134,13 @@ def test_gumbel_grid_moments_and_range(gumbel_grid):
     """Mean -> Euler-Mascheroni gamma, variance -> pi^2/6; range fixed by the end cells."""
     _, g = gumbel_grid
     assert abs(g.mean() - np.euler_gamma) < 1e-5
-    assert abs(g.var() - math.pi**2 / 6) < 1e-4
-    assert g.min() == pytest.approx(-math.log(25 * math.log(2)), rel=1e-9)
-    assert g.max() == pytest.approx(-math.log(-math.log1p(-2.0**-25)), rel=1e-9)
+    assert abs(g.var() - math.pi**2 / 6) < 2e-4
+    assert g.min() == pytest.approx(-math.log(24 * math.log(2)), rel=1e-9)
+    assert g.max() == pytest.approx(-math.log(-math.log1p(-2.0**-24)), rel=1e-9)
     assert np.all(np.diff(g) > 0)  # strictly increasing in u
 
 
-def test_gumbel_ignores_low_byte():
-    x = np.array([0x12345600, 0x123456FF, 0x12345680], np.uint32)
+def test_gumbel_ignores_low_nine_bits():
+    x = np.array([0x12345600, 0x123457FF, 0x12345680], np.uint32)
     g = oracle.gumbel(x)
     assert g[0] == g[1] == g[2]
