@@ -45,7 +45,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=0, help="rows per matrix in the CPU sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="least CPU time of the baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run 4 plain 1 GiB device copies (counter calibration under a profiler)")
     return p.parse_args()
 
 
@@ -89,32 +91,36 @@ def step_all(S, mats, step):
             run_pass(S, mt, p, step)
 
 
-def cpu_baseline(rows_per_matrix):
-    """The oracle on the first rows of each matrix of the layer (same shapes and generators,
-    CPU copies): forward, backward, pack and unpack.  Returns weights/s of whole steps."""
+def cpu_baseline(min_seconds=10.0, max_passes=8):
+    """The oracle over the same layer (same shapes, generators and parameters, CPU copies):
+    forward, backward, pack and unpack of all seven matrices, repeated over successive steps
+    until at least `min_seconds` of CPU time has been spent.  Returns weights/s of whole steps."""
     import torch
 
     import nm_synth
     import oracle
     threads = min(16, os.cpu_count() or 1)
-    total_w, elapsed = 0, 0.0
+    mats = []
     for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
         seed = nm_synth.input_seed(2, 0, i)
-        r = min(rows, rows_per_matrix)
-        w = nm_synth.normal((r, cols), 0.02, 3 * seed, torch.bfloat16)
-        L = nm_synth.prior_logits(w, N, M, 3 * seed + 1)
-        G = nm_synth.normal((r, cols), 1.0, 3 * seed + 2, torch.bfloat16)
-        t0 = time.perf_counter()
-        oracle.forward(w, L, N, M, KAPPA, TAU, seed, 0, rows=rows, nthreads=threads)
-        oracle.backward(w, L, G, N, M, KAPPA, TAU, seed, 0, rows=rows, nthreads=threads)
-        v, idx, _ = oracle.pack(w, L, N, M, nthreads=threads)
-        oracle.unpack(v, idx, cols, N, M, nthreads=threads)
-        elapsed += time.perf_counter() - t0
-        total_w += r * cols
+        w = nm_synth.normal((rows, cols), 0.02, 3 * seed, torch.bfloat16)
+        mats.append((seed, cols, w, nm_synth.prior_logits(w, N, M, 3 * seed + 1),
+                     nm_synth.normal((rows, cols), 1.0, 3 * seed + 2, torch.bfloat16)))
+    total_w, elapsed, passes = 0, 0.0, 0
+    while passes < max_passes and (passes == 0 or elapsed < min_seconds):
+        for seed, cols, w, L, G in mats:
+            t0 = time.perf_counter()
+            oracle.forward(w, L, N, M, KAPPA, TAU, seed, passes, nthreads=threads)
+            oracle.backward(w, L, G, N, M, KAPPA, TAU, seed, passes, nthreads=threads)
+            v, idx, _ = oracle.pack(w, L, N, M, nthreads=threads)
+            oracle.unpack(v, idx, cols, N, M, nthreads=threads)
+            elapsed += time.perf_counter() - t0
+            total_w += w.numel()
+        passes += 1
     return {"value": total_w / elapsed, "unit": "weights/s", "cores": oracle.threads_used(threads),
             "kind": "oracle",
-            "sample": f"first {rows_per_matrix} rows of each of the 7 matrices ({total_w} weights), "
-                      f"fwd+bwd+harden_pack+unpack, binary64, {elapsed:.1f} s"}
+            "sample": f"{passes} step(s) of the whole layer ({total_w} weight-passes): "
+                      f"fwd+bwd+harden_pack+unpack in binary64 on {threads} threads, {elapsed:.1f} s"}
 
 
 def main():
@@ -130,6 +136,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     mats = make_layer(dev)
     torch.cuda.synchronize()
     weights = nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
@@ -208,8 +221,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or 4096
-        result["cpu_baseline"] = cpu_baseline(rows)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "nm_kernels.hpp"
 
 namespace nm {
@@ -55,6 +57,30 @@ struct Candidates {
     }
 };
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.  Candidate membership
+// tests inside it are constant expressions, so they vanish from the generated code instead of
+// becoming run-time bit tests and selects.
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Lambda bodies of static_for are always inlined, so the arrays they reach stay in registers.
+#define NM_INLINE __attribute__((always_inline))
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Bit pattern of candidate k (k-th n-subset in lexicographic order) as a constant expression.
+template <int N, int M, int k>
+constexpr uint32_t cand_keep() {
+    constexpr uint32_t bits = Candidates<N, M>{}.keep[k];  // evaluated by the compiler
+    return bits;
+}
+
 // Groups per thread in the sampling kernels: enough for the thread's candidate slots to fill
 // whole Philox blocks when K is not a multiple of 4 (K = 6 -> 2 groups = 3 blocks).  K = 70 is
 // handled with one group per thread and a 0-or-2 word phase instead (2 groups would keep 280
@@ -99,25 +125,15 @@ __device__ __forceinline__ Philox4 noise_block(const NoiseKey& nk, uint64_t b) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Gumbel noise in base 2.  The sample is g = -ln(-ln u) with u = (j + 1/2) 2^-24, j = x >> 8.
+// Gumbel noise in base 2.  The sample is g = -ln(-ln u) with u = (j + 1/2) 2^-23, j = x >> 9.
 // Writing a = -log2(u) gives g = -ln2 * (log2(a) + log2(ln2)); the constant cancels in the
 // softmax, so the kernels work with h = log2(a) and z' = z * log2(e) = A*l - B*h + const, with
-// A = kappa*log2(e)/tau and B = 1/tau.
-//
-// u needs 25 significant bits when u >= 1/2, so fp32 cannot hold it; rounding it would put an
-// absolute error of 2^-25 into u, which near u = 1 is a large relative error of a (and an
-// unbounded one at u = 1 - 2^-25, which rounds to 1).  The transform therefore keeps
-// u = u_hi + r exactly (u_hi = fl32(u), r in {0, +-2^-25}) and uses
-//     -log2(u) = -log2(u_hi) - log2(1 + r/u_hi) ~= -log2(u_hi) - r*log2(e)*(2 - u_hi),
-// where 2 - u_hi stands in for 1/u_hi on [1/2, 1] (r = 0 below 1/2).  v_log_f32 is within
-// 1 ulp (relative) for the normal inputs used here.
+// A = kappa*log2(e)/tau and B = 1/tau.  u = (2j + 1) 2^-24 is exact in fp32, and v_log_f32 is
+// within about 1 ulp (relative) for normal inputs, also just below 1 where a is tiny, so
+// h is accurate to a few ulp everywhere.
 __device__ __forceinline__ float gumbel_log2(uint32_t x) {
-    const float jf = (float)(x >> 8);                           // exact: j < 2^24
-    const float u_hi = fmaf(jf, 0x1p-24f, 0x1p-25f);            // fl32(u)
-    const float r = fmaf(jf, 0x1p-24f, -u_hi) + 0x1p-25f;       // u - u_hi, exact
-    const float corr = (r * 1.4426950408889634f) * (2.0f - u_hi);
-    const float a = -(__builtin_amdgcn_logf(u_hi) + corr);      // -log2(u) > 0
-    return __builtin_amdgcn_logf(a);
+    const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);  // exact
+    return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -136,6 +152,23 @@ struct BF16 {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Streaming stores: outputs are written once and not read again by the same kernel, so they
+// are stored non-temporally (they are not kept in the caches at the expense of the inputs).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void nt_store(void* p, uint4 v) {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void nt_store(void* p, uint2 v) {
+    const u32x2_t x = {v.x, v.y};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void nt_store(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
 
 // Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -201,7 +234,9 @@ __device__ __forceinline__ void store_from_float(typename T::storage* __restrict
         if (vec && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i)
-                reinterpret_cast<float4*>(p)[i] = make_float4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+                nt_store(reinterpret_cast<uint4*>(p) + i,
+                         make_uint4(__float_as_uint(in[4 * i]), __float_as_uint(in[4 * i + 1]),
+                                    __float_as_uint(in[4 * i + 2]), __float_as_uint(in[4 * i + 3])));
             return;
         }
 #pragma unroll
@@ -211,16 +246,16 @@ __device__ __forceinline__ void store_from_float(typename T::storage* __restrict
         if (vec && CNT % 8 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 8; ++i)
-                reinterpret_cast<uint4*>(p)[i] =
-                    make_uint4(pack_bf16x2(in[8 * i], in[8 * i + 1]), pack_bf16x2(in[8 * i + 2], in[8 * i + 3]),
-                               pack_bf16x2(in[8 * i + 4], in[8 * i + 5]), pack_bf16x2(in[8 * i + 6], in[8 * i + 7]));
+                nt_store(reinterpret_cast<uint4*>(p) + i,
+                         make_uint4(pack_bf16x2(in[8 * i], in[8 * i + 1]), pack_bf16x2(in[8 * i + 2], in[8 * i + 3]),
+                                    pack_bf16x2(in[8 * i + 4], in[8 * i + 5]), pack_bf16x2(in[8 * i + 6], in[8 * i + 7])));
             return;
         }
         if (vec && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i)
-                reinterpret_cast<uint2*>(p)[i] =
-                    make_uint2(pack_bf16x2(in[4 * i], in[4 * i + 1]), pack_bf16x2(in[4 * i + 2], in[4 * i + 3]));
+                nt_store(reinterpret_cast<uint2*>(p) + i,
+                         make_uint2(pack_bf16x2(in[4 * i], in[4 * i + 1]), pack_bf16x2(in[4 * i + 2], in[4 * i + 3])));
             return;
         }
 #pragma unroll

@@ -43,7 +43,9 @@ __device__ __forceinline__ void store_f32(float* __restrict__ p, bool vec, int v
         if constexpr (ALIGN == 16 && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i)
-                reinterpret_cast<float4*>(p)[i] = make_float4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+                nt_store(reinterpret_cast<uint4*>(p) + i,
+                         make_uint4(__float_as_uint(in[4 * i]), __float_as_uint(in[4 * i + 1]),
+                                    __float_as_uint(in[4 * i + 2]), __float_as_uint(in[4 * i + 3])));
         } else {
 #pragma unroll
             for (int i = 0; i < CNT / 2; ++i) reinterpret_cast<float2*>(p)[i] = make_float2(in[2 * i], in[2 * i + 1]);
@@ -60,22 +62,22 @@ __device__ __forceinline__ void store_f32(float* __restrict__ p, bool vec, int v
 //
 // MaskLLM project page, Fig. 3 caption (Gumbel softmax over the candidates of each group) and
 // Fig. 5 caption (kappa scales the logits): y_k = softmax_k((kappa*l_k + g_k)/tau).  In base 2,
-// z'_k = A*l_k - B*h_k (see gumbel_log2).  The exponent of each candidate is formed as a
-// difference to a reference candidate r (the largest z'):
-//     d_k = A*(l_k - l_r) + B*(h_r - h_k),
-// so its rounding error is relative to |d_k| rather than to |A*l_k|; A*|l| reaches several
-// hundred at kappa = 100 while the differences that matter are small.  e_k = 2^(d_k) <= 1 up to
-// rounding, S = sum e_k >= 1, y_k = e_k / S.
+// z'_k = A*l_k - B*h_k (see gumbel_log2).  A*|l| reaches several hundred at kappa = 100 while the
+// differences between candidates that matter are small, so z'_k is carried as an fp32 head
+// hi_k = fl(A*l_k - B*h_k) plus the remainder rem_k = (A*l_k - hi_k) - B*h_k that the fma leaves
+// (exact up to the rounding of B*h_k).  With mu = max_k hi_k, e_k = 2^((hi_k - mu) + rem_k): the
+// rounding errors are relative to |z'_k - mu| rather than to |A*l_k|, and mu cancels in y.
 
 template <int N, int M>
 struct Sample {
-    static constexpr Candidates<N, M> C{};
     static constexpr int K = Candidates<N, M>::K;
     static constexpr int P = SlotTiling<K>::P;
     static constexpr int PK = P * K;
     static constexpr int PH = SlotTiling<K>::phased ? 2 : 0;  // extra words of a phased tile
     static constexpr int NB = (PK + PH + 3) / 4;              // Philox blocks per thread
     static constexpr int LALIGN = (PK * 4) % 16 == 0 ? 16 : 8; // byte alignment of a thread's logits
+    // stage logit-gradient stores through LDS when a thread's share is 2 to 4 16-byte vectors
+    static constexpr bool STAGE = LALIGN == 16 && PK >= 8 && PK <= 16;
 };
 
 // h[i] for the thread's slots i = 0 .. PK-1 (slot index relative to g0*K).  Each Philox block
@@ -109,29 +111,106 @@ __device__ __forceinline__ void thread_noise(const NoiseKey& nk, int64_t g0, flo
     }
 }
 
-// For group p of the thread: e[k] = 2^(d_k) and the inverse normaliser.
+// For group p of the thread: e[k] = 2^(z'_k - mu) (unnormalised probabilities).
 template <int N, int M>
-__device__ __forceinline__ float group_exp(const float* l, const float* h, float A, float B,
-                                           float (&e)[Candidates<N, M>::K]) {
+__device__ __forceinline__ void group_exp(const float* l, const float* h, float A, float B,
+                                          float (&e)[Candidates<N, M>::K]) {
     constexpr int K = Candidates<N, M>::K;
-    float zr = fmaf(A, l[0], -B * h[0]);
-    float lr = l[0], hr = h[0];
-#pragma unroll
-    for (int k = 1; k < K; ++k) {
-        const float z = fmaf(A, l[k], -B * h[k]);
-        const bool up = z > zr;
-        zr = up ? z : zr;
-        lr = up ? l[k] : lr;
-        hr = up ? h[k] : hr;
-    }
-    float s = 0.0f;
+    float hi[K], rem[K];
+    float mu = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const float d = fmaf(A, l[k] - lr, B * (hr - h[k]));
-        e[k] = exp2_fast(d);
-        s += e[k];
+        const float bh = B * h[k];
+        hi[k] = fmaf(A, l[k], -bh);
+        rem[k] = fmaf(A, l[k], -hi[k]) - bh;
+        mu = fmaxf(mu, hi[k]);
     }
-    return __builtin_amdgcn_rcpf(s);  // s in [1, K]: v_rcp_f32 is within 1 ulp
+#pragma unroll
+    for (int k = 0; k < K; ++k) e[k] = exp2_fast((hi[k] - mu) + rem[k]);
+}
+
+// Soft-mask sums s_j = sum over candidates k keeping j of e_k, and 1/S with S = sum_k e_k:
+// every candidate keeps N positions, so sum_j s_j = N * S.
+template <int N, int M>
+__device__ __forceinline__ float group_soft(const float (&e)[Candidates<N, M>::K], float (&sj)[M]) {
+    constexpr int K = Candidates<N, M>::K;
+    float tot = 0.0f;
+    static_for<0, M>([&](auto jc) NM_INLINE {
+        constexpr int j = decltype(jc)::value;
+        float acc = 0.0f;
+        static_for<0, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
+            if constexpr ((cand_keep<N, M, k>() >> j) & 1u) acc += e[k];
+        });
+        sj[j] = acc;
+        tot += acc;
+    });
+    return __builtin_amdgcn_rcpf(tot * (1.0f / N));  // S >= 1 (the largest e_k is ~1): rcp within 1 ulp
+}
+
+// ------------------------------------------------------------------------------------------
+// Block staging of logits and logit gradients through LDS.  A thread's PK floats are contiguous,
+// but lanes are PK*4 bytes apart, so direct 16-byte accesses would touch partly used cache lines
+// in every instruction.  In a block whose tiles are all present, the block's logits are moved as
+// one contiguous span with every lane on consecutive 16-byte vectors, and exchanged through an
+// LDS tile.  Partial blocks (the last one) use direct accesses.
+
+template <int N, int M>
+struct StageTile {
+    using S = Sample<N, M>;
+    static constexpr int VEC = S::STAGE ? kThreads * S::PK / 4 : 1;  // float4 slots
+};
+
+template <int N, int M>
+__device__ __forceinline__ bool block_full(int64_t groups) {
+    return ((int64_t)blockIdx.x + 1) * kThreads * Sample<N, M>::P <= groups;
+}
+
+template <int N, int M>
+__device__ __forceinline__ void load_logits(const float* logits, int64_t g0, bool full, int nvalid, bool staged,
+                                            float4* tile, float (&l)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    constexpr int PK = S::PK, V = PK / 4;
+    if constexpr (S::STAGE) {
+        if (staged) {
+            const float4* src = reinterpret_cast<const float4*>(logits + (int64_t)blockIdx.x * kThreads * PK);
+#pragma unroll
+            for (int i = 0; i < V; ++i) tile[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float4 v = tile[threadIdx.x * V + i];
+                l[4 * i] = v.x; l[4 * i + 1] = v.y; l[4 * i + 2] = v.z; l[4 * i + 3] = v.w;
+            }
+            return;
+        }
+    }
+    load_f32<PK, S::LALIGN>(logits + g0 * S::K, full, nvalid * S::K, l);
+}
+
+template <int N, int M>
+__device__ __forceinline__ void store_dlogits(float* dlogits, int64_t g0, bool full, int nvalid, bool staged,
+                                              float4* tile, const float (&dl)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    constexpr int PK = S::PK, V = PK / 4;
+    if constexpr (S::STAGE) {
+        if (staged) {
+            __syncthreads();  // every thread has read its logits out of the tile
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                tile[threadIdx.x * V + i] = make_float4(dl[4 * i], dl[4 * i + 1], dl[4 * i + 2], dl[4 * i + 3]);
+            __syncthreads();
+            float4* dst = reinterpret_cast<float4*>(dlogits + (int64_t)blockIdx.x * kThreads * PK);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float4 v = tile[threadIdx.x + i * kThreads];
+                nt_store(dst + threadIdx.x + i * kThreads,
+                         make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+            }
+            return;
+        }
+    }
+    store_f32<PK, S::LALIGN>(dlogits + g0 * S::K, full, nvalid * S::K, dl);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -148,8 +227,10 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
 
+    __shared__ float4 tile[StageTile<N, M>::VEC];
+    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
-    load_f32<PK, S::LALIGN>(a.logits + g0 * K, full, nvalid * K, l);
+    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
     float w[P * M];
     if constexpr (MODE == 0)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
@@ -159,15 +240,12 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     float out[P * M];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        float e[K];
-        const float inv = group_exp<N, M>(l + p * K, h + p * K, a.A, a.B, e);
+        float e[K], sj[M];
+        group_exp<N, M>(l + p * K, h + p * K, a.A, a.B, e);
+        const float inv = group_soft<N, M>(e, sj);
 #pragma unroll
         for (int j = 0; j < M; ++j) {
-            float sj = 0.0f;
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-                if (S::C.kept(k, j)) sj += e[k];
-            const float mj = sj * inv;
+            const float mj = sj[j] * inv;
             out[p * M + j] = MODE == 0 ? w[p * M + j] * mj : mj;
         }
     }
@@ -193,8 +271,10 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
 
+    __shared__ float4 tile[StageTile<N, M>::VEC];
+    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
-    load_f32<PK, S::LALIGN>(a.logits + g0 * K, full, nvalid * K, l);
+    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
     float w[P * M], gw[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.grad) + g0 * M, full, nvalid * M, gw);
@@ -204,28 +284,30 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     float dl[PK];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        float e[K];
-        const float inv = group_exp<N, M>(l + p * K, h + p * K, a.A, a.B, e);
+        float e[K], sj[M];
+        group_exp<N, M>(l + p * K, h + p * K, a.A, a.B, e);
+        const float inv = group_soft<N, M>(e, sj);
         float aj[M];
 #pragma unroll
         for (int j = 0; j < M; ++j) aj[j] = gw[p * M + j] * w[p * M + j];
         float d[K];
         float es = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
+        static_for<0, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
             float dk = 0.0f;
-#pragma unroll
-            for (int j = 0; j < M; ++j)
-                if (S::C.kept(k, j)) dk += aj[j];
+            static_for<0, M>([&](auto jc) NM_INLINE {
+                constexpr int j = decltype(jc)::value;
+                if constexpr ((cand_keep<N, M, k>() >> j) & 1u) dk += aj[j];
+            });
             d[k] = dk;
             es = fmaf(e[k], dk, es);
-        }
+        });
         const float s = es * inv;
         const float ci = a.C * inv;
 #pragma unroll
         for (int k = 0; k < K; ++k) dl[p * K + k] = (ci * e[k]) * (d[k] - s);
     }
-    store_f32<PK, S::LALIGN>(a.dlogits + g0 * K, full, nvalid * K, dl);
+    store_dlogits<N, M>(a.dlogits, g0, full, nvalid, staged, tile, dl);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -244,114 +326,344 @@ struct PackTiling {
     static constexpr int WPC = CHUNK_BITS / 32;                               // words per chunk
 };
 
-// Raw element bits (bit copies: the packed values keep NaN payloads and signed zeros).
-template <typename T>
-__device__ __forceinline__ uint32_t load_bits(const typename T::storage* p, int64_t i) {
-    if constexpr (T::bytes == 4) return __float_as_uint(reinterpret_cast<const float*>(p)[i]);
-    else return (uint32_t)p[i];
-}
-template <typename T>
-__device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, uint32_t v) {
-    if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = v;
-    else p[i] = (uint16_t)v;
+// Groups per 16-byte-multiple unit when a group occupies `bytes` bytes (8 B -> 2 groups).
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int unit_groups(int bytes) { return 16 / gcd_c(16, bytes); }
+
+// Raw element bits (bit copies: packed values keep NaN payloads and signed zeros).  CNT elements
+// of T, each zero-extended into a uint32.  vec: the caller guarantees 16-byte alignment, that
+// CNT * bytes is a multiple of 16 and that all CNT elements exist; otherwise element i is read
+// or written only if i < valid.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_raw(const typename T::storage* __restrict__ p, bool vec, int valid,
+                                         uint32_t* out) {
+    static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < CNT * T::bytes / 16; ++i) {
+            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (T::bytes == 4) {
+                    out[4 * i + q] = d[q];
+                } else {
+                    out[8 * i + 2 * q] = d[q] & 0xFFFFu;
+                    out[8 * i + 2 * q + 1] = d[q] >> 16;
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) out[i] = i < valid ? reinterpret_cast<const uint32_t*>(p)[i] : 0u;
+        else out[i] = i < valid ? (uint32_t)p[i] : 0u;
+    }
 }
 
+template <typename T, int CNT>
+__device__ __forceinline__ void store_raw(typename T::storage* __restrict__ p, bool vec, int valid,
+                                          const uint32_t* in) {
+    static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < CNT * T::bytes / 16; ++i) {
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (T::bytes == 4) d[q] = in[4 * i + q];
+                else d[q] = in[8 * i + 2 * q] | (in[8 * i + 2 * q + 1] << 16);
+            }
+            nt_store(reinterpret_cast<uint4*>(p) + i, make_uint4(d[0], d[1], d[2], d[3]));
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if (i < valid) {
+            if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = in[i];
+            else p[i] = (uint16_t)in[i];
+        }
+    }
+}
+
+// Logits of `cnt` groups starting at p (scalar path reads only the first `valid` floats).
+template <int CNT>
+__device__ __forceinline__ void load_logit_unit(const float* __restrict__ p, bool vec, int valid, float* out) {
+    if (vec) {
+        if constexpr (CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i) {
+                const float4 v = reinterpret_cast<const float4*>(p)[i];
+                out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CNT / 2; ++i) {
+                const float2 v = reinterpret_cast<const float2*>(p)[i];
+                out[2 * i] = v.x; out[2 * i + 1] = v.y;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) out[i] = i < valid ? p[i] : 0.0f;
+}
+
+// One group's raw weights (M elements) and the store of N kept values / M dense values, with
+// the widest single access the group's byte size allows when `vec` (rows 16-byte aligned, so a
+// group of 2^i bytes is 2^i-byte aligned); element accesses otherwise.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_group_raw(const typename T::storage* __restrict__ p, bool vec, uint32_t* out) {
+    constexpr int BYTES = CNT * T::bytes;
+    if constexpr (BYTES % 16 == 0) {
+        if (vec) {
+            load_raw<T, CNT>(p, true, CNT, out);
+            return;
+        }
+    } else if constexpr (BYTES == 8) {
+        if (vec) {
+            const uint2 d = *reinterpret_cast<const uint2*>(p);
+            if constexpr (T::bytes == 2) {
+                out[0] = d.x & 0xFFFFu; out[1] = d.x >> 16; out[2] = d.y & 0xFFFFu; out[3] = d.y >> 16;
+            } else {
+                out[0] = d.x; out[1] = d.y;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) out[i] = reinterpret_cast<const uint32_t*>(p)[i];
+        else out[i] = (uint32_t)p[i];
+    }
+}
+
+template <typename T, int CNT>
+__device__ __forceinline__ void store_group_raw(typename T::storage* __restrict__ p, bool vec, const uint32_t* in) {
+    constexpr int BYTES = CNT * T::bytes;
+    if constexpr (BYTES % 16 == 0) {
+        if (vec) {
+            store_raw<T, CNT>(p, true, CNT, in);
+            return;
+        }
+    } else if constexpr (BYTES == 8) {
+        if (vec) {
+            if constexpr (T::bytes == 2) nt_store(p, make_uint2(in[0] | (in[1] << 16), in[2] | (in[3] << 16)));
+            else nt_store(p, make_uint2(in[0], in[1]));
+            return;
+        }
+    } else if constexpr (BYTES == 4) {
+        if (vec) {
+            if constexpr (T::bytes == 2) nt_store(p, in[0] | (in[1] << 16));
+            else nt_store(p, in[0]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = in[i];
+        else p[i] = (uint16_t)in[i];
+    }
+}
+
+// The host sets `aligned` when every row of w, logits, values and dense starts on a 16-byte
+// boundary (then every group of a power-of-two byte size is aligned to that size).  Groups are
+// visited in a run-time loop; index fields go through a 64-bit bit window that is written out a
+// word at a time (a chunk's fields end on a word boundary, the row's last chunk on the row's
+// last word).
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
     using PT = PackTiling<N, M>;
-    constexpr Candidates<N, M> C{};
-    constexpr int K = Candidates<N, M>::K;
+    constexpr int K = Candidates<N, M>::K, GPC = PT::GPC;
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (t >= a.rows * a.chunks_per_row) return;
     const int64_t r = t / a.chunks_per_row;
     const int64_t c = t - r * a.chunks_per_row;
-    const int64_t q0 = c * PT::GPC;                       // first group of the chunk in its row
-    const int ng = (int)(a.gpr - q0 < PT::GPC ? a.gpr - q0 : PT::GPC);
-    const int64_t grow = r * a.gpr;                       // flat index of the row's first group
-    const auto* w = reinterpret_cast<const typename T::storage*>(a.w) + (grow + q0) * M;
-    const float* lg = a.logits + (grow + q0) * K;
-    auto* vals = reinterpret_cast<typename T::storage*>(a.values) + (grow + q0) * N;
-
-    uint32_t acc[PT::WPC];
+    const int64_t q0 = c * GPC;                           // first group of the chunk in its row
+    const int ng = (int)(a.gpr - q0 < GPC ? a.gpr - q0 : GPC);
+    const bool vec = a.aligned != 0;
+    const int64_t g0 = r * a.gpr + q0;                    // flat index of the chunk's first group
+    const auto* w = reinterpret_cast<const typename T::storage*>(a.w) + g0 * M;
+    const float* lg = a.logits + g0 * K;
+    auto* vals = reinterpret_cast<typename T::storage*>(a.values) + g0 * N;
+    uint32_t* idx = a.indices + r * a.words_per_row + c * PT::WPC;
+    uint64_t win = 0;
+    int nb = 0, wi = 0;
+    for (int q = 0; q < ng; ++q) {
+        float l[K];
+        load_f32<K, (K * 4) % 16 == 0 ? 16 : 8>(lg + q * K, vec, K, l);
+        // first largest logit; a NaN never compares greater, so it never displaces candidate 0
+        float best = l[0];
+        int bk = 0;
+        uint32_t keep = cand_keep<N, M, 0>();
+        static_for<1, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
+            const bool up = l[k] > best;
+            best = up ? l[k] : best;
+            bk = up ? k : bk;
+            keep = up ? cand_keep<N, M, k>() : keep;
+        });
+        if (a.hard) a.hard[g0 + q] = (uint8_t)bk;
+        uint32_t raw[M], v[N];
+        load_group_raw<T, M>(w + q * M, vec, raw);
 #pragma unroll
-    for (int i = 0; i < PT::WPC; ++i) acc[i] = 0u;
-
+        for (int tt = 0; tt < N; ++tt) {
+            const int p = __builtin_ctz(keep);  // kept positions in ascending order
+            keep &= keep - 1;
+            uint32_t x = raw[0];
 #pragma unroll
-    for (int q = 0; q < PT::GPC; ++q) {
-        if (q < ng) {  // predicated, so the loop unrolls and bit positions stay compile-time
-            // first largest logit; a NaN never compares greater, so it never displaces candidate 0
-            float best = lg[q * K];
-            int bk = 0;
-            uint32_t keep = C.keep[0];
-#pragma unroll
-            for (int k = 1; k < K; ++k) {
-                const float v = lg[q * K + k];
-                const bool up = v > best;
-                best = up ? v : best;
-                bk = up ? k : bk;
-                keep = up ? (uint32_t)C.keep[k] : keep;
-            }
-            if (a.hard) a.hard[grow + q0 + q] = (uint8_t)bk;
-            uint32_t raw[M];
-#pragma unroll
-            for (int j = 0; j < M; ++j) raw[j] = load_bits<T>(w, q * M + j);
-#pragma unroll
-            for (int tt = 0; tt < N; ++tt) {
-                const int p = __builtin_ctz(keep);  // kept positions in ascending order
-                keep &= keep - 1;
-                uint32_t v = raw[0];
-#pragma unroll
-                for (int j = 1; j < M; ++j) v = p == j ? raw[j] : v;
-                store_bits<T>(vals, q * N + tt, v);
-                const int bit = (q * N + tt) * PT::BITS;  // compile-time position inside the chunk
-                acc[bit / 32] |= (uint32_t)p << (bit % 32);
-                if ((bit % 32) + PT::BITS > 32) acc[bit / 32 + 1] |= (uint32_t)p >> (32 - bit % 32);
+            for (int j = 1; j < M; ++j) x = p == j ? raw[j] : x;
+            v[tt] = x;
+            win |= (uint64_t)p << nb;
+            nb += PT::BITS;
+            if (nb >= 32) {
+                idx[wi++] = (uint32_t)win;
+                win >>= 32;
+                nb -= 32;
             }
         }
+        store_group_raw<T, N>(vals + q * N, vec, v);
     }
-    uint32_t* idx = a.indices + r * a.words_per_row + c * PT::WPC;
-#pragma unroll
-    for (int i = 0; i < PT::WPC; ++i)
-        if (c * PT::WPC + i < a.words_per_row) idx[i] = acc[i];
+    if (nb > 0) idx[wi] = (uint32_t)win;  // the row's last word, high bits zero
 }
 
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
     using PT = PackTiling<N, M>;
+    constexpr int GPC = PT::GPC;
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (t >= a.rows * a.chunks_per_row) return;
     const int64_t r = t / a.chunks_per_row;
     const int64_t c = t - r * a.chunks_per_row;
-    const int64_t q0 = c * PT::GPC;
-    const int ng = (int)(a.gpr - q0 < PT::GPC ? a.gpr - q0 : PT::GPC);
-    const int64_t grow = r * a.gpr;
+    const int64_t q0 = c * GPC;
+    const int ng = (int)(a.gpr - q0 < GPC ? a.gpr - q0 : GPC);
+    const bool vec = a.aligned != 0;
+    const int64_t g0 = r * a.gpr + q0;
     const uint32_t* idx = a.indices + r * a.words_per_row + c * PT::WPC;
-    uint32_t acc[PT::WPC];
+    const auto* vals = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
+    auto* dense = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
+    uint64_t win = 0;
+    int nb = 0, wi = 0;
+    for (int q = 0; q < ng; ++q) {
+        uint32_t pos[N], v[N], o[M];
 #pragma unroll
-    for (int i = 0; i < PT::WPC; ++i) acc[i] = c * PT::WPC + i < a.words_per_row ? idx[i] : 0u;
-    const auto* vals = reinterpret_cast<const typename T::storage*>(a.values) + (grow + q0) * N;
-    auto* dense = reinterpret_cast<typename T::storage*>(a.dense) + (grow + q0) * M;
-#pragma unroll
-    for (int q = 0; q < PT::GPC; ++q) {
-        if (q < ng) {
-            uint32_t pos[N], v[N];
-#pragma unroll
-            for (int tt = 0; tt < N; ++tt) {
-                const int bit = (q * N + tt) * PT::BITS;
-                uint32_t f = acc[bit / 32] >> (bit % 32);
-                if ((bit % 32) + PT::BITS > 32) f |= acc[bit / 32 + 1] << (32 - bit % 32);
-                pos[tt] = f & ((1u << PT::BITS) - 1u);
-                v[tt] = load_bits<T>(vals, q * N + tt);
+        for (int tt = 0; tt < N; ++tt) {
+            if (nb < PT::BITS) {  // never reads past the row's last word
+                win |= (uint64_t)idx[wi++] << nb;
+                nb += 32;
             }
+            pos[tt] = (uint32_t)win & ((1u << PT::BITS) - 1u);
+            win >>= PT::BITS;
+            nb -= PT::BITS;
+        }
+        load_group_raw<T, N>(vals + q * N, vec, v);
 #pragma unroll
-            for (int j = 0; j < M; ++j) {
-                uint32_t o = 0u;  // +0.0 where nothing is kept
+        for (int j = 0; j < M; ++j) {
+            uint32_t x = 0u;  // +0.0 where nothing is kept
 #pragma unroll
-                for (int tt = 0; tt < N; ++tt) o = pos[tt] == (uint32_t)j ? v[tt] : o;  // later field wins
-                store_bits<T>(dense, q * M + j, o);
-            }
+            for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[tt] : x;  // later field wins
+            o[j] = x;
+        }
+        store_group_raw<T, M>(dense + q * M, vec, o);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Fast path of pack/unpack for groups of four keeping one or two (2 bits per kept value), when
+// every row's index bits fill whole words: a thread owns the U = 8/(2N) groups of one index
+// byte, so the index bytes, packed values, hard indices and dense weights of consecutive threads
+// are contiguous and every store instruction of a wave writes whole cache lines.
+
+template <int N, typename T>
+struct ByteTiling {
+    static constexpr int M = 4;
+    static constexpr int K = Candidates<N, M>::K;
+    static constexpr int U = 8 / (2 * N);  // groups per index byte
+    static_assert(N == 1 || N == 2, "one index byte holds whole groups");
+};
+
+template <int N, typename T>
+__global__ __launch_bounds__(kThreads) void k_pack_bytes(PackArgs a) {
+    using BT = ByteTiling<N, T>;
+    constexpr int M = 4, K = BT::K, U = BT::U;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t g0 = t * U;
+    if (g0 >= a.rows * a.gpr) return;  // groups come in whole bytes: no partial thread
+    float l[U * K];
+    load_logit_unit<U * K>(a.logits + g0 * K, true, U * K, l);
+    uint32_t raw[U * M];
+    load_raw<T, U * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true, U * M, raw);
+    uint32_t vals[U * N];
+    uint32_t byte = 0u, hard = 0u;
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+        const float* lq = l + q * K;
+        float best = lq[0];
+        int bk = 0;
+        uint32_t keep = cand_keep<N, M, 0>();
+        static_for<1, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
+            const bool up = lq[k] > best;  // a NaN never wins: candidate 0 keeps its place
+            best = up ? lq[k] : best;
+            bk = up ? k : bk;
+            keep = up ? cand_keep<N, M, k>() : keep;
+        });
+        hard |= (uint32_t)bk << (8 * q);
+#pragma unroll
+        for (int tt = 0; tt < N; ++tt) {
+            const int p = __builtin_ctz(keep);
+            keep &= keep - 1;
+            uint32_t v = raw[q * M];
+#pragma unroll
+            for (int j = 1; j < M; ++j) v = p == j ? raw[q * M + j] : v;
+            vals[q * N + tt] = v;
+            byte |= (uint32_t)p << (2 * (q * N + tt));
         }
     }
+    auto* vp = reinterpret_cast<typename T::storage*>(a.values) + g0 * N;
+    if constexpr (U * N * T::bytes == 16) {
+        store_raw<T, U * N>(vp, true, U * N, vals);
+    } else {  // 8 bytes: four bf16 values
+        nt_store(vp, make_uint2(vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)));
+    }
+    __builtin_nontemporal_store((uint8_t)byte, reinterpret_cast<uint8_t*>(a.indices) + t);  // byte t
+    if (a.hard) {
+        if constexpr (U == 2) __builtin_nontemporal_store((uint16_t)hard, reinterpret_cast<uint16_t*>(a.hard + g0));
+        else nt_store(a.hard + g0, hard);
+    }
+}
+
+template <int N, typename T>
+__global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
+    using BT = ByteTiling<N, T>;
+    constexpr int M = 4, U = BT::U;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t g0 = t * U;
+    if (g0 >= a.rows * a.gpr) return;
+    const uint32_t byte = reinterpret_cast<const uint8_t*>(a.indices)[t];
+    const auto* vp = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
+    uint32_t v[U * N];
+    if constexpr (U * N * T::bytes == 16) {
+        load_raw<T, U * N>(vp, true, U * N, v);
+    } else {
+        const uint2 d = reinterpret_cast<const uint2*>(vp)[0];
+        v[0] = d.x & 0xFFFFu; v[1] = d.x >> 16; v[2] = d.y & 0xFFFFu; v[3] = d.y >> 16;
+    }
+    uint32_t dense[U * M];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            uint32_t o = 0u;  // +0.0 where nothing is kept
+#pragma unroll
+            for (int tt = 0; tt < N; ++tt)
+                o = ((byte >> (2 * (q * N + tt))) & 3u) == (uint32_t)j ? v[q * N + tt] : o;  // later field wins
+            dense[q * M + j] = o;
+        }
+    }
+    store_raw<T, U * M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, U * M, dense);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -390,14 +702,35 @@ static hipError_t bwd_nmt(const BwdArgs& a, hipStream_t s) {
     k_backward<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
+// The byte path needs whole-word rows (no padding bits) so that index byte t of the whole
+// stream belongs to groups U*t .. U*t+U-1; all its accesses are then 16-byte aligned given the
+// 16-byte aligned base pointers the entry points require.
+template <int N, int M>
+static bool byte_path(int64_t gpr) {
+    if constexpr (M == 4 && (N == 1 || N == 2)) return (gpr * N * 2) % 32 == 0;
+    else return false;
+}
+
 template <int N, int M, typename T>
 static hipError_t pack_nmt(PackArgs a, hipStream_t s) {
+    if constexpr (M == 4 && (N == 1 || N == 2)) {
+        if (byte_path<N, M>(a.gpr)) {
+            k_pack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     a.chunks_per_row = (a.gpr + PackTiling<N, M>::GPC - 1) / PackTiling<N, M>::GPC;
     k_pack<N, M, T><<<grid_for(a.rows * a.chunks_per_row), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 template <int N, int M, typename T>
 static hipError_t unpack_nmt(UnpackArgs a, hipStream_t s) {
+    if constexpr (M == 4 && (N == 1 || N == 2)) {
+        if (byte_path<N, M>(a.gpr)) {
+            k_unpack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     a.chunks_per_row = (a.gpr + PackTiling<N, M>::GPC - 1) / PackTiling<N, M>::GPC;
     k_unpack<N, M, T><<<grid_for(a.rows * a.chunks_per_row), kThreads, 0, s>>>(a);
     return hipGetLastError();

@@ -40,6 +40,8 @@ struct PackArgs {
     int64_t rows, gpr;   // groups per row
     int64_t words_per_row;
     int64_t chunks_per_row;  // set by the launcher
+    int32_t aligned;         // rows of w, logits and values start on 16-byte boundaries
+    int32_t hard_aligned;    // rows of hard start on 16-byte boundaries
 };
 
 struct UnpackArgs {
@@ -48,6 +50,7 @@ struct UnpackArgs {
     void* dense;
     int64_t rows, gpr, words_per_row;
     int64_t chunks_per_row;  // set by the launcher
+    int32_t aligned;         // rows of values and dense start on 16-byte boundaries
 };
 
 struct NoiseArgs {

@@ -1,0 +1,222 @@
+"""Parity at the full sizes of the benchmark workloads, launched exactly as bench.py launches
+them (one C-ABI call per matrix and pass).  Where the oracle cannot cover a whole matrix in
+seconds, it checks sampled rows (first, second, middle, last), and properties that hold at any
+size are checked on the whole matrix on the GPU.
+
+Workloads:
+  1. one 256x256 fp32 weight, 2:4, kappa=100, tau=4, seed 0: everything, every element;
+  2. one LLaMA-2-7B-shaped decoder layer (7 matrices, bf16, magnitude-prior logits);
+  3. 32 such layers under the annealing schedule tau 4 -> 0.05, kappa 100 -> 500 over 10 steps
+     (sampled layers and steps);
+  4. every matrix of a Nemotron-15B-shaped model (32 layers x 6), pack/unpack round trip;
+  5. a 4096x11008 bf16 weight with 1:4, 2:8 and 4:8.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nm_synth
+import oracle
+import semi_structured_sparsity_amd as S
+from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, soft_mask_check,
+                    tol_for_tau)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _sample_rows(rows):
+    return sorted({0, 1, rows // 2, rows - 1})
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def _check_rows(w, L, G, n, m, kappa, tau, seed, offset, out_fwd, out_bwd):
+    """Oracle on sampled rows against full-size GPU outputs."""
+    rows = w.shape[0]
+    bf16 = w.dtype == torch.bfloat16
+    worst_f = worst_b = 0.0
+    for r in _sample_rows(rows):
+        wr, Lr = w[r:r + 1].cpu(), L[r:r + 1].cpu()
+        ref = oracle.forward(wr, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
+        soft = oracle.soft_mask(Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
+        rel, bad = forward_check(out_fwd[r:r + 1].double().cpu().numpy(), ref,
+                                 wr.double().numpy(), soft, m, tol_for_tau(tau), bf16)
+        assert bad == 0, f"forward row {r}: {bad} elements out of tolerance"
+        worst_f = max(worst_f, rel)
+        if G is not None:
+            Gr = G[r:r + 1].cpu()
+            refb = oracle.backward(wr, Lr, Gr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
+            y = oracle.probs(Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
+            d = candidate_sums(wr.double().numpy(), Gr.double().numpy(), n, m,
+                               oracle.candidate_matrix(n, m))
+            rel, bad = backward_check(out_bwd[r:r + 1].double().cpu().numpy(), refb, y, d,
+                                      kappa / tau, tol_for_tau(tau))
+            assert bad == 0, f"backward row {r}: {bad} elements out of tolerance"
+            worst_b = max(worst_b, rel)
+    return worst_f, worst_b
+
+
+def _check_pack_full(w, L, n, m):
+    """Whole matrix, bit-exact against the oracle; returns the GPU outputs."""
+    values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+    dense = S.nm_unpack(values, indices, w.shape[1], n, m)
+    rv, ri, rh = oracle.pack(w.cpu(), L.cpu(), n, m)
+    assert np.array_equal(hard.cpu().numpy(), rh)
+    assert np.array_equal(indices.cpu().numpy().view(np.uint32), ri)
+    assert np.array_equal(_bits(values).cpu().numpy(), rv.view(_bits(values).cpu().numpy().dtype))
+    keep = _keep_mask(hard, n, m)
+    want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
+    assert torch.equal(_bits(dense), want)
+    return values, indices, hard, dense
+
+
+def _keep_mask(hard, n, m):
+    """bool [rows, cols]: the hard mask expanded from candidate indices (torch, on the GPU)."""
+    table = torch.tensor(S.candidate_table(n, m), dtype=torch.int32, device=hard.device)
+    bits = table[hard.long()]                                        # [rows, gpr]
+    pos = torch.arange(m, device=hard.device, dtype=torch.int32)
+    return ((bits.unsqueeze(-1) >> pos) & 1).bool().reshape(hard.shape[0], -1)
+
+
+def _soft_properties(L, n, m, kappa, tau, seed, offset):
+    """Whole matrix: every group's soft mask sums to n and lies in [0, 1]."""
+    soft = S.nm_debug_soft_mask(L, n, m, kappa, tau, seed, offset)
+    sums = soft.view(-1, m).double().sum(1)
+    assert float((sums - n).abs().max()) <= 1e-5 * n
+    assert float(soft.min()) >= 0.0 and float(soft.max()) <= 1.0 + 1e-6
+
+
+def _grad_properties(w, G, dl, n, m, kappa, tau):
+    """Whole matrix: the logit gradient of each group sums to zero up to rounding of its terms."""
+    K = dl.shape[-1]
+    a = (G.float() * w.float()).abs().view(-1, m).sum(1)
+    s = dl.view(-1, K).double().sum(1).abs()
+    assert bool((s <= 1e-5 * (kappa / tau) * a.double() + 1e-30).all())
+
+
+# ---------------------------------------------------------------------------------------------
+
+def test_config1_single_256x256_fp32_weight_every_element():
+    n, m, kappa, tau, seed, off = 2, 4, 100.0, 4.0, 0, 0
+    w, L, G = nm_synth.matrix_inputs(256, 256, n, m, torch.float32, 0.02, nm_synth.input_seed(1, 0, 0))
+    wd, Ld, Gd = w.to(DEV), L.to(DEV), G.to(DEV)
+    soft = S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed, off).double().cpu().numpy()
+    ref_soft = oracle.soft_mask(L, n, m, kappa, tau, seed, off)
+    rel, bad = soft_mask_check(soft, ref_soft, m, TOL_FP32)
+    _say("config1 soft err/bound", rel)
+    assert bad == 0
+    out = S.nm_mask_forward(wd, Ld, n, m, kappa, tau, seed, off)
+    rel, bad = forward_check(out.double().cpu().numpy(), oracle.forward(w, L, n, m, kappa, tau, seed, off),
+                             w.double().numpy(), ref_soft, m, TOL_FP32, False)
+    _say("config1 fwd err/bound", rel)
+    assert bad == 0
+    dl = S.nm_mask_backward(wd, Ld, Gd, n, m, kappa, tau, seed, off)
+    y = oracle.probs(L, n, m, kappa, tau, seed, off)
+    d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
+    rel, bad = backward_check(dl.double().cpu().numpy(), oracle.backward(w, L, G, n, m, kappa, tau, seed, off),
+                              y, d, kappa / tau, TOL_FP32)
+    _say("config1 bwd err/bound", rel)
+    assert bad == 0
+    words = S.nm_debug_noise(256, 256, n, m, seed, off).cpu().numpy().view(np.uint32).reshape(-1)
+    assert np.array_equal(words, oracle.noise_words(seed, off, 0, words.size))
+    _check_pack_full(wd, Ld, n, m)
+
+
+@pytest.mark.parametrize("i", range(len(nm_synth.LLAMA2_7B_LAYER)))
+def test_config2_llama7b_layer(i):
+    n, m, kappa, tau = 2, 4, 100.0, 4.0
+    name, rows, cols = nm_synth.LLAMA2_7B_LAYER[i]
+    seed = nm_synth.input_seed(2, 0, i)
+    _say("config2", name, rows, cols)
+    w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
+                                     device=DEV)
+    out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, 0)
+    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, 0)
+    wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl)
+    _say("  sampled rows fwd/bwd err/bound", wf, wb)
+    _soft_properties(L, n, m, kappa, tau, seed, 0)
+    _grad_properties(w, G, dl, n, m, kappa, tau)
+    _check_pack_full(w, L, n, m)
+    # the prior's candidate is the hard mask wherever the prior logit margin (3) dominates
+    prior = nm_synth.magnitude_prior_index(w, n, m)
+    _, _, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+    assert float((hard.long() == prior).double().mean()) > 0.999
+
+
+def _schedule(step, steps=10):
+    """tau 4 -> 0.05 and kappa 100 -> 500, linear over steps 0 .. steps-1."""
+    f = step / (steps - 1)
+    return 100.0 + 400.0 * f, 4.0 + (0.05 - 4.0) * f
+
+
+@pytest.mark.parametrize("layer,step", [(0, 0), (0, 9), (17, 4), (31, 9)])
+def test_config3_annealed_sweep_sampled(layer, step):
+    n, m = 2, 4
+    kappa, tau = _schedule(step)
+    for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
+        seed = nm_synth.input_seed(3, layer, i)
+        _say("config3", layer, step, name)
+        w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
+                                         device=DEV)
+        out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, step)
+        dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, step)
+        _check_rows(w, L, G, n, m, kappa, tau, seed, step, out, dl)
+        _grad_properties(w, G, dl, n, m, kappa, tau)
+        if step == 9:
+            _check_pack_full(w, L, n, m)
+        del w, L, G, out, dl
+    torch.cuda.empty_cache()
+
+
+def test_config4_nemotron15b_every_matrix_round_trip():
+    n, m = 2, 4
+    total = 0
+    for layer in range(nm_synth.LAYERS):
+        for i, (name, rows, cols) in enumerate(nm_synth.NEMOTRON_15B_LAYER):
+            seed = nm_synth.input_seed(4, layer, i)
+            w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.015, seed,
+                                             with_grad=False, device=DEV)
+            values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+            dense = S.nm_unpack(values, indices, cols, n, m)
+            keep = _keep_mask(hard, n, m)
+            # round trip: exactly the selected weights survive, +0.0 elsewhere
+            assert torch.equal(_bits(dense), torch.where(keep, _bits(w), torch.zeros_like(_bits(w))))
+            assert int(keep.view(-1, m).sum(1).min()) == n == int(keep.view(-1, m).sum(1).max())
+            # hard mask = first argmax of the logits
+            assert torch.equal(hard.long(), torch.argmax(L, dim=-1))
+            if i in (0, 4):  # the oracle on sampled rows of a square and a rectangular matrix
+                for r in (0, rows - 1):
+                    rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
+                    assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri)
+                    assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16))
+            total += rows * cols
+            del w, L, values, indices, hard, dense, keep
+        if layer % 8 == 7:
+            _say("config4 through layer", layer)
+    torch.cuda.empty_cache()
+    assert total == 32 * nm_synth.layer_weights(nm_synth.NEMOTRON_15B_LAYER)
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 8), (4, 8)])
+def test_config5_general_nm_4096x11008(n, m):
+    rows, cols, kappa, tau = 4096, 11008, 100.0, 1.0
+    seed = nm_synth.input_seed(5, 0, m * 10 + n)
+    _say("config5", n, m)
+    w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, device=DEV)
+    out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, 0)
+    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, 0)
+    wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl)
+    _say("  sampled rows fwd/bwd err/bound", wf, wb)
+    _soft_properties(L, n, m, kappa, tau, seed, 0)
+    _grad_properties(w, G, dl, n, m, kappa, tau)
+    _check_pack_full(w, L, n, m)
