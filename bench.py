@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="least CPU time of the baseline")
+    p.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                   help="print the path kernels' average durations from rocprofv3 --stats output")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run 4 plain 1 GiB device copies (counter calibration under a profiler)")
     return p.parse_args()
@@ -65,7 +69,6 @@ def make_layer(dev):
                          dl=torch.empty_like(L),
                          values=torch.empty((rows, cols // M * N), dtype=w.dtype, device=dev),
                          indices=torch.empty((rows, cols // 32), dtype=torch.int32, device=dev),
-                         hard=torch.empty((rows, cols // M), dtype=torch.uint8, device=dev),
                          dense=torch.empty_like(w)))
     return mats
 
@@ -76,8 +79,8 @@ def run_pass(S, mt, which, step):
     elif which == "bwd":
         S.nm_mask_backward(mt["w"], mt["L"], mt["G"], N, M, KAPPA, TAU, mt["seed"], step, out=mt["dl"])
     elif which == "harden_pack":
-        S.nm_mask_harden_pack(mt["w"], mt["L"], N, M, with_hard=True,
-                              out=(mt["values"], mt["indices"], mt["hard"]))
+        # values and indices only: the optional hard-index bytes are not part of the pass
+        S.nm_mask_harden_pack(mt["w"], mt["L"], N, M, out=(mt["values"], mt["indices"], None))
     else:
         S.nm_unpack(mt["values"], mt["indices"], mt["cols"], N, M, out=mt["dense"])
 
@@ -86,8 +89,11 @@ PASSES = ("fwd", "bwd", "harden_pack", "unpack")
 
 
 def step_all(S, mats, step):
-    for mt in mats:
-        for p in PASSES:
+    # pass-major, as in a training step (all forwards, then all backwards, ...): each pass moves
+    # >= 2 GB across the seven matrices, so no pass finds a matrix's data left in the 256 MB
+    # last-level cache by the previous pass over the same matrix
+    for p in PASSES:
+        for mt in mats:
             run_pass(S, mt, p, step)
 
 
@@ -123,8 +129,91 @@ def cpu_baseline(min_seconds=10.0, max_passes=8):
                       f"fwd+bwd+harden_pack+unpack in binary64 on {threads} threads, {elapsed:.1f} s"}
 
 
+# ---------------------------------------------------------------------------------------------
+# rocprofv3 summaries (run on the CSV output of the commands printed in profiles/)
+
+KERNELS = {"fwd": "k_forward<2, 4, nm::BF16, 0>", "bwd": "k_backward<2, 4, nm::BF16>",
+           "harden_pack": "k_pack_bytes<2, nm::BF16>", "unpack": "k_unpack_bytes<2, nm::BF16>"}
+COPY_BYTES = 1 << 30  # the --copy-calibration copies
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources, so stored counter readings can be matched to the kernels."""
+    import hashlib
+    import semi_structured_sparsity_amd.build as b
+    h = hashlib.sha256()
+    for path in sorted(b.SOURCES + b.HEADERS):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _rows(csv_path):
+    import csv
+    with open(csv_path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(stats_csv):
+    """Average launch duration of each path kernel from a --kernel-trace --stats run."""
+    out = {}
+    for row in _rows(stats_csv):
+        for p, k in KERNELS.items():
+            if k in row["Name"]:
+                out[p] = {"kernel": k, "calls": int(row["Calls"]), "avg_us": float(row["AverageNs"]) / 1e3}
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per dispatch of each path kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each divided by what the same counter reads, per byte, for the 1 GiB calibration copies."""
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _rows(path) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]
+                  and float(r["Counter_Value"]) * 1024 > 0.4 * COPY_BYTES]
+        if not copies:
+            raise SystemExit(f"no calibration copy in {path}")
+        scale = (sum(copies) / len(copies)) / COPY_BYTES
+        for p, k in KERNELS.items():
+            vals = [float(r["Counter_Value"]) * 1024 for r in rows if k in r["Kernel_Name"]]
+            if vals:
+                res.setdefault(p, {})[counter] = {"dispatches": len(vals), "copy_scale": round(scale, 4),
+                                                  "bytes_per_dispatch": sum(vals) / len(vals) / scale}
+    return res
+
+
+def write_traffic(fetch_csv, write_csv, out_json):
+    pmc = summarize_pmc(fetch_csv, write_csv)
+    doc = {"source_hash": kernel_source_hash(), "unit": "bytes per launch (average over the layer)",
+           "kernels": {p: v["FETCH_SIZE"]["bytes_per_dispatch"] + v["WRITE_SIZE"]["bytes_per_dispatch"]
+                       for p, v in pmc.items() if "FETCH_SIZE" in v and "WRITE_SIZE" in v},
+           "detail": pmc}
+    with open(out_json, "w") as f:
+        json.dump(doc, f, indent=1)
+    return doc
+
+
+def stored_traffic(kernel):
+    """Measured bytes per launch of `kernel` if the counters were taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("source_hash") != kernel_source_hash():
+        return None
+    v = doc.get("kernels", {}).get(kernel)
+    return None if v is None else round(v, 0)
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return
+    if args.summarize_pmc:
+        print(json.dumps(write_traffic(*args.summarize_pmc, os.path.join(ROOT, "profiles", "traffic.json")),
+                         indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): the layer is independent "
               "per group and this build has no multi-GPU path.", file=sys.stderr)
@@ -189,10 +278,7 @@ def main():
     dom = max(PASSES, key=lambda p: passes[p]["avg_launch_us"])
     dom_bytes = bpw[dom] * weights / len(mats)
     achieved = dom_bytes / (passes[dom]["avg_launch_us"] * 1e-6) / 1e9
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tpath):
-        traffic = json.load(open(tpath)).get(f"k_{'forward' if dom == 'fwd' else 'backward' if dom == 'bwd' else 'pack' if dom == 'harden_pack' else 'unpack'}")
+    traffic = stored_traffic(dom)
     step_bytes = sum(bpw.values()) * weights
     result = {
         "metric": METRIC,
@@ -216,9 +302,11 @@ def main():
         "step_pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
         "fwd_bwd": fwd_bwd,
         "passes": passes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": round(dom_bytes, 0),
+                     "avg_launch_us": passes[dom]["avg_launch_us"]},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
