@@ -41,6 +41,12 @@ def bytes_per_weight(wb=WB, n=N, m=M, k=K):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default="llama7b_layer",
+                   choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256"],
+                   help="llama7b_layer (default): one LLaMA-2-7B-shaped layer per step; sweep32: 32 such "
+                        "layers x 10 annealed steps of fwd+bwd+pack; general_nm: 4096x11008 with 1:4, 2:8, "
+                        "4:8; nemotron_pack: pack+unpack of every Nemotron-15B-shaped matrix; single256: "
+                        "one 256x256 fp32 weight (latency-bound)")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -205,8 +211,196 @@ def stored_traffic(kernel):
     return None if v is None else round(v, 0)
 
 
+# ---------------------------------------------------------------------------------------------
+# other workloads (reported separately; the default line is the LLaMA-7B layer)
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _elapsed_ms(fn, reps=1):
+    import torch
+    a, b = _events()
+    torch.cuda.synchronize()
+    a.record()
+    for r in range(reps):
+        fn(r)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def workload_sweep32(args):
+    """32 LLaMA-7B-shaped layers resident in HBM; 10 steps with tau 4 -> 0.05 and kappa
+    100 -> 500 (linear), offset = step; per step the forward of every matrix (layers 0..31),
+    then the backward (layers 31..0), then harden+pack."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    layers = []
+    for layer in range(nm_synth.LAYERS):
+        mats = []
+        for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
+            seed = nm_synth.input_seed(3, layer, i)
+            w, L, G = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed,
+                                             logits="prior", device=dev)
+            mats.append(dict(rows=rows, cols=cols, seed=seed, w=w, L=L, G=G))
+        layers.append(mats)
+    outs = {}
+    for name, rows, cols in nm_synth.LLAMA2_7B_LAYER:
+        outs[(rows, cols)] = dict(out=torch.empty((rows, cols), dtype=torch.bfloat16, device=dev),
+                                  dl=torch.empty((rows, cols // M, K), device=dev),
+                                  values=torch.empty((rows, cols // M * N), dtype=torch.bfloat16, device=dev),
+                                  indices=torch.empty((rows, cols // 32), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+
+    def step(s):
+        f = s / 9.0
+        kappa, tau = 100.0 + 400.0 * f, 4.0 + (0.05 - 4.0) * f
+        for mats in layers:
+            for mt in mats:
+                o = outs[(mt["rows"], mt["cols"])]
+                S.nm_mask_forward(mt["w"], mt["L"], N, M, kappa, tau, mt["seed"], s, out=o["out"])
+        for mats in reversed(layers):
+            for mt in mats:
+                o = outs[(mt["rows"], mt["cols"])]
+                S.nm_mask_backward(mt["w"], mt["L"], mt["G"], N, M, kappa, tau, mt["seed"], s, out=o["dl"])
+        for mats in layers:
+            for mt in mats:
+                o = outs[(mt["rows"], mt["cols"])]
+                S.nm_mask_harden_pack(mt["w"], mt["L"], N, M, out=(o["values"], o["indices"], None))
+
+    step(0)  # warm-up
+    ms = _elapsed_ms(step, reps=10)  # the 10 annealed steps, timed together
+    weights = nm_synth.LAYERS * nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
+    bpw = bytes_per_weight()
+    byts = weights * (bpw["fwd"] + bpw["bwd"] + bpw["harden_pack"])
+    return {"metric": "masked weights/sec fwd+bwd+pack over a 32-layer 7B-shaped sweep", "value": weights / (ms * 1e-3),
+            "unit": "weights/s", "ms_per_step": round(ms, 3), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+            "config": {"workload": "32 LLaMA-2-7B-shaped layers (6,476,005,376 bf16 weights), 2:4, 10 annealed "
+                                   "steps (tau 4->0.05, kappa 100->500), fwd+bwd+harden_pack per step",
+                       "steps_timed": 10}}
+
+
+def workload_general_nm(args):
+    """4096x11008 bf16, 1:4 / 2:8 / 4:8, kappa 100, tau 1: every pass timed on its own."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    rows, cols = 4096, 11008
+    res = {}
+    for n, m in ((1, 4), (2, 8), (4, 8)):
+        k = S.num_candidates(n, m)
+        seed = nm_synth.input_seed(5, 0, m * 10 + n)
+        w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, device=dev)
+        out, dl = torch.empty_like(w), torch.empty_like(L)
+        wpr = S.index_words_per_row(cols, n, m)
+        values = torch.empty((rows, cols // m * n), dtype=w.dtype, device=dev)
+        idx = torch.empty((rows, wpr), dtype=torch.int32, device=dev)
+        dense = torch.empty_like(w)
+        bpw = bytes_per_weight(2, n, m, k)
+        calls = {"fwd": lambda r: S.nm_mask_forward(w, L, n, m, 100.0, 1.0, seed, r, out=out),
+                 "bwd": lambda r: S.nm_mask_backward(w, L, G, n, m, 100.0, 1.0, seed, r, out=dl),
+                 "harden_pack": lambda r: S.nm_mask_harden_pack(w, L, n, m, out=(values, idx, None)),
+                 "unpack": lambda r: S.nm_unpack(values, idx, cols, n, m, out=dense)}
+        entry = {}
+        for p, fn in calls.items():
+            fn(0)
+            us = _elapsed_ms(fn, reps=args.kernel_reps) * 1e3
+            gbps = bpw[p] * rows * cols / (us * 1e-6) / 1e9
+            entry[p] = {"avg_launch_us": round(us, 2), "bytes_per_weight": round(bpw[p], 4),
+                        "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+        fb = entry["fwd"]["avg_launch_us"] + entry["bwd"]["avg_launch_us"]
+        entry["fwd_bwd_weights_per_s"] = rows * cols / (fb * 1e-6)
+        res[f"{n}:{m}"] = entry
+        del w, L, G, out, dl, values, idx, dense
+        torch.cuda.empty_cache()
+    return {"metric": "per-pass throughput, general N:M on a 4096x11008 bf16 weight", "unit": "GB/s",
+            "config": {"workload": "4096x11008 bf16, kappa=100, tau=1, logits N(0,1)"}, "results": res}
+
+
+def workload_nemotron_pack(args):
+    """Every Nemotron-15B-shaped matrix (32 layers x 6, bf16, logits N(0,1)): harden+pack and
+    unpack, generated and timed layer by layer."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    t_pack = t_unpack = 0.0
+    weights = 0
+    for layer in range(nm_synth.LAYERS):
+        mats = []
+        for i, (name, rows, cols) in enumerate(nm_synth.NEMOTRON_15B_LAYER):
+            seed = nm_synth.input_seed(4, layer, i)
+            w, L, _ = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.015, seed,
+                                             with_grad=False, device=dev)
+            mats.append((w, L, cols, torch.empty((rows, cols // 2), dtype=w.dtype, device=dev),
+                         torch.empty((rows, cols // 32), dtype=torch.int32, device=dev), torch.empty_like(w)))
+            weights += rows * cols
+        def pack(r):
+            for w, L, c, v, ix, d in mats:
+                S.nm_mask_harden_pack(w, L, N, M, out=(v, ix, None))
+
+        def unpack(r):
+            for w, L, c, v, ix, d in mats:
+                S.nm_unpack(v, ix, c, N, M, out=d)
+
+        pack(0)  # untimed: first touch of this layer's freshly allocated buffers
+        unpack(0)
+        t_pack += _elapsed_ms(pack)
+        t_unpack += _elapsed_ms(unpack)
+        del mats
+    bpw = bytes_per_weight()
+    res = {}
+    for p, t in (("harden_pack", t_pack), ("unpack", t_unpack)):
+        gbps = bpw[p] * weights / (t * 1e-3) / 1e9
+        res[p] = {"ms": round(t, 3), "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+    return {"metric": "harden+pack and unpack over every Nemotron-15B-shaped matrix", "unit": "GB/s",
+            "config": {"workload": "32 layers x (q,k,v,o 6144x6144, up 24576x6144, down 6144x24576), "
+                                   "14,495,514,624 bf16 weights, 2:4"}, "weights": weights, "results": res}
+
+
+def workload_single256(args):
+    """One 256x256 fp32 weight, 2:4, kappa 100, tau 4, seed 0: launch-latency-bound."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    w, L, G = nm_synth.matrix_inputs(256, 256, N, M, torch.float32, 0.02, nm_synth.input_seed(1, 0, 0))
+    w, L, G = w.cuda(), L.cuda(), G.cuda()
+    out, dl = torch.empty_like(w), torch.empty_like(L)
+    v = torch.empty((256, 128), device="cuda")
+    ix = torch.empty((256, 8), dtype=torch.int32, device="cuda")
+    d = torch.empty_like(w)
+    calls = {"fwd": lambda r: S.nm_mask_forward(w, L, N, M, 100.0, 4.0, 0, r, out=out),
+             "bwd": lambda r: S.nm_mask_backward(w, L, G, N, M, 100.0, 4.0, 0, r, out=dl),
+             "harden_pack": lambda r: S.nm_mask_harden_pack(w, L, N, M, out=(v, ix, None)),
+             "unpack": lambda r: S.nm_unpack(v, ix, 256, N, M, out=d)}
+    res = {}
+    for p, fn in calls.items():
+        fn(0)
+        res[p] = {"avg_launch_us": round(_elapsed_ms(fn, reps=200) * 1e3, 2)}
+    return {"metric": "launch latency, one 256x256 fp32 weight", "unit": "us", "results": res}
+
+
 def main():
     args = parse()
+    if args.workload != "llama7b_layer":
+        import torch
+        torch.cuda.set_device(0)
+        fn = {"sweep32": workload_sweep32, "general_nm": workload_general_nm,
+              "nemotron_pack": workload_nemotron_pack, "single256": workload_single256}[args.workload]
+        out = fn(args)
+        out.update({"n_gpus": 1, "data": "synthetic, seeded, generated on the GPU", "dtype": "f32"})
+        print(json.dumps(out), flush=True)
+        return
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
         return

@@ -95,7 +95,12 @@ struct SlotTiling {
 // Philox4x32 (Salmon, Moraes, Dror, Shaw, SC'11, section 3.3): 10 rounds; each multiplies words
 // 0 and 2 by fixed odd constants, the high halves are xored into the other two words with the
 // round key, and the key is advanced by two Weyl increments between rounds.  The key (the seed)
-// and the high counter half (the offset) are uniform across a launch and stay in SGPRs.
+// and the high counter half (the offset) are uniform across a launch and stay in SGPRs.  Each
+// three-way xor is one gfx950 v_bitop3_b32 (truth table 0x96: odd number of ones).
+
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 
 struct Philox4 {
     uint32_t v[4];
@@ -107,8 +112,8 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
