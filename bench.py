@@ -482,6 +482,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_events": round(step_ms, 4),
+        "step_ms_wall": round(step_ms_wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -178,7 +178,7 @@ nm_status nm_mask_harden_pack(const nm_shape* shape, const void* w, const float*
     const bool aligned = (shape->cols * wb) % 16 == 0 && (gpr * K * 4) % 16 == 0 &&
                          (gpr * shape->n * wb) % 16 == 0;
     nm::PackArgs a{w, logits, values, indices, hard_idx, shape->rows, gpr,
-                   nm_index_words_per_row(shape), 0, aligned ? 1 : 0, gpr % 16 == 0 ? 1 : 0};
+                   nm_index_words_per_row(shape), aligned ? 1 : 0, gpr % 16 == 0 ? 1 : 0};
     return launched(nm::launch_pack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
@@ -193,7 +193,7 @@ nm_status nm_unpack(const nm_shape* shape, const void* values, const uint32_t* i
     if (!aligned16(values) || !aligned16(indices) || !aligned16(w_dense)) return NM_EALIGN;
     const int64_t gpr = shape->cols / shape->m, wb = shape->wtype == NM_BF16 ? 2 : 4;
     const bool aligned = (shape->cols * wb) % 16 == 0 && (gpr * shape->n * wb) % 16 == 0;
-    nm::UnpackArgs a{values, indices, w_dense, shape->rows, gpr, nm_index_words_per_row(shape), 0,
+    nm::UnpackArgs a{values, indices, w_dense, shape->rows, gpr, nm_index_words_per_row(shape),
                      aligned ? 1 : 0};
     return launched(nm::launch_unpack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }

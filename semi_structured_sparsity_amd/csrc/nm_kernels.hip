@@ -76,9 +76,15 @@ struct Sample {
     static constexpr int PH = SlotTiling<K>::phased ? 2 : 0;  // extra words of a phased tile
     static constexpr int NB = (PK + PH + 3) / 4;              // Philox blocks per thread
     static constexpr int LALIGN = (PK * 4) % 16 == 0 ? 16 : 8; // byte alignment of a thread's logits
-    // stage logit-gradient stores through LDS when a thread's share is 2 to 4 16-byte vectors
-    static constexpr bool STAGE = LALIGN == 16 && PK >= 8 && PK <= 16;
+    // Stage a block's logits (and logit gradients) through LDS when a thread's share is more than
+    // one vector: then neighbouring lanes are more than a vector apart and direct accesses leave
+    // partly used cache lines in every instruction.  Tile: kThreads * PK floats (<= 70 KB).
+    static constexpr bool STAGE = PK * 4 > LALIGN;
 };
+
+template <int VW> struct StageVec;
+template <> struct StageVec<16> { using type = float4; };
+template <> struct StageVec<8> { using type = float2; };
 
 // h[i] for the thread's slots i = 0 .. PK-1 (slot index relative to g0*K).  Each Philox block
 // is turned into Gumbel exponents as soon as it is generated; only the last two words of the
@@ -158,7 +164,9 @@ __device__ __forceinline__ float group_soft(const float (&e)[Candidates<N, M>::K
 template <int N, int M>
 struct StageTile {
     using S = Sample<N, M>;
-    static constexpr int VEC = S::STAGE ? kThreads * S::PK / 4 : 1;  // float4 slots
+    using vec = typename StageVec<S::LALIGN>::type;
+    static constexpr int PER = S::PK * 4 / S::LALIGN;               // vectors per thread
+    static constexpr int VEC = S::STAGE ? kThreads * PER : 1;       // vectors per tile
 };
 
 template <int N, int M>
@@ -166,22 +174,39 @@ __device__ __forceinline__ bool block_full(int64_t groups) {
     return ((int64_t)blockIdx.x + 1) * kThreads * Sample<N, M>::P <= groups;
 }
 
+template <typename V>
+__device__ __forceinline__ void vec_to_floats(const V& v, float* out) {
+    if constexpr (sizeof(V) == 16) { out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w; }
+    else { out[0] = v.x; out[1] = v.y; }
+}
+template <typename V>
+__device__ __forceinline__ V floats_to_vec(const float* in) {
+    if constexpr (sizeof(V) == 16) return make_float4(in[0], in[1], in[2], in[3]);
+    else return make_float2(in[0], in[1]);
+}
+template <typename V>
+__device__ __forceinline__ void nt_store_vec(V* p, const V& v) {
+    if constexpr (sizeof(V) == 16)
+        nt_store(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+    else
+        nt_store(p, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
+}
+
 template <int N, int M>
 __device__ __forceinline__ void load_logits(const float* logits, int64_t g0, bool full, int nvalid, bool staged,
-                                            float4* tile, float (&l)[Sample<N, M>::PK]) {
+                                            typename StageTile<N, M>::vec* tile, float (&l)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
-    constexpr int PK = S::PK, V = PK / 4;
+    using ST = StageTile<N, M>;
+    using V = typename ST::vec;
+    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
     if constexpr (S::STAGE) {
         if (staged) {
-            const float4* src = reinterpret_cast<const float4*>(logits + (int64_t)blockIdx.x * kThreads * PK);
+            const V* src = reinterpret_cast<const V*>(logits + (int64_t)blockIdx.x * kThreads * PK);
 #pragma unroll
-            for (int i = 0; i < V; ++i) tile[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
+            for (int i = 0; i < PER; ++i) tile[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const float4 v = tile[threadIdx.x * V + i];
-                l[4 * i] = v.x; l[4 * i + 1] = v.y; l[4 * i + 2] = v.z; l[4 * i + 3] = v.w;
-            }
+            for (int i = 0; i < PER; ++i) vec_to_floats(tile[threadIdx.x * PER + i], l + W * i);
             return;
         }
     }
@@ -190,23 +215,21 @@ __device__ __forceinline__ void load_logits(const float* logits, int64_t g0, boo
 
 template <int N, int M>
 __device__ __forceinline__ void store_dlogits(float* dlogits, int64_t g0, bool full, int nvalid, bool staged,
-                                              float4* tile, const float (&dl)[Sample<N, M>::PK]) {
+                                              typename StageTile<N, M>::vec* tile,
+                                              const float (&dl)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
-    constexpr int PK = S::PK, V = PK / 4;
+    using ST = StageTile<N, M>;
+    using V = typename ST::vec;
+    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
     if constexpr (S::STAGE) {
         if (staged) {
             __syncthreads();  // every thread has read its logits out of the tile
 #pragma unroll
-            for (int i = 0; i < V; ++i)
-                tile[threadIdx.x * V + i] = make_float4(dl[4 * i], dl[4 * i + 1], dl[4 * i + 2], dl[4 * i + 3]);
+            for (int i = 0; i < PER; ++i) tile[threadIdx.x * PER + i] = floats_to_vec<V>(dl + W * i);
             __syncthreads();
-            float4* dst = reinterpret_cast<float4*>(dlogits + (int64_t)blockIdx.x * kThreads * PK);
+            V* dst = reinterpret_cast<V*>(dlogits + (int64_t)blockIdx.x * kThreads * PK);
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const float4 v = tile[threadIdx.x + i * kThreads];
-                nt_store(dst + threadIdx.x + i * kThreads,
-                         make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
-            }
+            for (int i = 0; i < PER; ++i) nt_store_vec(dst + threadIdx.x + i * kThreads, tile[threadIdx.x + i * kThreads]);
             return;
         }
     }
@@ -227,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
 
-    __shared__ float4 tile[StageTile<N, M>::VEC];
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
     load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
@@ -271,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
 
-    __shared__ float4 tile[StageTile<N, M>::VEC];
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
     load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
@@ -319,16 +342,23 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
 template <int N, int M>
 struct PackTiling {
     static constexpr int BITS = M <= 2 ? 1 : (M <= 4 ? 2 : (M <= 8 ? 3 : 4));  // ceil(log2 M)
-    static constexpr int GBITS = N * BITS;                                    // bits per group
-    static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
-    static constexpr int CHUNK_BITS = GBITS / gcd(GBITS, 32) * 32;            // lcm(GBITS, 32)
-    static constexpr int GPC = CHUNK_BITS / GBITS;                            // groups per chunk
-    static constexpr int WPC = CHUNK_BITS / 32;                               // words per chunk
 };
 
 // Groups per 16-byte-multiple unit when a group occupies `bytes` bytes (8 B -> 2 groups).
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int unit_groups(int bytes) { return 16 / gcd_c(16, bytes); }
+
+// One element's raw bits (zero-extended to 32 for bf16).
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const typename T::storage* p, int64_t i) {
+    if constexpr (T::bytes == 4) return reinterpret_cast<const uint32_t*>(p)[i];
+    else return (uint32_t)p[i];
+}
+template <typename T>
+__device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, uint32_t v) {
+    if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = v;
+    else p[i] = (uint16_t)v;
+}
 
 // Raw element bits (bit copies: packed values keep NaN payloads and signed zeros).  CNT elements
 // of T, each zero-extended into a uint32.  vec: the caller guarantees 16-byte alignment, that
@@ -468,105 +498,147 @@ __device__ __forceinline__ void store_group_raw(typename T::storage* __restrict_
     }
 }
 
-// The host sets `aligned` when every row of w, logits, values and dense starts on a 16-byte
-// boundary (then every group of a power-of-two byte size is aligned to that size).  Groups are
-// visited in a run-time loop; index fields go through a 64-bit bit window that is written out a
-// word at a time (a chunk's fields end on a word boundary, the row's last chunk on the row's
-// last word).
+// General pack/unpack: a block owns a tile of consecutive groups of one row (grid x = tile within
+// the row, grid y = row, looping over rows beyond the grid's y limit).  A thread owns GT
+// consecutive groups, GT chosen so that its weights / dense output are one 16-byte vector
+// (2 groups of four bf16, else 1), so weights, packed values, hard indices and dense output of
+// neighbouring lanes are contiguous.  Index fields, which straddle words for 3-bit positions,
+// are assembled in LDS (ds_or of at most two words per thread) and stored as whole words after
+// a barrier; every tile starts on a word boundary because kThreads * GT * N * BITS is a
+// multiple of 32.  The host sets `aligned` when every row of w, logits, values and dense starts
+// on a 16-byte boundary (then every thread's vector is aligned to its size).
+
+template <int N, int M, typename T>
+struct TileShape {
+    static constexpr int K = Candidates<N, M>::K;
+    static constexpr int BITS = PackTiling<N, M>::BITS;
+    static constexpr int GT = M * T::bytes >= 16 ? 1 : 16 / (M * T::bytes);  // groups per thread
+    static constexpr int TILE = kThreads * GT;                               // groups per block
+    static constexpr int WORDS = TILE * N * BITS / 32;                        // index words per tile
+    static constexpr int TBITS = GT * N * BITS;                               // a thread's index bits
+    static_assert(TILE * N * BITS % 32 == 0 && TBITS <= 32, "tiles start on words; <= 2 words per thread");
+};
+
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
-    using PT = PackTiling<N, M>;
-    constexpr int K = Candidates<N, M>::K, GPC = PT::GPC;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= a.rows * a.chunks_per_row) return;
-    const int64_t r = t / a.chunks_per_row;
-    const int64_t c = t - r * a.chunks_per_row;
-    const int64_t q0 = c * GPC;                           // first group of the chunk in its row
-    const int ng = (int)(a.gpr - q0 < GPC ? a.gpr - q0 : GPC);
-    const bool vec = a.aligned != 0;
-    const int64_t g0 = r * a.gpr + q0;                    // flat index of the chunk's first group
-    const auto* w = reinterpret_cast<const typename T::storage*>(a.w) + g0 * M;
-    const float* lg = a.logits + g0 * K;
-    auto* vals = reinterpret_cast<typename T::storage*>(a.values) + g0 * N;
-    uint32_t* idx = a.indices + r * a.words_per_row + c * PT::WPC;
-    uint64_t win = 0;
-    int nb = 0, wi = 0;
-    for (int q = 0; q < ng; ++q) {
-        float l[K];
-        load_f32<K, (K * 4) % 16 == 0 ? 16 : 8>(lg + q * K, vec, K, l);
-        // first largest logit; a NaN never compares greater, so it never displaces candidate 0
-        float best = l[0];
-        int bk = 0;
-        uint32_t keep = cand_keep<N, M, 0>();
-        static_for<1, K>([&](auto kc) NM_INLINE {
-            constexpr int k = decltype(kc)::value;
-            const bool up = l[k] > best;
-            best = up ? l[k] : best;
-            bk = up ? k : bk;
-            keep = up ? cand_keep<N, M, k>() : keep;
-        });
-        if (a.hard) a.hard[g0 + q] = (uint8_t)bk;
-        uint32_t raw[M], v[N];
-        load_group_raw<T, M>(w + q * M, vec, raw);
+    using TS = TileShape<N, M, T>;
+    constexpr int K = TS::K, GT = TS::GT, BITS = TS::BITS;
+    __shared__ uint32_t words[TS::WORDS];
+    const int64_t q_begin = (int64_t)blockIdx.x * TS::TILE;
+    const int ng = (int)(a.gpr - q_begin < TS::TILE ? a.gpr - q_begin : TS::TILE);
+    const int nwords = (ng * N * BITS + 31) / 32;
+    const int lq = threadIdx.x * GT;                        // first group of this thread in the tile
+    const int mine = ng - lq < 0 ? 0 : (ng - lq < GT ? ng - lq : GT);
+    const bool vec = a.aligned != 0 && mine == GT;
+    for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+        for (int i = threadIdx.x; i < TS::WORDS; i += kThreads) words[i] = 0u;
+        __syncthreads();
+        if (mine > 0) {
+            const int64_t g0 = r * a.gpr + q_begin + lq;    // flat index of the thread's first group
+            float l[GT * K];
+            if (vec) load_logit_unit<GT * K>(a.logits + g0 * K, true, GT * K, l);
+            else load_logit_unit<GT * K>(a.logits + g0 * K, false, mine * K, l);
+            uint32_t raw[GT * M], v[GT * N], hard[GT];
+            load_group_raw<T, GT * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, vec, raw);
+            uint64_t acc = 0;
 #pragma unroll
-        for (int tt = 0; tt < N; ++tt) {
-            const int p = __builtin_ctz(keep);  // kept positions in ascending order
-            keep &= keep - 1;
-            uint32_t x = raw[0];
+            for (int i = 0; i < GT; ++i) {
+                const float* li = l + i * K;
+                // first largest logit; a NaN never compares greater, so it never displaces candidate 0
+                float best = li[0];
+                int bk = 0;
+                uint32_t keep = cand_keep<N, M, 0>();
+                static_for<1, K>([&](auto kc) NM_INLINE {
+                    constexpr int k = decltype(kc)::value;
+                    const bool up = li[k] > best;
+                    best = up ? li[k] : best;
+                    bk = up ? k : bk;
+                    keep = up ? cand_keep<N, M, k>() : keep;
+                });
+                hard[i] = (uint32_t)bk;
 #pragma unroll
-            for (int j = 1; j < M; ++j) x = p == j ? raw[j] : x;
-            v[tt] = x;
-            win |= (uint64_t)p << nb;
-            nb += PT::BITS;
-            if (nb >= 32) {
-                idx[wi++] = (uint32_t)win;
-                win >>= 32;
-                nb -= 32;
+                for (int tt = 0; tt < N; ++tt) {
+                    const int p = __builtin_ctz(keep);  // kept positions in ascending order
+                    keep &= keep - 1;
+                    uint32_t x = raw[i * M];
+#pragma unroll
+                    for (int j = 1; j < M; ++j) x = p == j ? raw[i * M + j] : x;
+                    v[i * N + tt] = x;
+                    if (i < mine) acc |= (uint64_t)p << ((i * N + tt) * BITS);
+                }
             }
+            auto* vp = reinterpret_cast<typename T::storage*>(a.values) + g0 * N;
+            if (vec) {
+                store_group_raw<T, GT * N>(vp, true, v);
+            } else {
+                for (int e = 0; e < mine * N; ++e) store_bits<T>(vp, e, v[e]);
+            }
+            if (a.hard) {
+#pragma unroll
+                for (int i = 0; i < GT; ++i)
+                    if (i < mine) a.hard[g0 + i] = (uint8_t)hard[i];
+            }
+            const int lb = lq * N * BITS;                   // the thread's first bit in the tile
+            atomicOr(&words[lb / 32], (uint32_t)(acc << (lb % 32)));
+            if ((lb % 32) + TS::TBITS > 32) atomicOr(&words[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
         }
-        store_group_raw<T, N>(vals + q * N, vec, v);
+        __syncthreads();
+        uint32_t* idx = a.indices + r * a.words_per_row + q_begin * N * BITS / 32;
+        for (int i = threadIdx.x; i < nwords; i += kThreads) nt_store(idx + i, words[i]);
+        __syncthreads();  // the next row reuses the tile
     }
-    if (nb > 0) idx[wi] = (uint32_t)win;  // the row's last word, high bits zero
 }
 
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
-    using PT = PackTiling<N, M>;
-    constexpr int GPC = PT::GPC;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= a.rows * a.chunks_per_row) return;
-    const int64_t r = t / a.chunks_per_row;
-    const int64_t c = t - r * a.chunks_per_row;
-    const int64_t q0 = c * GPC;
-    const int ng = (int)(a.gpr - q0 < GPC ? a.gpr - q0 : GPC);
-    const bool vec = a.aligned != 0;
-    const int64_t g0 = r * a.gpr + q0;
-    const uint32_t* idx = a.indices + r * a.words_per_row + c * PT::WPC;
-    const auto* vals = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
-    auto* dense = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
-    uint64_t win = 0;
-    int nb = 0, wi = 0;
-    for (int q = 0; q < ng; ++q) {
-        uint32_t pos[N], v[N], o[M];
+    using TS = TileShape<N, M, T>;
+    constexpr int GT = TS::GT, BITS = TS::BITS;
+    __shared__ uint32_t words[TS::WORDS];
+    const int64_t q_begin = (int64_t)blockIdx.x * TS::TILE;
+    const int ng = (int)(a.gpr - q_begin < TS::TILE ? a.gpr - q_begin : TS::TILE);
+    const int nwords = (ng * N * BITS + 31) / 32;
+    const int lq = threadIdx.x * GT;
+    const int mine = ng - lq < 0 ? 0 : (ng - lq < GT ? ng - lq : GT);
+    const bool vec = a.aligned != 0 && mine == GT;
+    for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+        const uint32_t* idx = a.indices + r * a.words_per_row + q_begin * N * BITS / 32;
+        for (int i = threadIdx.x; i < nwords; i += kThreads) words[i] = idx[i];
+        __syncthreads();
+        if (mine > 0) {
+            const int64_t g0 = r * a.gpr + q_begin + lq;
+            const int lb = lq * N * BITS;
+            uint64_t acc = words[lb / 32];
+            if ((lb % 32) + TS::TBITS > 32) acc |= (uint64_t)words[lb / 32 + 1] << 32;
+            acc >>= lb % 32;
+            uint32_t v[GT * N], o[GT * M];
+            const auto* vp = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
+            if (vec) {
+                load_group_raw<T, GT * N>(vp, true, v);
+            } else {
 #pragma unroll
-        for (int tt = 0; tt < N; ++tt) {
-            if (nb < PT::BITS) {  // never reads past the row's last word
-                win |= (uint64_t)idx[wi++] << nb;
-                nb += 32;
+                for (int e = 0; e < GT * N; ++e) v[e] = e < mine * N ? load_bits<T>(vp, e) : 0u;
             }
-            pos[tt] = (uint32_t)win & ((1u << PT::BITS) - 1u);
-            win >>= PT::BITS;
-            nb -= PT::BITS;
-        }
-        load_group_raw<T, N>(vals + q * N, vec, v);
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            uint32_t x = 0u;  // +0.0 where nothing is kept
+            for (int i = 0; i < GT; ++i) {
+                uint32_t pos[N];
 #pragma unroll
-            for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[tt] : x;  // later field wins
-            o[j] = x;
+                for (int tt = 0; tt < N; ++tt) pos[tt] = (uint32_t)(acc >> ((i * N + tt) * BITS)) & ((1u << BITS) - 1u);
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    uint32_t x = 0u;  // +0.0 where nothing is kept
+#pragma unroll
+                    for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[i * N + tt] : x;  // later field wins
+                    o[i * M + j] = x;
+                }
+            }
+            auto* dp = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
+            if (vec) {
+                store_group_raw<T, GT * M>(dp, true, o);
+            } else {
+                for (int e = 0; e < mine * M; ++e) store_bits<T>(dp, e, o[e]);
+            }
         }
-        store_group_raw<T, M>(dense + q * M, vec, o);
+        __syncthreads();  // the next row reuses the tile
     }
 }
 
@@ -702,6 +774,13 @@ static hipError_t bwd_nmt(const BwdArgs& a, hipStream_t s) {
     k_backward<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
+// Tile grid of the general pack/unpack: x = tiles per row, y = rows (capped; the kernels loop).
+template <int N, int M, typename T>
+static dim3 tile_grid(int64_t rows, int64_t gpr) {
+    const int64_t tiles = (gpr + TileShape<N, M, T>::TILE - 1) / TileShape<N, M, T>::TILE;
+    return dim3((unsigned)tiles, (unsigned)(rows < 65535 ? rows : 65535), 1);
+}
+
 // The byte path needs whole-word rows (no padding bits) so that index byte t of the whole
 // stream belongs to groups U*t .. U*t+U-1; all its accesses are then 16-byte aligned given the
 // 16-byte aligned base pointers the entry points require.
@@ -719,8 +798,7 @@ static hipError_t pack_nmt(PackArgs a, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    a.chunks_per_row = (a.gpr + PackTiling<N, M>::GPC - 1) / PackTiling<N, M>::GPC;
-    k_pack<N, M, T><<<grid_for(a.rows * a.chunks_per_row), kThreads, 0, s>>>(a);
+    k_pack<N, M, T><<<tile_grid<N, M, T>(a.rows, a.gpr), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 template <int N, int M, typename T>
@@ -731,8 +809,7 @@ static hipError_t unpack_nmt(UnpackArgs a, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    a.chunks_per_row = (a.gpr + PackTiling<N, M>::GPC - 1) / PackTiling<N, M>::GPC;
-    k_unpack<N, M, T><<<grid_for(a.rows * a.chunks_per_row), kThreads, 0, s>>>(a);
+    k_unpack<N, M, T><<<tile_grid<N, M, T>(a.rows, a.gpr), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -776,15 +853,6 @@ hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-int pack_groups_per_chunk(int n, int m) {
-    switch (m * 16 + n) {
-#define NM_GPC(nn, mm) case mm * 16 + nn: return PackTiling<nn, mm>::GPC;
-        NM_GPC(1, 4) NM_GPC(2, 4) NM_GPC(3, 4) NM_GPC(1, 8) NM_GPC(2, 8) NM_GPC(3, 8) NM_GPC(4, 8)
-        NM_GPC(5, 8) NM_GPC(6, 8) NM_GPC(7, 8)
-#undef NM_GPC
-    default: return 0;
-    }
-}
 int groups_per_thread(int n, int m) {
     const int K = binom(m, n);
     if (K % 4 == 0 || K == 70) return 1;

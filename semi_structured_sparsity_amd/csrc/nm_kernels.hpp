@@ -39,7 +39,6 @@ struct PackArgs {
     uint8_t* hard;       // may be null
     int64_t rows, gpr;   // groups per row
     int64_t words_per_row;
-    int64_t chunks_per_row;  // set by the launcher
     int32_t aligned;         // rows of w, logits and values start on 16-byte boundaries
     int32_t hard_aligned;    // rows of hard start on 16-byte boundaries
 };
@@ -49,7 +48,6 @@ struct UnpackArgs {
     const uint32_t* indices;
     void* dense;
     int64_t rows, gpr, words_per_row;
-    int64_t chunks_per_row;  // set by the launcher
     int32_t aligned;         // rows of values and dense start on 16-byte boundaries
 };
 
@@ -71,7 +69,6 @@ hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
 hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s);
-int pack_groups_per_chunk(int n, int m);
 int groups_per_thread(int n, int m);
 
 }  // namespace nm
