@@ -52,6 +52,7 @@ def lib():
             "ref_pack": (i32, [P, i64, i64, P, P, P, P, P, i32]),
             "ref_unpack": (i32, [P, i64, i64, P, P, P, i32]),
             "ref_threads_used": (i32, [i32]),
+            "ref_prior_init": (i32, [P, i64, i64, P, ctypes.c_float, P, P, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -280,3 +281,18 @@ def unpack(values, indices, cols, n, m, nthreads=0):
     rc = lib().ref_unpack(ctypes.byref(s), 0, wr, _ptr(V), _ptr(I), _ptr(out), nthreads)
     _check(rc, "unpack")
     return out
+
+
+def prior_init(w, n, m, alpha=3.0, rows=None, row_begin=0, nthreads=0):
+    """(logits fp32 [window_rows, cols/m, K], prior index uint8 [window_rows, cols/m])."""
+    W = _contig(w)
+    wr, cols = W.shape
+    rows = wr if rows is None else rows
+    K = num_candidates(n, m)
+    logits = _unwritten((wr, cols // m, K), np.float32)
+    idx = _unwritten((wr, cols // m), np.uint8)
+    s = _shape(rows, cols, n, m, _wtype_of(W))
+    rc = lib().ref_prior_init(ctypes.byref(s), row_begin, _window(wr, row_begin, rows), _ptr(W), alpha,
+                              _ptr(logits), _ptr(idx), nthreads)
+    _check(rc, "prior_init")
+    return logits, idx

@@ -567,3 +567,59 @@ int32_t ref_unpack(const ref_shape *shape, int64_t row_begin, int64_t row_end,
     run_rows(&jb, row_begin, row_end, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Magnitude prior ("Accelerating Sparse Deep Neural Networks" summary page, section 4.1:
+ * magnitude pruning keeps the largest magnitudes of each group; MaskLLM project page, Table 2
+ * caption: prior masks initialise the logits of the learned masks).  Selection (a reading that
+ * fixes ties): n rounds, each taking the first unchosen position with the largest |w| (a strictly
+ * larger magnitude replaces the current choice, so ties keep the lower position and a NaN is
+ * taken only when it is the first unchosen position).  Logits: alpha on the prior candidate,
+ * 0 elsewhere. */
+static int32_t prior_candidate(const group_ctx *c, const double *mag) {
+    uint32_t chosen = 0;
+    for (int32_t t = 0; t < c->n; ++t) {
+        int32_t best = -1;
+        for (int32_t j = 0; j < c->m; ++j) {
+            if (chosen >> j & 1u) continue;
+            if (best < 0 || mag[j] > mag[best]) best = j;
+        }
+        chosen |= 1u << best;
+    }
+    for (int32_t k = 0; k < c->K; ++k)
+        if (c->cand[k] == chosen) return k;
+    return -1; /* not reached: every n-subset is a candidate */
+}
+
+static void row_prior(const job *jb, int64_t r) {
+    const ref_shape *s = jb->s;
+    int64_t gpr = s->cols / s->m;
+    double mag[MAX_M];
+    for (int64_t q = 0; q < gpr; ++q) {
+        int64_t local = (r - jb->rb) * gpr + q;
+        for (int32_t j = 0; j < s->m; ++j)
+            mag[j] = fabs(load_w(jb->w, s->wtype, (r - jb->rb) * s->cols + q * s->m + j));
+        int32_t k = prior_candidate(&jb->ctx, mag);
+        float *l = (float *)jb->out + local * jb->ctx.K;
+        for (int32_t i = 0; i < jb->ctx.K; ++i) l[i] = i == k ? (float)jb->ctx.kappa : 0.0f;
+        if (jb->hard) jb->hard[local] = (uint8_t)k;
+    }
+}
+
+int32_t ref_prior_init(const ref_shape *shape, int64_t row_begin, int64_t row_end, const void *w,
+                       float alpha, float *logits, uint8_t *prior_idx, int32_t nthreads) {
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    /* alpha travels in the kappa slot of the context */
+    if (!window_ok(shape, row_begin, row_end) || !init_ctx(&jb.ctx, shape, (double)alpha, 1.0, 0, 0))
+        return -1;
+    if (row_end > row_begin && (!w || !logits)) return -1;
+    jb.s = shape;
+    jb.rb = row_begin;
+    jb.w = w;
+    jb.out = logits;
+    jb.hard = prior_idx;
+    jb.fn = row_prior;
+    run_rows(&jb, row_begin, row_end, nthreads);
+    return 0;
+}

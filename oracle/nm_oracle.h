@@ -116,6 +116,13 @@ int32_t ref_pack(const ref_shape *shape, int64_t row_begin, int64_t row_end, con
 int32_t ref_unpack(const ref_shape *shape, int64_t row_begin, int64_t row_end,
                    const void *values, const uint32_t *indices, void *dense, int32_t nthreads);
 
+/* --- magnitude prior -------------------------------------------------------------------- */
+/* logits [rows, cols/m, K] fp32 (overwritten): alpha on the candidate that keeps the n largest
+ * |w| of the group (n rounds of "first largest |w| among unchosen positions"), 0 elsewhere;
+ * prior_idx [rows, cols/m] (optional) gets that candidate's index. */
+int32_t ref_prior_init(const ref_shape *shape, int64_t row_begin, int64_t row_end, const void *w,
+                       float alpha, float *logits, uint8_t *prior_idx, int32_t nthreads);
+
 /* number of worker threads a call with this nthreads argument uses */
 int32_t ref_threads_used(int32_t nthreads);
 

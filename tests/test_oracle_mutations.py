@@ -45,6 +45,9 @@ MUTANTS = {
                           "put_bits(idx, (q * s->m + t) * nb, (uint32_t)j, nb);"),
     "pack_bits_for_m8": ("while ((1 << b) < m) ++b;", "while ((1 << b) < m) ++b;\n    if (m == 8) b = 4;"),
     "unpack_no_zero_fill": ("for (int64_t c = 0; c < s->cols; ++c) zero_w(jb->out, lr * s->cols + c, s->wtype);", ""),
+    "prior_takes_last_of_ties": ("if (best < 0 || mag[j] > mag[best]) best = j;",
+                                 "if (best < 0 || mag[j] >= mag[best]) best = j;"),
+    "prior_signed_magnitude": ("mag[j] = fabs(load_w(", "mag[j] = (load_w("),
     "candidates_skip_last": ("for (int32_t p = start; p <= m - (n - depth); ++p)",
                              "for (int32_t p = start; p < m - (n - depth); ++p)"),
 }

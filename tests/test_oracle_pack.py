@@ -152,3 +152,53 @@ def test_magnitude_prior_keeps_the_largest_magnitudes():
     assert nm_synth.magnitude_prior_index(w, 2, 4)[0, 0] == 0   # keeps {0, 1}
     L = nm_synth.prior_logits(w, 2, 4, seed=1)
     np.testing.assert_array_equal(oracle.harden(L, 2, 4), nm_synth.magnitude_prior_index(w, 2, 4))
+
+
+# --- magnitude prior (the step before the path) ----------------------------------------------
+
+def _brute_prior(group, n):
+    """The n largest magnitudes; equal magnitudes keep the lower position (stable ranking)."""
+    return tuple(sorted(sorted(range(len(group)), key=lambda j: (-abs(group[j]), j))[:n]))
+
+
+@pytest.mark.parametrize("n,m", NM)
+@pytest.mark.parametrize("wtype", [torch.float32, torch.bfloat16])
+def test_prior_init_keeps_the_largest_magnitudes(n, m, wtype):
+    rows, cols = 6, m * 24
+    w = nm_synth.normal((rows, cols), 0.02, 11, wtype)
+    w[0, :m] = 0.5                                   # all tied
+    w[1, :m] = torch.tensor([0.5, -0.5] * (m // 2))  # tied magnitudes, opposite signs
+    w[2, :m] = 0.0
+    w[2, 1] = -0.0                                   # -0.0 and +0.0 have equal magnitude
+    logits, idx = oracle.prior_init(w, n, m, alpha=2.5)
+    cand = list(itertools.combinations(range(m), n))
+    a = w.float().numpy()
+    for r in range(rows):
+        for q in range(cols // m):
+            keep = _brute_prior(list(a[r, q * m:(q + 1) * m]), n)
+            k = cand.index(keep)
+            assert idx[r, q] == k
+            want = np.zeros(len(cand), np.float32)
+            want[k] = 2.5
+            assert logits[r, q].tobytes() == want.tobytes()
+    # the input generator's torch implementation of the same rule agrees
+    np.testing.assert_array_equal(idx, nm_synth.magnitude_prior_index(w, n, m).numpy())
+    # and its logits are exactly alpha * onehot
+    assert set(np.unique(logits)) <= {0.0, 2.5}
+
+
+def test_prior_init_nan_rule():
+    """A NaN magnitude is taken only as the first unchosen position (no comparison favours it)."""
+    w = torch.tensor([[float("nan"), 1.0, 2.0, 3.0, 1.0, float("nan"), 2.0, 0.5]])
+    _, idx = oracle.prior_init(w, 2, 4)
+    cand = list(itertools.combinations(range(4), 2))
+    assert cand[idx[0, 0]] == (0, 3)   # NaN first, then the largest of the rest
+    assert cand[idx[0, 1]] == (0, 2)   # 1.0 first (NaN never beats it), then 2.0
+
+
+def test_prior_init_windows_match_the_whole_matrix():
+    w = nm_synth.normal((9, 64), 1.0, 12, torch.bfloat16)
+    full_l, full_i = oracle.prior_init(w, 2, 4)
+    win_l, win_i = oracle.prior_init(w[3:7], 2, 4, rows=9, row_begin=3)
+    np.testing.assert_array_equal(win_l, full_l[3:7])
+    np.testing.assert_array_equal(win_i, full_i[3:7])
