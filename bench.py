@@ -42,11 +42,13 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama7b_layer",
-                   choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256"],
+                   choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256",
+                            "prior_init"],
                    help="llama7b_layer (default): one LLaMA-2-7B-shaped layer per step; sweep32: 32 such "
                         "layers x 10 annealed steps of fwd+bwd+pack; general_nm: 4096x11008 with 1:4, 2:8, "
                         "4:8; nemotron_pack: pack+unpack of every Nemotron-15B-shaped matrix; single256: "
-                        "one 256x256 fp32 weight (latency-bound)")
+                        "one 256x256 fp32 weight (latency-bound); prior_init: magnitude-prior "
+                        "logit initialisation")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -390,13 +392,54 @@ def workload_single256(args):
     return {"metric": "launch latency, one 256x256 fp32 weight", "unit": "us", "results": res}
 
 
+def workload_prior_init(args):
+    """Magnitude-prior logit initialisation of every matrix of one LLaMA-7B-shaped layer (2:4,
+    alpha 3) and of a 4096x11008 matrix for 2:8 and 4:8: read w, write the K logits of each group
+    (and the one-byte prior index where noted)."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    res = {}
+    cases = [("2:4 layer", 2, 4, nm_synth.LLAMA2_7B_LAYER, False),
+             ("2:4 layer +idx", 2, 4, nm_synth.LLAMA2_7B_LAYER, True),
+             ("2:8 4096x11008", 2, 8, [("down", 4096, 11008)], False),
+             ("4:8 4096x11008", 4, 8, [("down", 4096, 11008)], False)]
+    for label, n, m, shapes, with_idx in cases:
+        k = S.num_candidates(n, m)
+        mats = []
+        for i, (name, rows, cols) in enumerate(shapes):
+            w = nm_synth.normal((rows, cols), 0.02, 3 * nm_synth.input_seed(2, 0, i), torch.bfloat16, device=dev)
+            mats.append((w, torch.empty((rows, cols // m, k), device=dev),
+                         torch.empty((rows, cols // m), dtype=torch.uint8, device=dev) if with_idx else None))
+        weights = sum(w.numel() for w, _, _ in mats)
+
+        def run(r):
+            for w, L, ix in mats:
+                S.nm_prior_init(w, n, m, 3.0, out=(L, ix))
+
+        run(0)
+        t = _elapsed_ms(run, reps=args.kernel_reps)
+        bpw = WB + 4 * k / m + (1 / m if with_idx else 0)
+        gbps = bpw * weights / (t * 1e-3) / 1e9
+        res[label] = {"ms_per_pass": round(t, 4), "avg_launch_us": round(t * 1e3 / len(mats), 2),
+                      "bytes_per_weight": bpw, "GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+        del mats
+    return {"metric": "magnitude-prior logit initialisation", "unit": "GB/s",
+            "config": {"workload": "LLaMA-2-7B-shaped layer (202,375,168 bf16 weights) at 2:4; "
+                                   "4096x11008 bf16 at 2:8 and 4:8; alpha=3"}, "results": res}
+
+
 def main():
     args = parse()
     if args.workload != "llama7b_layer":
         import torch
         torch.cuda.set_device(0)
         fn = {"sweep32": workload_sweep32, "general_nm": workload_general_nm,
-              "nemotron_pack": workload_nemotron_pack, "single256": workload_single256}[args.workload]
+              "nemotron_pack": workload_nemotron_pack, "single256": workload_single256,
+              "prior_init": workload_prior_init}[args.workload]
         out = fn(args)
         out.update({"n_gpus": 1, "data": "synthetic, seeded, generated on the GPU", "dtype": "f32"})
         print(json.dumps(out), flush=True)

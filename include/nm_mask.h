@@ -126,6 +126,21 @@ nm_status nm_mask_harden_pack(const nm_shape *shape, const void *w, const float 
 nm_status nm_unpack(const nm_shape *shape, const void *values, const uint32_t *indices,
                     void *w_dense, void *stream);
 
+/* Magnitude-prior initialisation of the logits, the step before the learnable layer
+ * (MaskLLM project page, Table 2 caption: prior masks initialise the logits; "Accelerating
+ * Sparse Deep Neural Networks" summary page, section 4.1: magnitude pruning keeps the largest
+ * magnitudes of each group).  Per group the prior candidate keeps the n largest |w|: n rounds,
+ * each taking the first not yet taken position whose |w| no earlier free position reaches, so
+ * equal magnitudes keep the lower position and a NaN is taken only as the first free position.
+ * Its logit is alpha, every other logit of the group +0.0.
+ *   w          [rows, cols] wtype, read
+ *   alpha      finite (any sign), else NM_EINVAL
+ *   logits     [rows, cols/m, K] fp32, overwritten
+ *   prior_idx  [rows, cols/m] uint8, written with the prior candidate's index; may be NULL
+ *              (no alignment requirement) */
+nm_status nm_prior_init(const nm_shape *shape, float alpha, const void *w, float *logits,
+                        uint8_t *prior_idx, void *stream);
+
 /* ---- host-only helpers (no device work, no HIP call) ---------------------------------- */
 /* K = C(m, n) for a supported (n, m), else -1. */
 int32_t nm_num_candidates(int32_t n, int32_t m);

@@ -53,6 +53,7 @@ def lib():
             "ref_unpack": (i32, [P, i64, i64, P, P, P, i32]),
             "ref_threads_used": (i32, [i32]),
             "ref_prior_init": (i32, [P, i64, i64, P, ctypes.c_float, P, P, i32]),
+            "ref_monitor": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, P, P, P, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -296,3 +297,24 @@ def prior_init(w, n, m, alpha=3.0, rows=None, row_begin=0, nthreads=0):
                               _ptr(logits), _ptr(idx), nthreads)
     _check(rc, "prior_init")
     return logits, idx
+
+
+def monitor(logits, n, m, kappa, tau, seed, offset, prev_sample=None, rows=None, row_begin=0,
+            nthreads=0):
+    """Per group of the window: (max probability of softmax(kappa*l) float64, sampled candidate
+    uint8, L1 distance to prev_sample uint8 or None) -- all [window_rows, cols/m]."""
+    L = _contig(logits, np.float32)
+    wr, gpr, K = L.shape
+    rows = wr if rows is None else rows
+    maxp = _unwritten((wr, gpr), np.float64)
+    samp = _unwritten((wr, gpr), np.uint8)
+    prev = None if prev_sample is None else _contig(prev_sample, np.uint8)
+    if prev is not None and prev.shape != (wr, gpr):
+        raise ValueError("prev_sample must be [window_rows, cols/m]")
+    l1 = None if prev is None else _unwritten((wr, gpr), np.uint8)
+    s = _shape(rows, gpr * m, n, m, F32)
+    rc = lib().ref_monitor(ctypes.byref(s), kappa, tau, seed, offset, row_begin,
+                           _window(wr, row_begin, rows), _ptr(L), None if prev is None else _ptr(prev),
+                           _ptr(maxp), _ptr(samp), None if l1 is None else _ptr(l1), nthreads)
+    _check(rc, "monitor")
+    return maxp, samp, l1

@@ -623,3 +623,76 @@ int32_t ref_prior_init(const ref_shape *shape, int64_t row_begin, int64_t row_en
     run_rows(&jb, row_begin, row_end, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Convergence monitors (MaskLLM project page, Fig. 5 caption): (a) the L1 distance between the
+ * masks sampled at adjacent training steps, (b) the largest probability of the mask
+ * distribution.  Readings: the distribution is p = softmax(kappa * l) (the one the Gumbel
+ * softmax relaxes, no noise); the step's sampled mask is the candidate with the largest
+ * perturbed score (kappa*l_k + g_k)/tau of that step's noise (Gumbel-max, first one on exact
+ * ties); the L1 distance of two 0/1 masks counts the positions where they differ.  A previous
+ * index outside [0, K) stands for the empty mask. */
+static double group_max_prob(const group_ctx *c, const float *l) {
+    double lmax = -INFINITY;
+    for (int32_t k = 0; k < c->K; ++k)
+        if ((double)l[k] > lmax) lmax = (double)l[k];
+    double sum = 0.0;
+    for (int32_t k = 0; k < c->K; ++k) sum += exp(c->kappa * ((double)l[k] - lmax));
+    return 1.0 / sum; /* p_max = exp(0) / sum */
+}
+
+static int32_t group_sample(const group_ctx *c, int64_t g, const float *l) {
+    int32_t best = 0;
+    double zbest = 0.0;
+    for (int32_t k = 0; k < c->K; ++k) {
+        uint32_t x = ref_noise_word(c->seed, c->offset, (uint64_t)g * (uint64_t)c->K + (uint64_t)k);
+        double z = (c->kappa * (double)l[k] + ref_gumbel(x)) / c->tau;
+        if (k == 0 || z > zbest) {
+            best = k;
+            zbest = z;
+        }
+    }
+    return best;
+}
+
+static int32_t mask_l1(const group_ctx *c, int32_t k, int32_t prev) {
+    uint32_t a = c->cand[k], b = (prev >= 0 && prev < c->K) ? c->cand[prev] : 0u;
+    int32_t d = 0;
+    for (int32_t j = 0; j < c->m; ++j) d += (int32_t)((a >> j & 1u) != (b >> j & 1u));
+    return d;
+}
+
+static void row_monitor(const job *jb, int64_t r) {
+    const ref_shape *s = jb->s;
+    int64_t gpr = s->cols / s->m;
+    for (int64_t q = 0; q < gpr; ++q) {
+        int64_t g = r * gpr + q;
+        int64_t local = (r - jb->rb) * gpr + q;
+        const float *l = jb->logits + local * jb->ctx.K;
+        ((double *)jb->out)[local] = group_max_prob(&jb->ctx, l);
+        int32_t k = group_sample(&jb->ctx, g, l);
+        jb->hard[local] = (uint8_t)k;
+        if (jb->grad)
+            ((uint8_t *)jb->out2)[local] = (uint8_t)mask_l1(&jb->ctx, k, ((const uint8_t *)jb->grad)[local]);
+    }
+}
+
+int32_t ref_monitor(const ref_shape *shape, double kappa, double tau, uint64_t seed, uint64_t offset,
+                    int64_t row_begin, int64_t row_end, const float *logits, const uint8_t *prev_sample,
+                    double *max_prob, uint8_t *sample, uint8_t *l1, int32_t nthreads) {
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    if (!window_ok(shape, row_begin, row_end) || !init_ctx(&jb.ctx, shape, kappa, tau, seed, offset))
+        return -1;
+    if (row_end > row_begin && (!logits || !max_prob || !sample || (prev_sample && !l1))) return -1;
+    jb.s = shape;
+    jb.rb = row_begin;
+    jb.logits = logits;
+    jb.grad = prev_sample;
+    jb.out = max_prob;
+    jb.out2 = l1;
+    jb.hard = sample;
+    jb.fn = row_monitor;
+    run_rows(&jb, row_begin, row_end, nthreads);
+    return 0;
+}

@@ -123,6 +123,15 @@ int32_t ref_unpack(const ref_shape *shape, int64_t row_begin, int64_t row_end,
 int32_t ref_prior_init(const ref_shape *shape, int64_t row_begin, int64_t row_end, const void *w,
                        float alpha, float *logits, uint8_t *prior_idx, int32_t nthreads);
 
+/* --- convergence monitors ------------------------------------------------------------------ */
+/* Per group of the window: max_prob = max_k softmax(kappa*l)_k (no noise); sample = the index of
+ * the largest (kappa*l_k + g_k)/tau with the noise of (seed, offset), first one on exact ties;
+ * if prev_sample is given, l1 = number of positions where the masks of sample and prev_sample
+ * differ (a prev_sample entry >= K stands for the empty mask).  All three are [window groups]. */
+int32_t ref_monitor(const ref_shape *shape, double kappa, double tau, uint64_t seed, uint64_t offset,
+                    int64_t row_begin, int64_t row_end, const float *logits, const uint8_t *prev_sample,
+                    double *max_prob, uint8_t *sample, uint8_t *l1, int32_t nthreads);
+
 /* number of worker threads a call with this nthreads argument uses */
 int32_t ref_threads_used(int32_t nthreads);
 

@@ -11,6 +11,7 @@ Entry points, named as in the C ABI:
     nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset) -> grad_logits
     nm_mask_harden_pack(w, logits, n, m, with_hard=False)             -> values, indices[, hard]
     nm_unpack(values, indices, cols, n, m)                            -> w_dense
+    nm_prior_init(w, n, m, alpha, with_idx=False)                     -> logits[, prior_idx]
 and `mask(...)`, the autograd function whose backward is nm_mask_backward (the weights are frozen
 and get no gradient).
 """
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "nm_mask_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
     "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nm_candidate_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P]),
     "nm_packed_value_elems": (ctypes.c_int64, [_P]),
@@ -223,6 +225,26 @@ def nm_unpack(values, indices, cols, n, m, out=None):
     return out
 
 
+def nm_prior_init(w, n, m, alpha, with_idx=False, out=None):
+    """Logits initialised from the magnitude prior: alpha on the candidate keeping the n largest
+    |w| of each group, 0 elsewhere (MaskLLM project page, Table 2 caption; "Accelerating Sparse
+    Deep Neural Networks" summary page, section 4.1).  Returns logits[, prior_idx uint8]."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    lshape = _logit_shape(rows, cols, n, m)
+    if out is None:
+        logits = torch.empty(lshape, dtype=torch.float32, device=w.device)
+        idx = torch.empty((rows, cols // m), dtype=torch.uint8, device=w.device) if with_idx else None
+    else:
+        logits, idx = out
+    st = lib().nm_prior_init(ctypes.byref(sh), float(alpha), _dev(w, "w"),
+                             _dev(logits, "logits", torch.float32, lshape),
+                             None if idx is None else _dev(idx, "prior_idx", torch.uint8, (rows, cols // m)),
+                             _stream(w.device))
+    _check(st, "nm_prior_init")
+    return (logits, idx) if with_idx else logits
+
+
 # ---------------------------------------------------------------------------------------------
 # diagnostics (same device functions as the kernels)
 
@@ -290,6 +312,6 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
 
 
 __all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
-           "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "nm_prior_init", "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
-           "NMError", "EXPORTS", "library_path", "math"]
+           "NMError", "EXPORTS", "library_path"]

@@ -198,6 +198,20 @@ nm_status nm_unpack(const nm_shape* shape, const void* values, const uint32_t* i
     return launched(nm::launch_unpack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
+nm_status nm_prior_init(const nm_shape* shape, float alpha, const void* w, float* logits,
+                        uint8_t* prior_idx, void* stream) {
+    int64_t groups;
+    int32_t K;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if (!isfinite(alpha)) return NM_EINVAL;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits)) return NM_EALIGN;
+    nm::PriorArgs a{w, logits, prior_idx, groups, alpha};
+    return launched(nm::launch_prior(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
 nm_status nm_debug_noise(const nm_shape* shape, const nm_sample* sample, uint32_t* words, void* stream) {
     int64_t groups;
     int32_t K;

@@ -739,6 +739,66 @@ __global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Magnitude prior ("Accelerating Sparse Deep Neural Networks" summary page, section 4.1:
+// magnitude pruning keeps the largest magnitudes of each group; MaskLLM project page, Table 2
+// caption: prior masks initialise the learnable logits).  Per group the candidate that keeps the
+// N largest |w| is found in N rounds, each taking the first free position whose magnitude no
+// earlier free position reaches (ties keep the lower position; a NaN is taken only as the first
+// free position, since no comparison favours it).  Its logit is alpha, the others 0.
+
+template <int N, int M>
+__device__ __forceinline__ int prior_candidate(const float* w) {
+    constexpr int K = Candidates<N, M>::K;
+    float mag[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) mag[j] = fabsf(w[j]);
+    uint32_t chosen = 0u;
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        int best = -1;
+        float bm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const bool take = !((chosen >> j) & 1u) && (best < 0 || mag[j] > bm);
+            best = take ? j : best;
+            bm = take ? mag[j] : bm;
+        }
+        chosen |= 1u << best;
+    }
+    int kstar = 0;
+    static_for<0, K>([&](auto kc) NM_INLINE {
+        constexpr int k = decltype(kc)::value;
+        kstar = chosen == cand_keep<N, M, k>() ? k : kstar;
+    });
+    return kstar;
+}
+
+template <int N, int M, typename T>
+__global__ __launch_bounds__(kThreads) void k_prior(PriorArgs a) {
+    using S = Sample<N, M>;
+    constexpr int K = S::K, P = S::P, PK = S::PK;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t g0 = t * P;
+    if (g0 >= a.groups) return;
+    const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
+    const bool full = nvalid == P;
+
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
+    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
+    float w[P * M];
+    load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
+    float l[PK];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int kstar = prior_candidate<N, M>(w + p * M);
+#pragma unroll
+        for (int k = 0; k < K; ++k) l[p * K + k] = k == kstar ? a.alpha : 0.0f;
+        if (a.idx && p < nvalid) a.idx[g0 + p] = (uint8_t)kstar;
+    }
+    store_dlogits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+}
+
+// ------------------------------------------------------------------------------------------
 // Diagnostics: raw noise words and the base-2 Gumbel exponent, from the same device functions.
 
 __global__ __launch_bounds__(kThreads) void k_debug_noise(NoiseArgs a) {
@@ -843,6 +903,15 @@ hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s
 }
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s) {
     NM_DISPATCH(unpack_nmt, n, m, wtype, a, s);
+}
+template <int N, int M, typename T>
+static hipError_t prior_nmt(const PriorArgs& a, hipStream_t s) {
+    const int64_t threads = (a.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
+    k_prior<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s) {
+    NM_DISPATCH(prior_nmt, n, m, wtype, a, s);
 }
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s) {
     k_debug_noise<<<grid_for((a.slots + 3) / 4), kThreads, 0, s>>>(a);

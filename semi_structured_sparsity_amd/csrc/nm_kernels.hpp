@@ -51,6 +51,14 @@ struct UnpackArgs {
     int32_t aligned;         // rows of values and dense start on 16-byte boundaries
 };
 
+struct PriorArgs {
+    const void* w;
+    float* logits;
+    uint8_t* idx;        // may be null
+    int64_t groups;
+    float alpha;
+};
+
 struct NoiseArgs {
     uint32_t* words;
     int64_t slots;       // groups * K
@@ -67,6 +75,7 @@ hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_m
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
+hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s);
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
 hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s);
 int groups_per_thread(int n, int m);

@@ -24,7 +24,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = S.lib()
     declared = _declared()
-    assert len(declared) >= 13
+    assert len(declared) >= 14
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(S.EXPORTS)
@@ -57,6 +57,7 @@ def test_bad_shapes_are_rejected_on_the_host(kw, status):
     assert L.nm_unpack(sh, FAKE, FAKE, FAKE, None) == status
     assert L.nm_debug_noise(sh, _sample(), FAKE, None) == status
     assert L.nm_debug_soft_mask(sh, _sample(), FAKE, FAKE, None) == status
+    assert L.nm_prior_init(sh, 3.0, FAKE, FAKE, FAKE, None) == status
     assert L.nm_packed_value_elems(sh) == -1 and L.nm_index_words_per_row(sh) == -1
 
 
@@ -100,6 +101,14 @@ def test_null_and_misaligned_pointers_are_rejected_on_the_host():
         assert L.nm_unpack(sh, *args, None) == NM_EINVAL
         args[i] = ODD
         assert L.nm_unpack(sh, *args, None) == NM_EALIGN
+    for i in range(2):
+        args = [FAKE] * 2
+        args[i] = None
+        assert L.nm_prior_init(sh, 3.0, *args, FAKE, None) == NM_EINVAL
+        args[i] = ODD
+        assert L.nm_prior_init(sh, 3.0, *args, FAKE, None) == NM_EALIGN
+    for alpha in (float("nan"), float("inf"), -float("inf")):
+        assert L.nm_prior_init(sh, alpha, FAKE, FAKE, None, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(FAKE, FAKE, -1, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(None, FAKE, 5, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(ODD, FAKE, 5, None) == NM_EALIGN
@@ -117,6 +126,7 @@ def test_empty_matrices_are_valid_and_launch_nothing(rows, cols):
     assert L.nm_debug_noise(sh, sm, None, None) == NM_OK
     assert L.nm_debug_soft_mask(sh, sm, None, None, None) == NM_OK
     assert L.nm_debug_gumbel_log2(None, None, 0, None) == NM_OK
+    assert L.nm_prior_init(sh, 3.0, None, None, None, None) == NM_OK
     assert L.nm_packed_value_elems(sh) == 0
 
 

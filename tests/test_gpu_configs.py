@@ -151,6 +151,13 @@ def test_config2_llama7b_layer(i):
     prior = nm_synth.magnitude_prior_index(w, n, m)
     _, _, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
     assert float((hard.long() == prior).double().mean()) > 0.999
+    # the prior-initialisation kernel over the whole matrix, every element against the oracle
+    del out, dl, G
+    Lp, ip = S.nm_prior_init(w, n, m, 3.0, with_idx=True)
+    rl, ri = oracle.prior_init(w.cpu(), n, m, alpha=3.0)
+    assert np.array_equal(ip.cpu().numpy(), ri)
+    assert np.array_equal(Lp.cpu().numpy().view(np.uint32), rl.view(np.uint32))
+    assert torch.equal(ip.long(), prior)
 
 
 def _schedule(step, steps=10):

@@ -217,6 +217,51 @@ def test_unpack_of_malformed_metadata_matches_oracle(n, m):
 
 
 # ---------------------------------------------------------------------------------------------
+# magnitude-prior initialisation of the logits
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("wtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,gpr", SHAPES + [(5, 41), (129, 33)])
+def test_prior_init_is_bit_exact(n, m, wtype, rows, gpr):
+    _say("prior", n, m, wtype, rows, gpr)
+    w = nm_synth.normal((rows, gpr * m), 0.02, 21, wtype)
+    w[0, :m] = 0.25                                     # all tied: the first n positions
+    if gpr > 1:
+        w[0, m:2 * m] = torch.tensor([-0.5, 0.5] * (m // 2))   # tied magnitudes, opposite signs
+    if gpr > 2:
+        w[0, 2 * m:3 * m] = 0.0
+        w[0, 2 * m + 1] = -0.0
+    if gpr > 3:
+        w[0, 3 * m + 1] = float("nan")                  # NaN never wins a comparison
+    if gpr > 4:
+        w[0, 4 * m] = float("nan")                      # NaN as the first free position
+        w[0, 4 * m + 2] = float("inf")
+    alpha = -2.75 if n == 3 else 3.0
+    logits, idx = S.nm_prior_init(w.to(DEV), n, m, alpha, with_idx=True)
+    rl, ri = oracle.prior_init(w, n, m, alpha=alpha)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(logits.cpu().numpy().view(np.uint32), rl.view(np.uint32))
+    # without the optional index output the logits are the same
+    assert torch.equal(S.nm_prior_init(w.to(DEV), n, m, alpha), logits)
+
+
+def test_prior_init_overwrites_and_feeds_the_hard_mask():
+    """Logits are overwritten (not accumulated); hardening the prior gives the prior's mask."""
+    n, m, rows, cols = 2, 4, 64, 1024
+    w = nm_synth.normal((rows, cols), 0.02, 22, torch.bfloat16).to(DEV)
+    logits = torch.full((rows, cols // m, 6), 7.0, device=DEV)
+    idx = torch.full((rows, cols // m), 255, dtype=torch.uint8, device=DEV)
+    S.nm_prior_init(w, n, m, 3.0, with_idx=True, out=(logits, idx))
+    assert set(torch.unique(logits).tolist()) == {0.0, 3.0}
+    _, _, hard = S.nm_mask_harden_pack(w, logits, n, m, with_hard=True)
+    assert torch.equal(hard, idx)
+    # the kept values are the two largest magnitudes of each group
+    values, _ = S.nm_mask_harden_pack(w, logits, n, m)
+    top = w.float().abs().view(-1, m).topk(n, dim=1).values.sum(1)
+    assert torch.equal(values.float().abs().view(-1, n).sum(1), top)
+
+
+# ---------------------------------------------------------------------------------------------
 # edge cases of the binding
 
 def test_empty_matrices():
@@ -228,6 +273,7 @@ def test_empty_matrices():
         assert S.nm_mask_backward(w, L, w, n, m, 1.0, 1.0, 0, 0).shape == (0, 8, K)
         v, i = S.nm_mask_harden_pack(w, L, n, m)
         assert v.numel() == 0 and i.numel() == 0
+        assert S.nm_prior_init(w, n, m, 3.0).shape == (0, 8, K)
 
 
 def test_misaligned_views_are_refused():

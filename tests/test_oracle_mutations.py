@@ -16,7 +16,8 @@ import pytest
 from oracle import build as oracle_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PINS = ["tests/test_oracle_noise.py", "tests/test_oracle_layer.py", "tests/test_oracle_pack.py"]
+PINS = ["tests/test_oracle_noise.py", "tests/test_oracle_layer.py", "tests/test_oracle_pack.py",
+        "tests/test_oracle_monitor.py"]
 
 MUTANTS = {
     "philox_swaps_hi_and_lo": ("uint32_t n0 = hi1 ^ x1 ^ k0;", "uint32_t n0 = lo1 ^ x1 ^ k0;"),
@@ -48,6 +49,17 @@ MUTANTS = {
     "prior_takes_last_of_ties": ("if (best < 0 || mag[j] > mag[best]) best = j;",
                                  "if (best < 0 || mag[j] >= mag[best]) best = j;"),
     "prior_signed_magnitude": ("mag[j] = fabs(load_w(", "mag[j] = (load_w("),
+    "monitor_max_prob_drops_kappa": ("sum += exp(c->kappa * ((double)l[k] - lmax));",
+                                     "sum += exp(((double)l[k] - lmax));"),
+    "monitor_sample_last_max": ("if (k == 0 || z > zbest) {", "if (k == 0 || z >= zbest) {"),
+    "monitor_sample_noise_subtracted": ("double z = (c->kappa * (double)l[k] + ref_gumbel(x)) / c->tau;",
+                                        "double z = (c->kappa * (double)l[k] - ref_gumbel(x)) / c->tau;"),
+    "monitor_sample_wrong_slot": ("(uint64_t)g * (uint64_t)c->K + (uint64_t)k);\n        double z =",
+                                  "(uint64_t)g * (uint64_t)c->K + (uint64_t)(k + 1));\n        double z ="),
+    "monitor_l1_counts_agreement": ("(int32_t)((a >> j & 1u) != (b >> j & 1u));",
+                                    "(int32_t)((a >> j & 1u) == (b >> j & 1u));"),
+    "monitor_prev_out_of_range_wraps": ("(prev >= 0 && prev < c->K) ? c->cand[prev] : 0u",
+                                        "c->cand[prev % c->K]"),
     "candidates_skip_last": ("for (int32_t p = start; p <= m - (n - depth); ++p)",
                              "for (int32_t p = start; p < m - (n - depth); ++p)"),
 }
