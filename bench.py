@@ -43,12 +43,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama7b_layer",
                    choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256",
-                            "prior_init"],
+                            "prior_init", "monitor"],
                    help="llama7b_layer (default): one LLaMA-2-7B-shaped layer per step; sweep32: 32 such "
                         "layers x 10 annealed steps of fwd+bwd+pack; general_nm: 4096x11008 with 1:4, 2:8, "
                         "4:8; nemotron_pack: pack+unpack of every Nemotron-15B-shaped matrix; single256: "
                         "one 256x256 fp32 weight (latency-bound); prior_init: magnitude-prior "
-                        "logit initialisation")
+                        "logit initialisation; monitor: forward with the fused Fig. 5 monitors")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -221,8 +221,12 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def _elapsed_ms(fn, reps=1):
+def _elapsed_ms(fn, reps=1, warm=None):
+    """Average ms of fn(r) over `reps` calls, after `warm` untimed calls (default: reps) that
+    bring the GPU to its working clocks."""
     import torch
+    for r in range(reps if warm is None else warm):
+        fn(r)
     a, b = _events()
     torch.cuda.synchronize()
     a.record()
@@ -392,6 +396,55 @@ def workload_single256(args):
     return {"metric": "launch latency, one 256x256 fp32 weight", "unit": "us", "results": res}
 
 
+def workload_monitor(args):
+    """Forward of one LLaMA-7B-shaped layer (2:4, kappa 100, tau 4, prior logits) with the fused
+    convergence monitors, next to the plain forward: per call the monitored kernel plus its
+    one-block reduction; algorithmic bytes add the sample written and the previous sample read
+    (1 byte per group each)."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    mats = make_layer(dev)
+    for mt in mats:
+        g = (mt["rows"], mt["cols"] // M)
+        mt["prev"] = torch.zeros(g, dtype=torch.uint8, device=dev)
+        mt["sample"] = torch.empty(g, dtype=torch.uint8, device=dev)
+        mt["stats"] = torch.zeros(2, dtype=torch.float64, device=dev)
+        mt["ws"] = torch.empty(S.monitor_workspace_bytes(mt["rows"], mt["cols"], N, M), dtype=torch.uint8,
+                               device=dev)
+    weights = nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
+
+    def plain(r):
+        for mt in mats:
+            run_pass(S, mt, "fwd", r)
+
+    def monitored(r):
+        for mt in mats:
+            S.nm_mask_forward_monitor(mt["w"], mt["L"], N, M, KAPPA, TAU, mt["seed"], r, prev_sample=mt["prev"],
+                                      out=(mt["out"], mt["sample"], mt["stats"]), workspace=mt["ws"])
+            mt["prev"], mt["sample"] = mt["sample"], mt["prev"]   # this step's sample is the next one's prev
+
+    plain(0)
+    monitored(0)
+    res = {}
+    for label, fn, bpw in (("fwd", plain, bytes_per_weight()["fwd"]),
+                           ("fwd+monitors", monitored, bytes_per_weight()["fwd"] + 2 / M)):
+        t = _elapsed_ms(fn, reps=args.kernel_reps)
+        gbps = bpw * weights / (t * 1e-3) / 1e9
+        res[label] = {"ms_per_pass": round(t, 4), "avg_call_us": round(t * 1e3 / len(mats), 2),
+                      "bytes_per_weight": bpw, "GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+    res["overhead_pct"] = round(100 * (res["fwd+monitors"]["ms_per_pass"] / res["fwd"]["ms_per_pass"] - 1), 1)
+    means = [(mt["stats"][0].item() / (mt["rows"] * mt["cols"] / M),
+              mt["stats"][1].item() / (mt["rows"] * mt["cols"] / M)) for mt in mats]
+    return {"metric": "forward with fused Fig. 5 monitors vs plain forward", "unit": "GB/s",
+            "config": {"workload": "LLaMA-2-7B-shaped decoder layer, 7 matrices, 202,375,168 bf16 weights, "
+                                   "2:4, kappa=100, tau=4, prior logits"},
+            "results": res, "monitor_means_last_call": [[round(a, 6), round(b, 6)] for a, b in means]}
+
+
 def workload_prior_init(args):
     """Magnitude-prior logit initialisation of every matrix of one LLaMA-7B-shaped layer (2:4,
     alpha 3) and of a 4096x11008 matrix for 2:8 and 4:8: read w, write the K logits of each group
@@ -439,7 +492,7 @@ def main():
         torch.cuda.set_device(0)
         fn = {"sweep32": workload_sweep32, "general_nm": workload_general_nm,
               "nemotron_pack": workload_nemotron_pack, "single256": workload_single256,
-              "prior_init": workload_prior_init}[args.workload]
+              "prior_init": workload_prior_init, "monitor": workload_monitor}[args.workload]
         out = fn(args)
         out.update({"n_gpus": 1, "data": "synthetic, seeded, generated on the GPU", "dtype": "f32"})
         print(json.dumps(out), flush=True)

@@ -97,6 +97,31 @@ typedef struct {
 nm_status nm_mask_forward(const nm_shape *shape, const nm_sample *sample, const void *w,
                           const float *logits, void *w_masked, void *stream);
 
+/* Forward with the convergence monitors of MaskLLM project page, Fig. 5 caption fused in: (a) the
+ * L1 distance between the masks sampled at adjacent training steps, (b) the largest probability
+ * of the mask distribution.  w_masked is the same as nm_mask_forward's (same sample); besides it,
+ * per group g:
+ *   sampled candidate  s_g = the first k with the largest (kappa*l_k + g_k)/tau for this step's
+ *                      noise (the Gumbel-max hard sample; the decision is taken in fp32, so on
+ *                      near-ties within the fp32 rounding of the scores either candidate may win)
+ *   max probability    p_g = max_k softmax(kappa * l)_k (the distribution itself, no noise)
+ *   L1 distance        d_g = number of positions where the masks of s_g and prev_sample[g]
+ *                      differ; a prev_sample entry >= K stands for the empty mask
+ *   w, logits, w_masked  as nm_mask_forward
+ *   prev_sample  [rows, cols/m] uint8, read, may be NULL (then no L1 distance is taken)
+ *   sample_idx   [rows, cols/m] uint8, written with s_g, may be NULL; pass it as the next step's
+ *                prev_sample (no alignment requirement for either)
+ *   stats        2 doubles, written: stats[0] = sum of p_g, stats[1] = sum of d_g (0 without
+ *                prev_sample); divide by the group count rows*cols/m for the means.  Left
+ *                untouched for an empty matrix (nothing is launched).
+ *   workspace    device memory of at least nm_monitor_workspace_bytes(shape) bytes, overwritten
+ *                with per-block partial sums; workspace_bytes is its size (NM_EINVAL if short).
+ * The sums are added in a fixed order: repeated calls give identical stats. */
+nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample, const void *w,
+                                  const float *logits, void *w_masked, const uint8_t *prev_sample,
+                                  uint8_t *sample_idx, double *stats, void *workspace,
+                                  int64_t workspace_bytes, void *stream);
+
 /* Backward to the logits (Fig. 3 caption: every step is differentiable).  With the upstream
  * gradient G = dL/dw_masked, d_k = sum over positions j kept by candidate k of G_j * w_j,
  * s = sum_k y_k d_k and grad_logits_k = (kappa/tau) * y_k * (d_k - s).  The noise is
@@ -152,6 +177,9 @@ int64_t nm_packed_value_elems(const nm_shape *shape);
 int64_t nm_index_words_per_row(const nm_shape *shape);
 /* rows * nm_index_words_per_row, or -1. */
 int64_t nm_packed_index_words(const nm_shape *shape);
+/* Workspace bytes nm_mask_forward_monitor needs for this shape (8 per block of its grid), or -1
+ * for an invalid shape. */
+int64_t nm_monitor_workspace_bytes(const nm_shape *shape);
 /* Static description of a status code. */
 const char *nm_status_str(nm_status status);
 

@@ -12,6 +12,8 @@ Entry points, named as in the C ABI:
     nm_mask_harden_pack(w, logits, n, m, with_hard=False)             -> values, indices[, hard]
     nm_unpack(values, indices, cols, n, m)                            -> w_dense
     nm_prior_init(w, n, m, alpha, with_idx=False)                     -> logits[, prior_idx]
+    nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None)
+                                                                      -> w_masked, sample, stats
 and `mask(...)`, the autograd function whose backward is nm_mask_backward (the weights are frozen
 and get no gradient).
 """
@@ -53,6 +55,8 @@ _SIGNATURES = {
     "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
+    "nm_mask_forward_monitor": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
+    "nm_monitor_workspace_bytes": (ctypes.c_int64, [_P]),
     "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nm_candidate_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P]),
     "nm_packed_value_elems": (ctypes.c_int64, [_P]),
@@ -169,6 +173,40 @@ def nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset, out=None):
                                _dev(out, "out", w.dtype, w.shape), _stream(w.device))
     _check(st, "nm_mask_forward")
     return out
+
+
+def monitor_workspace_bytes(rows, cols, n, m):
+    return lib().nm_monitor_workspace_bytes(ctypes.byref(_shape(rows, cols, n, m, NM_F32)))
+
+
+def nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None, out=None,
+                            workspace=None):
+    """The forward plus the convergence monitors (MaskLLM project page, Fig. 5 caption).
+    Returns (w_masked, sample uint8 [rows, cols/m], stats float64 [2] on the device) with
+    stats = (sum of the largest probability of softmax(kappa*l), sum of the L1 distance between
+    this step's sampled mask and prev_sample's) over all groups."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    need = lib().nm_monitor_workspace_bytes(ctypes.byref(sh))
+    if need < 0:
+        raise NMError(NM_EINVAL, "nm_mask_forward_monitor")
+    if out is None:
+        out = (torch.empty_like(w), torch.empty((rows, cols // m), dtype=torch.uint8, device=w.device),
+               torch.zeros(2, dtype=torch.float64, device=w.device))
+    w_masked, sample, stats = out
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    gshape = (rows, cols // m)
+    st = lib().nm_mask_forward_monitor(
+        ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)), _dev(w, "w"),
+        _dev(logits, "logits", torch.float32, _logit_shape(rows, cols, n, m)),
+        _dev(w_masked, "w_masked", w.dtype, w.shape),
+        None if prev_sample is None else _dev(prev_sample, "prev_sample", torch.uint8, gshape),
+        None if sample is None else _dev(sample, "sample", torch.uint8, gshape),
+        _dev(stats, "stats", torch.float64, (2,)), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(w.device))
+    _check(st, "nm_mask_forward_monitor")
+    return w_masked, sample, stats
 
 
 def nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset, out=None):
@@ -312,6 +350,6 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
 
 
 __all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
-           "nm_prior_init", "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
            "NMError", "EXPORTS", "library_path"]

@@ -131,6 +131,35 @@ nm_status nm_mask_forward(const nm_shape* shape, const nm_sample* sample, const 
     return launched(nm::launch_forward(shape->n, shape->m, shape->wtype, a, false, (hipStream_t)stream));
 }
 
+int64_t nm_monitor_workspace_bytes(const nm_shape* shape) {
+    int64_t groups;
+    int32_t K;
+    if (check_shape(shape, &groups, &K) != NM_OK) return -1;
+    return 8 * nm::monitor_parts(shape->n, shape->m, groups);
+}
+
+nm_status nm_mask_forward_monitor(const nm_shape* shape, const nm_sample* sample, const void* w,
+                                  const float* logits, void* w_masked, const uint8_t* prev_sample,
+                                  uint8_t* sample_idx, double* stats, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !w_masked || !stats || !workspace) return NM_EINVAL;
+    if (workspace_bytes < 8 * nm::monitor_parts(shape->n, shape->m, groups)) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked) || !aligned16(stats) ||
+        !aligned16(workspace))
+        return NM_EALIGN;
+    const float A0 = (float)((double)sample->kappa * 1.4426950408889634074);
+    nm::MonitorArgs a{nm::FwdArgs{w, logits, w_masked, groups, A, B, noise_key(sample)},
+                      prev_sample, sample_idx, static_cast<float2*>(workspace), stats, A0};
+    return launched(nm::launch_forward_monitor(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
 nm_status nm_debug_soft_mask(const nm_shape* shape, const nm_sample* sample, const float* logits,
                              float* soft_mask, void* stream) {
     int64_t groups;

@@ -21,6 +21,15 @@ struct FwdArgs {
     NoiseKey nk;
 };
 
+struct MonitorArgs {
+    FwdArgs f;           // the forward's arguments (f.out = w_masked)
+    const uint8_t* prev; // previous step's sampled candidates, may be null
+    uint8_t* sample;     // this step's sampled candidates, may be null
+    float2* part;        // per-block sums (monitor_parts entries)
+    double* stats;       // [2]: sum of p_max, sum of l1
+    float A0;            // kappa*log2(e)
+};
+
 struct BwdArgs {
     const void* w;
     const float* logits;
@@ -75,6 +84,8 @@ hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_m
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
+hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a, hipStream_t s);
+int64_t monitor_parts(int n, int m, int64_t groups);
 hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s);
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
 hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s);

@@ -66,3 +66,54 @@ def candidate_sums(w, grad, n, m, cand_matrix):
     a = (np.asarray(grad, np.float64) * np.asarray(w, np.float64))
     rows, cols = a.shape
     return a.reshape(rows, cols // m, m) @ cand_matrix.T
+
+
+# --- convergence monitors -------------------------------------------------------------------
+
+LN2 = 0.6931471805599453
+H_ABS_MAX = 24.0   # |log2(-log2 u)| over the 2^23 uniform cells (u in [2^-24, 1 - 2^-24])
+
+
+def perturbed_scores(L, kappa, tau, words, gumbel):
+    """z = (kappa * l + g) / tau in float64, with g the oracle's Gumbel samples of `words`."""
+    L = np.asarray(L, np.float64)
+    g = np.asarray(gumbel(words), np.float64).reshape(L.shape)
+    return (kappa * L + g) / tau
+
+
+def sample_bound(L, kappa, tau):
+    """Largest error of the kernel's fp32 comparison of two candidates' scores, in units of z,
+    per group: the Gumbel exponent h = log2(-log2 u) is within 2^-21 + 2 ulp(h) (2 ulp <=
+    2^-22 |h|) and enters as h / tau; the fp32 head and residual of z' = A l - B h round
+    relative to |A l| + |B h| (2^-23 covers both roundings); two candidates, base 2 -> base e."""
+    L = np.abs(np.asarray(L, np.float64))
+    A = kappa * 1.4426950408889634 / tau
+    B = 1.0 / tau
+    per = B * (2.0**-21 + 2.0**-22 * H_ABS_MAX) + 2.0**-23 * (A * L.max(-1) + B * H_ABS_MAX)
+    return 2.0 * LN2 * per
+
+
+def sample_check(got, ref, z, bound):
+    """Sampled candidates: equal wherever the oracle's top-two margin exceeds the bound; where
+    they differ, the GPU's candidate scores within the bound of the top.  Returns the number of
+    groups that differ (all of them near-ties)."""
+    got = np.asarray(got).astype(np.int64)
+    ref = np.asarray(ref).astype(np.int64)
+    zs = np.sort(z, -1)
+    margin = zs[..., -1] - zs[..., -2]
+    diff = got != ref
+    assert not (diff & (margin > bound)).any(), "sample differs where the oracle's choice is unique"
+    zg = np.take_along_axis(z, got[..., None], -1)[..., 0]
+    assert (zs[..., -1] - zg <= bound)[diff].all(), "sample is not among the near-tied top candidates"
+    return int(diff.sum())
+
+
+def l1_of(sample, prev, cand_bits):
+    """Sum over groups of popcount(mask(sample) xor mask(prev)); prev >= K: the empty mask."""
+    bits = np.asarray(cand_bits, np.int64)
+    K = bits.size
+    s = bits[np.asarray(sample).astype(np.int64)]
+    p = np.asarray(prev).astype(np.int64)
+    pb = np.where(p < K, bits[np.minimum(p, K - 1)], 0)
+    x = s ^ pb
+    return int(sum(((x >> j) & 1).sum() for j in range(8)))

@@ -24,7 +24,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = S.lib()
     declared = _declared()
-    assert len(declared) >= 14
+    assert len(declared) >= 16
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(S.EXPORTS)
@@ -58,6 +58,9 @@ def test_bad_shapes_are_rejected_on_the_host(kw, status):
     assert L.nm_debug_noise(sh, _sample(), FAKE, None) == status
     assert L.nm_debug_soft_mask(sh, _sample(), FAKE, FAKE, None) == status
     assert L.nm_prior_init(sh, 3.0, FAKE, FAKE, FAKE, None) == status
+    assert L.nm_mask_forward_monitor(sh, _sample(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     1 << 40, None) == status
+    assert L.nm_monitor_workspace_bytes(sh) == -1
     assert L.nm_packed_value_elems(sh) == -1 and L.nm_index_words_per_row(sh) == -1
 
 
@@ -69,6 +72,8 @@ def test_bad_samples_are_rejected_on_the_host(kappa, tau):
     assert L.nm_mask_forward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_mask_backward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_debug_soft_mask(_shape(), _sample(kappa, tau), FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_forward_monitor(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, None, None,
+                                     FAKE, FAKE, 1 << 20, None) == NM_EINVAL
 
 
 def test_null_and_misaligned_pointers_are_rejected_on_the_host():
@@ -107,6 +112,19 @@ def test_null_and_misaligned_pointers_are_rejected_on_the_host():
         assert L.nm_prior_init(sh, 3.0, *args, FAKE, None) == NM_EINVAL
         args[i] = ODD
         assert L.nm_prior_init(sh, 3.0, *args, FAKE, None) == NM_EALIGN
+    big = 1 << 20
+    for i in range(5):   # w, logits, w_masked, stats, workspace
+        args = [FAKE] * 5
+        args[i] = None
+        mon = lambda a: L.nm_mask_forward_monitor(sh, sm, a[0], a[1], a[2], None, None, a[3], a[4], big, None)
+        assert mon(args) == NM_EINVAL
+        args[i] = ODD
+        assert mon(args) == NM_EALIGN
+    # prev_sample and sample are optional and need no alignment
+    assert L.nm_mask_forward_monitor(sh, sm, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0, None) == NM_EINVAL
+    need = L.nm_monitor_workspace_bytes(sh)
+    assert need == 8   # 16 groups of 2:4: one block of 256 threads
+    assert L.nm_mask_forward_monitor(sh, sm, FAKE, FAKE, FAKE, ODD, ODD, FAKE, FAKE, need - 1, None) == NM_EINVAL
     for alpha in (float("nan"), float("inf"), -float("inf")):
         assert L.nm_prior_init(sh, alpha, FAKE, FAKE, None, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(FAKE, FAKE, -1, None) == NM_EINVAL
@@ -127,6 +145,7 @@ def test_empty_matrices_are_valid_and_launch_nothing(rows, cols):
     assert L.nm_debug_soft_mask(sh, sm, None, None, None) == NM_OK
     assert L.nm_debug_gumbel_log2(None, None, 0, None) == NM_OK
     assert L.nm_prior_init(sh, 3.0, None, None, None, None) == NM_OK
+    assert L.nm_mask_forward_monitor(sh, sm, None, None, None, None, None, None, None, 0, None) == NM_OK
     assert L.nm_packed_value_elems(sh) == 0
 
 
@@ -139,6 +158,16 @@ def test_candidate_table_and_sizes_agree_with_the_oracle(n, m):
         sh = S._Shape(5, cols, n, m, 1)
         assert S.lib().nm_packed_value_elems(ctypes.byref(sh)) == 5 * cols // m * n
         assert S.lib().nm_packed_index_words(ctypes.byref(sh)) == 5 * oracle.index_words_per_row(cols, n, m)
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+def test_monitor_workspace_is_one_float_pair_per_block(n, m):
+    K = oracle.num_candidates(n, m)
+    P = 1 if (K % 4 == 0 or K == 70) else (2 if K % 2 == 0 else 4)
+    for rows, cols in [(1, m), (37, 23 * m), (4096, 4096)]:
+        groups = rows * cols // m
+        blocks = -(-(-(-groups // P)) // 256)
+        assert S.monitor_workspace_bytes(rows, cols, n, m) == 8 * blocks
 
 
 def test_unsupported_helpers():

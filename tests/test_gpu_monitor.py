@@ -1,0 +1,126 @@
+"""GPU parity of the forward with the fused convergence monitors (MaskLLM project page, Fig. 5
+caption) against the oracle: the masked weights equal the plain forward's bit for bit; sampled
+candidates equal the oracle's except on fp32 near-ties, where the GPU's choice must be one of
+the tied candidates; the L1 sum is exact for the GPU's samples; the max-probability sum is
+within 1e-5 relative.  Every call goes through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nm_synth
+import oracle
+import semi_structured_sparsity_amd as S
+from parity import l1_of, perturbed_scores, sample_bound, sample_check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SUPPORTED = [(n, m) for m in (4, 8) for n in range(1, m)]
+SHAPES = [(1, 1), (3, 5), (37, 23), (64, 64), (129, 33)]
+TOL_MAXP = 1e-5
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_step(L, n, m, kappa, tau, seed, offset, got_sample, stats, prev=None):
+    """Compare one monitored step with the oracle; returns the number of near-tie differences."""
+    maxp, ref_sample, _ = oracle.monitor(L, n, m, kappa, tau, seed, offset)
+    words = oracle.noise_words(seed, offset, 0, L.numel())
+    z = perturbed_scores(L, kappa, tau, words, oracle.gumbel)
+    got = got_sample.cpu().numpy()
+    ndiff = sample_check(got, ref_sample, z, sample_bound(L, kappa, tau))
+    st = stats.cpu().numpy()
+    ref_p = float(maxp.sum())
+    assert abs(st[0] - ref_p) <= TOL_MAXP * ref_p, (st[0], ref_p)
+    if prev is None:
+        assert st[1] == 0.0
+    else:
+        assert st[1] == l1_of(got, prev, oracle.candidate_bits(n, m))
+        if ndiff == 0:
+            _, _, l1 = oracle.monitor(L, n, m, kappa, tau, seed, offset, prev_sample=prev)
+            assert st[1] == float(l1.sum(dtype=np.int64))
+    return ndiff
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("rows,gpr", SHAPES)
+def test_monitored_forward_matches_oracle(n, m, rows, gpr):
+    kappa, tau, seed = 30.0, 0.5, 41
+    _say("monitor", n, m, rows, gpr)
+    w, L, _ = nm_synth.matrix_inputs(rows, gpr * m, n, m, torch.bfloat16, 0.5, 31)
+    wd, Ld = w.to(DEV), L.to(DEV)
+    prev = None
+    for offset in (5, 6, 7):
+        prev_d = None if prev is None else torch.from_numpy(prev).to(DEV)
+        out, sample, stats = S.nm_mask_forward_monitor(wd, Ld, n, m, kappa, tau, seed, offset, prev_sample=prev_d)
+        plain = S.nm_mask_forward(wd, Ld, n, m, kappa, tau, seed, offset)
+        assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+        _check_step(L, n, m, kappa, tau, seed, offset, sample, stats, prev)
+        prev = sample.cpu().numpy()
+
+
+@pytest.mark.parametrize("kappa,tau", [(100.0, 4.0), (1.0, 1.0), (0.0, 2.0), (5.0, 0.1), (1e4, 1.0)])
+def test_monitor_over_sample_parameters(kappa, tau):
+    n, m, rows, gpr = 2, 4, 96, 77
+    w, L, _ = nm_synth.matrix_inputs(rows, gpr * m, n, m, torch.float32, 0.5, 32)
+    wd, Ld = w.to(DEV), L.to(DEV)
+    rng = np.random.default_rng(1)
+    prev = rng.integers(0, 6, size=(rows, gpr)).astype(np.uint8)
+    prev[0, :3] = [6, 200, 255]                       # out of range: the empty mask
+    out, sample, stats = S.nm_mask_forward_monitor(wd, Ld, n, m, kappa, tau, 3, 9,
+                                                   prev_sample=torch.from_numpy(prev).to(DEV))
+    _check_step(L, n, m, kappa, tau, 3, 9, sample, stats, prev)
+    if kappa == 0.0:
+        assert stats.cpu()[0].item() == pytest.approx(rows * gpr / 6, rel=1e-6)
+
+
+def test_single_group_max_probability():
+    """One group per call: stats[0] is that group's largest probability."""
+    for n, m in [(2, 4), (4, 8), (1, 8)]:
+        K = S.num_candidates(n, m)
+        for seed in range(6):
+            L = nm_synth.gaussian_logits(1, m, n, m, 100 + seed, std=1.5)
+            w = torch.ones((1, m), dtype=torch.float32)
+            kappa = [0.0, 0.5, 2.0, 7.0, 30.0, 300.0][seed]
+            _, sample, stats = S.nm_mask_forward_monitor(w.to(DEV), L.to(DEV), n, m, kappa, 1.0, seed, 0)
+            maxp, ref_s, _ = oracle.monitor(L, n, m, kappa, 1.0, seed, 0)
+            assert abs(stats.cpu()[0].item() - maxp[0, 0]) <= TOL_MAXP * maxp[0, 0]
+            if kappa == 0.0:
+                assert stats.cpu()[0].item() == pytest.approx(1.0 / K, rel=1e-6)
+
+
+def test_monitor_is_deterministic_and_outputs_are_optional():
+    n, m = 2, 8
+    w, L, _ = nm_synth.matrix_inputs(300, 512, n, m, torch.bfloat16, 0.5, 33)
+    wd, Ld = w.to(DEV), L.to(DEV)
+    prev = torch.zeros((300, 64), dtype=torch.uint8, device=DEV)
+    a = S.nm_mask_forward_monitor(wd, Ld, n, m, 4.0, 1.0, 1, 2, prev_sample=prev)
+    b = S.nm_mask_forward_monitor(wd, Ld, n, m, 4.0, 1.0, 1, 2, prev_sample=prev)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    # without the sample output the stats are the same
+    ws = torch.empty(S.monitor_workspace_bytes(300, 512, n, m), dtype=torch.uint8, device=DEV)
+    out = (torch.empty_like(wd), None, torch.zeros(2, dtype=torch.float64, device=DEV))
+    c = S.nm_mask_forward_monitor(wd, Ld, n, m, 4.0, 1.0, 1, 2, prev_sample=prev, out=out, workspace=ws)
+    assert torch.equal(c[2], a[2]) and torch.equal(c[0].view(torch.int16), a[0].view(torch.int16))
+
+
+def test_monitor_full_llama7b_down_projection():
+    """11008x4096 bf16 of the LLaMA-2-7B-shaped layer, prior logits, kappa 100, tau 4: two
+    consecutive steps against the oracle over the whole matrix."""
+    n, m, kappa, tau = 2, 4, 100.0, 4.0
+    name, rows, cols = nm_synth.LLAMA2_7B_LAYER[-1]
+    seed = nm_synth.input_seed(2, 0, len(nm_synth.LLAMA2_7B_LAYER) - 1)
+    _say("monitor full", name, rows, cols)
+    w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior", device=DEV)
+    Lc = L.cpu()
+    _, s0, st0 = S.nm_mask_forward_monitor(w, L, n, m, kappa, tau, seed, 0)
+    nd0 = _check_step(Lc, n, m, kappa, tau, seed, 0, s0, st0)
+    prev = s0.cpu().numpy()
+    _, s1, st1 = S.nm_mask_forward_monitor(w, L, n, m, kappa, tau, seed, 1, prev_sample=s0)
+    nd1 = _check_step(Lc, n, m, kappa, tau, seed, 1, s1, st1, prev)
+    _say("  near-tie differences", nd0, nd1, "of", rows * cols // m)
+    assert nd0 + nd1 <= 1e-4 * rows * cols // m
