@@ -200,6 +200,23 @@ def test_harden_pack_unpack_are_bit_exact(n, m, wtype, rows, gpr):
     assert torch.equal(_bits_t(v2), _bits_t(values)) and torch.equal(i2, indices)
 
 
+@pytest.mark.parametrize("n,m,gpr", [(3, 8, 3), (2, 4, 5), (2, 4, 16)])
+def test_pack_unpack_beyond_the_grid_row_limit(n, m, gpr):
+    """More rows than the tile grid's y dimension holds (65535): the tile kernels loop over
+    rows; (2, 4, 16) takes the byte path with a flat grid over the same rows."""
+    rows = 70001
+    _say("pack rows", n, m, rows, gpr)
+    w, L, _ = nm_synth.matrix_inputs(rows, gpr * m, n, m, torch.bfloat16, 0.5, 9)
+    wd, Ld = w.to(DEV), L.to(DEV)
+    values, indices, hard = S.nm_mask_harden_pack(wd, Ld, n, m, with_hard=True)
+    rv, ri, rh = oracle.pack(w, L, n, m)
+    np.testing.assert_array_equal(hard.cpu().numpy(), rh)
+    np.testing.assert_array_equal(indices.cpu().numpy().view(np.uint32), ri)
+    np.testing.assert_array_equal(_bits(values), oracle._np(rv).view(np.int16))
+    dense = S.nm_unpack(values, indices, gpr * m, n, m)
+    np.testing.assert_array_equal(_bits(dense), oracle.unpack(rv, ri, gpr * m, n, m).view(np.int16))
+
+
 def _bits_t(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
