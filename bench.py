@@ -131,10 +131,34 @@ def cpu_baseline(min_seconds=10.0, max_passes=8):
             elapsed += time.perf_counter() - t0
             total_w += w.numel()
         passes += 1
+    # the same four passes on one thread over the first matrix (q, 4096x4096)
+    seed, cols, w, L, G = mats[0]
+    t0 = time.perf_counter()
+    oracle.forward(w, L, N, M, KAPPA, TAU, seed, 0, nthreads=1)
+    oracle.backward(w, L, G, N, M, KAPPA, TAU, seed, 0, nthreads=1)
+    v, idx, _ = oracle.pack(w, L, N, M, nthreads=1)
+    oracle.unpack(v, idx, cols, N, M, nthreads=1)
+    t1 = time.perf_counter() - t0
     return {"value": total_w / elapsed, "unit": "weights/s", "cores": oracle.threads_used(threads),
             "kind": "oracle",
             "sample": f"{passes} step(s) of the whole layer ({total_w} weight-passes): "
-                      f"fwd+bwd+harden_pack+unpack in binary64 on {threads} threads, {elapsed:.1f} s"}
+                      f"fwd+bwd+harden_pack+unpack in binary64 on {threads} threads, {elapsed:.1f} s",
+            "single_thread": {"value": w.numel() / t1, "unit": "weights/s",
+                              "sample": f"fwd+bwd+harden_pack+unpack of the 4096x4096 q matrix on 1 thread, "
+                                        f"{t1:.1f} s"}}
+
+
+def copy_ceiling(dev, reps=10):
+    """GB/s (read + write) of the library's plain flat copy over 1 GiB: the streaming ceiling
+    of this GPU, measured in the same run."""
+    import torch
+
+    import semi_structured_sparsity_amd as S
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t = _elapsed_ms(lambda r: S.nm_debug_copy(src, dst), reps=reps)
+    del src, dst
+    return 2 * (1 << 30) / (t * 1e-3) / 1e9
 
 
 # ---------------------------------------------------------------------------------------------
@@ -522,6 +546,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy_gbps = copy_ceiling(dev)
     mats = make_layer(dev)
     torch.cuda.synchronize()
     weights = nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
@@ -560,7 +585,8 @@ def main():
         passes[p] = {"avg_launch_us": round(avg_us, 2), "launches_per_step": len(mats),
                      "bytes_per_weight": bpw[p],
                      "GBps": round(alg_bytes / (avg_us * 1e-6) / 1e9, 1),
-                     "pct_hbm_peak": round(100 * alg_bytes / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
+                     "pct_hbm_peak": round(100 * alg_bytes / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+                     "pct_of_copy": round(100 * alg_bytes / (avg_us * 1e-6) / 1e9 / copy_gbps, 1)}
     fb_us = (passes["fwd"]["avg_launch_us"] + passes["bwd"]["avg_launch_us"]) * len(mats)
     fwd_bwd = {"weights_per_s": weights / (fb_us * 1e-6),
                "GBps": round((bpw["fwd"] + bpw["bwd"]) * weights / (fb_us * 1e-6) / 1e9, 1)}
@@ -592,6 +618,8 @@ def main():
                    "global_batch": 1, "parallelism": "single GPU"},
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+        "copy_ceiling": {"GBps": round(copy_gbps, 1), "kernel": "k_debug_copy",
+                         "what": "flat 16-byte-per-thread copy of 1 GiB, read + write bytes"},
         "fwd_bwd": fwd_bwd,
         "passes": passes,
         "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 1),

@@ -65,6 +65,7 @@ _SIGNATURES = {
     "nm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "nm_debug_noise": (ctypes.c_int, [_P, _P, _P, _P]),
     "nm_debug_gumbel_log2": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "nm_debug_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
     "nm_debug_soft_mask": (ctypes.c_int, [_P, _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGNATURES)
@@ -306,6 +307,16 @@ def nm_debug_gumbel_log2(words):
     return out
 
 
+def nm_debug_copy(src, dst):
+    """dst <- src with the path kernels' access pattern (both contiguous, same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    st = lib().nm_debug_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(src.device))
+    _check(st, "nm_debug_copy")
+    return dst
+
+
 def nm_debug_soft_mask(logits, n, m, kappa, tau, seed, offset):
     """fp32 soft mask [rows, cols] of a sample."""
     rows, gpr, K = logits.shape
@@ -350,6 +361,7 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
 
 
 __all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
-           "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise",
+           "nm_debug_copy", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
            "NMError", "EXPORTS", "library_path"]

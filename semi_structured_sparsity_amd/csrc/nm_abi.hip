@@ -254,6 +254,14 @@ nm_status nm_debug_noise(const nm_shape* shape, const nm_sample* sample, uint32_
     return launched(nm::launch_debug_noise(a, (hipStream_t)stream));
 }
 
+nm_status nm_debug_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0 || bytes / 16 > kMaxThreads) return NM_EINVAL;
+    if (bytes == 0) return NM_OK;
+    if (!src || !dst) return NM_EINVAL;
+    if (!aligned16(src) || !aligned16(dst)) return NM_EALIGN;
+    return launched(nm::launch_debug_copy(src, dst, bytes / 16, (hipStream_t)stream));
+}
+
 nm_status nm_debug_gumbel_log2(const uint32_t* words, float* h, int64_t count, void* stream) {
     if (count < 0 || count > kMaxThreads) return NM_EINVAL;
     if (count == 0) return NM_OK;

@@ -988,6 +988,14 @@ __global__ __launch_bounds__(kThreads) void k_debug_noise(NoiseArgs a) {
         if (b * 4 + q < a.slots) a.words[b * 4 + q] = blk.v[q];
 }
 
+// A plain flat copy with the path kernels' access pattern (one 16-byte vector per thread, one
+// tile per thread, non-temporal store): the streaming ceiling the path is compared with.
+__global__ __launch_bounds__(kThreads) void k_debug_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        int64_t vecs) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < vecs) nt_store(dst + i, src[i]);
+}
+
 __global__ __launch_bounds__(kThreads) void k_debug_gumbel(GumbelArgs a) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= a.count) return;
@@ -1112,6 +1120,10 @@ hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t
 }
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s) {
     k_debug_noise<<<grid_for((a.slots + 3) / 4), kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+hipError_t launch_debug_copy(const void* src, void* dst, int64_t vecs, hipStream_t s) {
+    k_debug_copy<<<grid_for(vecs), kThreads, 0, s>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), vecs);
     return hipGetLastError();
 }
 hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s) {

@@ -88,6 +88,7 @@ hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a,
 int64_t monitor_parts(int n, int m, int64_t groups);
 hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s);
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
+hipError_t launch_debug_copy(const void* src, void* dst, int64_t vecs, hipStream_t s);
 hipError_t launch_debug_gumbel(const GumbelArgs& a, hipStream_t s);
 int groups_per_thread(int n, int m);
 

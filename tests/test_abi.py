@@ -24,7 +24,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = S.lib()
     declared = _declared()
-    assert len(declared) >= 16
+    assert len(declared) >= 17
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(S.EXPORTS)
@@ -127,6 +127,11 @@ def test_null_and_misaligned_pointers_are_rejected_on_the_host():
     assert L.nm_mask_forward_monitor(sh, sm, FAKE, FAKE, FAKE, ODD, ODD, FAKE, FAKE, need - 1, None) == NM_EINVAL
     for alpha in (float("nan"), float("inf"), -float("inf")):
         assert L.nm_prior_init(sh, alpha, FAKE, FAKE, None, None) == NM_EINVAL
+    assert L.nm_debug_copy(FAKE, FAKE, -16, None) == NM_EINVAL
+    assert L.nm_debug_copy(FAKE, FAKE, 24, None) == NM_EINVAL      # not a multiple of 16
+    assert L.nm_debug_copy(None, FAKE, 32, None) == NM_EINVAL
+    assert L.nm_debug_copy(FAKE, ODD, 32, None) == NM_EALIGN
+    assert L.nm_debug_copy(None, None, 0, None) == NM_OK
     assert L.nm_debug_gumbel_log2(FAKE, FAKE, -1, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(None, FAKE, 5, None) == NM_EINVAL
     assert L.nm_debug_gumbel_log2(ODD, FAKE, 5, None) == NM_EALIGN

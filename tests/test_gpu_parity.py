@@ -293,6 +293,13 @@ def test_empty_matrices():
         assert S.nm_prior_init(w, n, m, 3.0).shape == (0, 8, K)
 
 
+def test_debug_copy_copies():
+    src = torch.arange(3 * 4096 + 4, dtype=torch.int32, device=DEV)   # 16 bytes beyond whole blocks
+    dst = torch.zeros_like(src)
+    S.nm_debug_copy(src, dst)
+    assert torch.equal(src, dst)
+
+
 def test_misaligned_views_are_refused():
     n, m = 2, 4
     base = torch.zeros(4 * 64 + 2, dtype=torch.bfloat16, device=DEV)
