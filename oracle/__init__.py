@@ -54,6 +54,7 @@ def lib():
             "ref_threads_used": (i32, [i32]),
             "ref_prior_init": (i32, [P, i64, i64, P, ctypes.c_float, P, P, i32]),
             "ref_monitor": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, P, P, P, i32]),
+            "ref_sparse_matmul": (i32, [P, i64, i64, P, P, P, i32, i64, P, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -318,3 +319,23 @@ def monitor(logits, n, m, kappa, tau, seed, offset, prev_sample=None, rows=None,
                            _ptr(maxp), _ptr(samp), None if l1 is None else _ptr(l1), nthreads)
     _check(rc, "monitor")
     return maxp, samp, l1
+
+
+def sparse_matmul(values, indices, x, n, m, rows=None, row_begin=0, nthreads=0):
+    """float64 Y [tokens, window_rows] = X times the transpose of the unpacked weights, from the
+    packed form (values [window_rows, cols*n/m], indices [window_rows, words]) of W rows
+    row_begin .. row_begin + window_rows - 1.  x: [tokens, cols] float32 or bf16."""
+    V = _contig(values)
+    I = _contig(indices, np.uint32)
+    X = _contig(x)
+    wr = V.shape[0]
+    rows = wr if rows is None else rows
+    tokens, cols = X.shape
+    if V.shape[1] != cols // m * n:
+        raise ValueError("values do not match x's columns")
+    y = _unwritten((tokens, wr), np.float64)
+    s = _shape(rows, cols, n, m, _wtype_of(V))
+    rc = lib().ref_sparse_matmul(ctypes.byref(s), row_begin, _window(wr, row_begin, rows), _ptr(V), _ptr(I),
+                                 _ptr(X), _wtype_of(X), tokens, _ptr(y), nthreads)
+    _check(rc, "sparse_matmul")
+    return y

@@ -212,6 +212,9 @@ struct job {
     void *out;
     void *out2;
     uint8_t *hard;
+    int64_t tokens;  /* sparse product: rows of X */
+    int64_t ystride; /* sparse product: row stride of Y (the window's W rows) */
+    int32_t xtype;   /* sparse product: element type of X */
     row_fn fn;
 };
 
@@ -693,6 +696,58 @@ int32_t ref_monitor(const ref_shape *shape, double kappa, double tau, uint64_t s
     jb.out2 = l1;
     jb.hard = sample;
     jb.fn = row_monitor;
+    run_rows(&jb, row_begin, row_end, nthreads);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Deployment product with the compressed weights ("Accelerating Sparse Deep Neural Networks"
+ * summary page, sections 3.1-3.2: the sparse operand is used in its compressed form, kept
+ * values plus their positions, against a dense operand).  For a linear layer with weights
+ * W [out, in] (groups of m along in, packed as above) and activations X [tokens, in]:
+ *     Y[t, o] = sum over groups q and kept values u of values[o, q*n + u] * X[t, q*m + p_u]
+ * with p_u the position field of (o, q, u): X times the transpose of the unpacked W.  Binary64
+ * products and sums, groups and kept values in ascending order.  Work is split over W rows;
+ * y is [tokens, window rows] (column o - row_begin holds W row o). */
+static void row_sparse_matmul(const job *jb, int64_t o) {
+    const ref_shape *s = jb->s;
+    int64_t gpr = s->cols / s->m;
+    int64_t wpr = ref_index_words_per_row(s);
+    int32_t nb = index_bits(s->m);
+    int64_t lo = o - jb->rb;
+    const uint32_t *idx = (const uint32_t *)jb->grad + lo * wpr;
+    for (int64_t t = 0; t < jb->tokens; ++t) {
+        double acc = 0.0;
+        for (int64_t q = 0; q < gpr; ++q) {
+            for (int32_t u = 0; u < s->n; ++u) {
+                uint32_t p = get_bits(idx, (q * s->n + u) * nb, nb);
+                if ((int32_t)p >= s->m) continue; /* malformed metadata: nothing kept there */
+                double v = load_w(jb->w, s->wtype, lo * (gpr * s->n) + q * s->n + u);
+                acc += v * load_w(jb->out2, jb->xtype, t * s->cols + q * s->m + p);
+            }
+        }
+        ((double *)jb->out)[t * jb->ystride + lo] = acc;
+    }
+}
+
+int32_t ref_sparse_matmul(const ref_shape *shape, int64_t row_begin, int64_t row_end,
+                          const void *values, const uint32_t *indices, const void *x,
+                          int32_t xtype, int64_t tokens, double *y, int32_t nthreads) {
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    if (!window_ok(shape, row_begin, row_end) || !init_ctx(&jb.ctx, shape, 1.0, 1.0, 0, 0)) return -1;
+    if (tokens < 0 || (xtype != REF_F32 && xtype != REF_BF16)) return -1;
+    if (row_end > row_begin && tokens > 0 && (!values || !indices || !x || !y)) return -1;
+    jb.s = shape;
+    jb.rb = row_begin;
+    jb.w = values;
+    jb.grad = indices;
+    jb.out2 = (void *)x; /* read only */
+    jb.out = y;
+    jb.tokens = tokens;
+    jb.ystride = row_end - row_begin;
+    jb.xtype = xtype;
+    jb.fn = row_sparse_matmul;
     run_rows(&jb, row_begin, row_end, nthreads);
     return 0;
 }

@@ -132,6 +132,14 @@ int32_t ref_monitor(const ref_shape *shape, double kappa, double tau, uint64_t s
                     int64_t row_begin, int64_t row_end, const float *logits, const uint8_t *prev_sample,
                     double *max_prob, uint8_t *sample, uint8_t *l1, int32_t nthreads);
 
+/* --- product with the compressed weights ------------------------------------------------ */
+/* y [tokens, row_end - row_begin] binary64 (overwritten): y[t, o - row_begin] = sum over the
+ * kept values of W row o (values, indices in the packed layout, rows of the window) times the
+ * matching elements of X row t.  x [tokens, cols] of type xtype (REF_F32 or REF_BF16 bits). */
+int32_t ref_sparse_matmul(const ref_shape *shape, int64_t row_begin, int64_t row_end,
+                          const void *values, const uint32_t *indices, const void *x,
+                          int32_t xtype, int64_t tokens, double *y, int32_t nthreads);
+
 /* number of worker threads a call with this nthreads argument uses */
 int32_t ref_threads_used(int32_t nthreads);
 

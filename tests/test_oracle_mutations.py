@@ -17,7 +17,7 @@ from oracle import build as oracle_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_noise.py", "tests/test_oracle_layer.py", "tests/test_oracle_pack.py",
-        "tests/test_oracle_monitor.py"]
+        "tests/test_oracle_monitor.py", "tests/test_oracle_matmul.py"]
 
 MUTANTS = {
     "philox_swaps_hi_and_lo": ("uint32_t n0 = hi1 ^ x1 ^ k0;", "uint32_t n0 = lo1 ^ x1 ^ k0;"),
@@ -60,6 +60,11 @@ MUTANTS = {
                                     "(int32_t)((a >> j & 1u) == (b >> j & 1u));"),
     "monitor_prev_out_of_range_wraps": ("(prev >= 0 && prev < c->K) ? c->cand[prev] : 0u",
                                         "c->cand[prev % c->K]"),
+    "matmul_position_ignored": ("load_w(jb->out2, jb->xtype, t * s->cols + q * s->m + p)",
+                                "load_w(jb->out2, jb->xtype, t * s->cols + q * s->m + u)"),
+    "matmul_skips_last_kept": ("for (int32_t u = 0; u < s->n; ++u) {\n                uint32_t p",
+                               "for (int32_t u = 0; u + 1 < s->n; ++u) {\n                uint32_t p"),
+    "matmul_subtracts": ("acc += v * load_w(", "acc -= v * load_w("),
     "candidates_skip_last": ("for (int32_t p = start; p <= m - (n - depth); ++p)",
                              "for (int32_t p = start; p < m - (n - depth); ++p)"),
 }
