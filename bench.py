@@ -43,12 +43,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama7b_layer",
                    choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256",
-                            "prior_init", "monitor"],
+                            "prior_init", "monitor", "spmm"],
                    help="llama7b_layer (default): one LLaMA-2-7B-shaped layer per step; sweep32: 32 such "
                         "layers x 10 annealed steps of fwd+bwd+pack; general_nm: 4096x11008 with 1:4, 2:8, "
                         "4:8; nemotron_pack: pack+unpack of every Nemotron-15B-shaped matrix; single256: "
                         "one 256x256 fp32 weight (latency-bound); prior_init: magnitude-prior "
-                        "logit initialisation; monitor: forward with the fused Fig. 5 monitors")
+                        "logit initialisation; monitor: forward with the fused Fig. 5 monitors; spmm: "
+                        "sparse x dense product on the packed weights")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -469,6 +470,57 @@ def workload_monitor(args):
             "results": res, "monitor_means_last_call": [[round(a, 6), round(b, 6)] for a, b in means]}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity factor)
+
+
+def workload_spmm(args):
+    """Product of bf16 activations (4096 tokens) with each 2:4-packed matrix of one
+    LLaMA-7B-shaped layer on the sparse matrix cores, next to torch's dense bf16 product with the
+    unpacked weights (the library GEMM) for context.  Useful flops are the kept products:
+    2 * tokens * out * in / 2; the dense-equivalent rate counts 2 * tokens * out * in."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    tokens = 4096
+    mats = []
+    for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
+        seed = nm_synth.input_seed(2, 0, i)
+        w, L, _ = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed, logits="prior", device=dev)
+        values, indices = S.nm_mask_harden_pack(w, L, N, M)
+        dense_t = S.nm_unpack(values, indices, cols, N, M).t().contiguous()  # [in, out], contiguous
+        x = nm_synth.normal((tokens, cols), 1.0, seed + 7, torch.bfloat16, device=dev)
+        y = torch.empty((tokens, rows), dtype=torch.bfloat16, device=dev)
+        mats.append(dict(name=name, rows=rows, cols=cols, values=values, indices=indices, dense_t=dense_t, x=x, y=y))
+        del w, L
+    useful = sum(2.0 * tokens * mt["rows"] * mt["cols"] / 2 for mt in mats)
+
+    def sparse(r):
+        for mt in mats:
+            S.nm_sparse_matmul(mt["values"], mt["indices"], mt["x"], out=mt["y"])
+
+    def dense(r):
+        for mt in mats:
+            torch.mm(mt["x"], mt["dense_t"], out=mt["y"])
+
+    res = {}
+    for label, fn in (("sparse_smfmac", sparse), ("dense_torch", dense)):
+        t = _elapsed_ms(fn, reps=args.kernel_reps)
+        res[label] = {"ms_per_layer": round(t, 4), "avg_call_us": round(t * 1e3 / len(mats), 2),
+                      "useful_TFLOPs": round(useful / (t * 1e-3) / 1e12, 1),
+                      "dense_equivalent_TFLOPs": round(2 * useful / (t * 1e-3) / 1e12, 1),
+                      "pct_dense_bf16_peak_useful": round(100 * useful / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1)}
+    res["speedup_vs_dense"] = round(res["dense_torch"]["ms_per_layer"] / res["sparse_smfmac"]["ms_per_layer"], 3)
+    return {"metric": "2:4 sparse x dense product on the packed weights vs dense bf16 GEMM", "unit": "TFLOP/s",
+            "config": {"workload": "LLaMA-2-7B-shaped layer (7 matrices) packed 2:4, X 4096 tokens bf16, "
+                                   "Y bf16, fp32 accumulation"},
+            "roofline": {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "achieved": res["sparse_smfmac"]["useful_TFLOPs"],
+                         "frac": round(res["sparse_smfmac"]["useful_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "results": res}
+
+
 def workload_prior_init(args):
     """Magnitude-prior logit initialisation of every matrix of one LLaMA-7B-shaped layer (2:4,
     alpha 3) and of a 4096x11008 matrix for 2:8 and 4:8: read w, write the K logits of each group
@@ -516,7 +568,8 @@ def main():
         torch.cuda.set_device(0)
         fn = {"sweep32": workload_sweep32, "general_nm": workload_general_nm,
               "nemotron_pack": workload_nemotron_pack, "single256": workload_single256,
-              "prior_init": workload_prior_init, "monitor": workload_monitor}[args.workload]
+              "prior_init": workload_prior_init, "monitor": workload_monitor,
+              "spmm": workload_spmm}[args.workload]
         out = fn(args)
         out.update({"n_gpus": 1, "data": "synthetic, seeded, generated on the GPU", "dtype": "f32"})
         print(json.dumps(out), flush=True)

@@ -166,6 +166,21 @@ nm_status nm_unpack(const nm_shape *shape, const void *values, const uint32_t *i
 nm_status nm_prior_init(const nm_shape *shape, float alpha, const void *w, float *logits,
                         uint8_t *prior_idx, void *stream);
 
+/* Product with the packed weights on gfx950's sparse matrix cores, the deployment step after
+ * the path ("Accelerating Sparse Deep Neural Networks" summary page, sections 3.1-3.2: the
+ * compressed operand, values plus 2-bit positions, is multiplied as is and the pruned products
+ * are skipped).  For a linear layer W [out, in] pruned 2:4 along `in` and packed by
+ * nm_mask_harden_pack:  Y[t, o] = sum_i X[t, i] * W[o, i], accumulated in fp32.
+ *   w_shape   rows = out, cols = in, n = 2, m = 4, wtype = NM_BF16 (else NM_EUNSUPPORTED)
+ *   values    [out, in/2] bf16, indices [out, in/32] uint32: the packed form, read
+ *   x         [tokens, in] bf16, read
+ *   y         [tokens, out], ytype NM_F32 or NM_BF16 (round to nearest even), overwritten
+ * Supported sizes: in a positive multiple of 64, out and tokens multiples of 256 (else
+ * NM_EUNSUPPORTED); out = 0 or tokens = 0 launches nothing.  Pointers 16-byte aligned.
+ * Deterministic: every output is accumulated in a fixed order. */
+nm_status nm_sparse_matmul(const nm_shape *w_shape, const void *values, const uint32_t *indices,
+                           const void *x, int64_t tokens, void *y, int32_t ytype, void *stream);
+
 /* ---- host-only helpers (no device work, no HIP call) ---------------------------------- */
 /* K = C(m, n) for a supported (n, m), else -1. */
 int32_t nm_num_candidates(int32_t n, int32_t m);

@@ -57,6 +57,7 @@ _SIGNATURES = {
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
     "nm_mask_forward_monitor": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
     "nm_monitor_workspace_bytes": (ctypes.c_int64, [_P]),
+    "nm_sparse_matmul": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, _P]),
     "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nm_candidate_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P]),
     "nm_packed_value_elems": (ctypes.c_int64, [_P]),
@@ -284,6 +285,25 @@ def nm_prior_init(w, n, m, alpha, with_idx=False, out=None):
     return (logits, idx) if with_idx else logits
 
 
+def nm_sparse_matmul(values, indices, x, out_dtype=torch.bfloat16, out=None):
+    """Y [tokens, out] = X [tokens, in] times the transpose of the 2:4 weights W [out, in] held in
+    nm_mask_harden_pack's packed form (values [out, in/2] bf16, indices [out, in/32]), on the
+    sparse matrix cores ("Accelerating Sparse Deep Neural Networks" summary page, 3.1-3.2)."""
+    rows, half = values.shape
+    tokens, cols = x.shape
+    if cols != 2 * half:
+        raise ValueError(f"x has {cols} columns, the packed weights {2 * half}")
+    sh = _shape(rows, cols, 2, 4, _wtype(values.dtype))
+    ytype = _wtype(out_dtype)
+    y = torch.empty((tokens, rows), dtype=out_dtype, device=x.device) if out is None else out
+    st = lib().nm_sparse_matmul(ctypes.byref(sh), _dev(values, "values"),
+                                _dev(indices, "indices", torch.int32, (rows, cols // 32)),
+                                _dev(x, "x", torch.bfloat16), tokens,
+                                _dev(y, "y", out_dtype, (tokens, rows)), ytype, _stream(x.device))
+    _check(st, "nm_sparse_matmul")
+    return y
+
+
 # ---------------------------------------------------------------------------------------------
 # diagnostics (same device functions as the kernels)
 
@@ -362,6 +382,6 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
 
 __all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
            "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise",
-           "nm_debug_copy", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "nm_debug_copy", "nm_sparse_matmul", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
            "NMError", "EXPORTS", "library_path"]

@@ -10,7 +10,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "nm_kernels.hip"), os.path.join(CSRC, "nm_abi.hip")]
+SOURCES = [os.path.join(CSRC, "nm_kernels.hip"), os.path.join(CSRC, "nm_spmm.hip"),
+           os.path.join(CSRC, "nm_abi.hip")]
 HEADERS = [os.path.join(CSRC, "nm_device.hpp"), os.path.join(CSRC, "nm_kernels.hpp"),
            os.path.join(ROOT, "include", "nm_mask.h")]
 LIB = os.path.join(PKG, "libnm_mask.so")

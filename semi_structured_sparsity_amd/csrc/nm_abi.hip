@@ -241,6 +241,26 @@ nm_status nm_prior_init(const nm_shape* shape, float alpha, const void* w, float
     return launched(nm::launch_prior(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
+nm_status nm_sparse_matmul(const nm_shape* w_shape, const void* values, const uint32_t* indices,
+                           const void* x, int64_t tokens, void* y, int32_t ytype, void* stream) {
+    int64_t groups;
+    int32_t K;
+    nm_status st = check_shape(w_shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if (tokens < 0 || (ytype != NM_F32 && ytype != NM_BF16)) return NM_EINVAL;
+    if (w_shape->n != 2 || w_shape->m != 4 || w_shape->wtype != NM_BF16) return NM_EUNSUPPORTED;
+    const int64_t out = w_shape->rows, in = w_shape->cols;
+    if (out == 0 || tokens == 0) return NM_OK;
+    if (in == 0 || in % 64 != 0 || out % 256 != 0 || tokens % 256 != 0) return NM_EUNSUPPORTED;
+    if ((out / 256) * (tokens / 256) > (int64_t)INT32_MAX - 8) return NM_EINVAL;  // one block per tile
+    if (tokens > INT64_MAX / 4 / (in > out ? in : out)) return NM_EINVAL;
+    if (!values || !indices || !x || !y) return NM_EINVAL;
+    if (!aligned16(values) || !aligned16(indices) || !aligned16(x) || !aligned16(y)) return NM_EALIGN;
+    nm::SpmmArgs a{static_cast<const uint16_t*>(values), indices, static_cast<const uint16_t*>(x), y,
+                   out, in, tokens, in / 2, in / 32, in, out, ytype == NM_F32 ? 0 : 1};
+    return launched(nm::launch_spmm24(a, (hipStream_t)stream));
+}
+
 nm_status nm_debug_noise(const nm_shape* shape, const nm_sample* sample, uint32_t* words, void* stream) {
     int64_t groups;
     int32_t K;

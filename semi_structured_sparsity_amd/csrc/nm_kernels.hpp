@@ -80,6 +80,19 @@ struct GumbelArgs {
     int64_t count;
 };
 
+// Product with packed 2:4 bf16 weights: Y [tokens, out] = X [tokens, in] * W^T, W [out, in].
+struct SpmmArgs {
+    const uint16_t* values;    // [out, in/2] bf16 bits
+    const uint32_t* indices;   // [out, in/32]
+    const uint16_t* x;         // [tokens, in] bf16 bits
+    void* y;                   // [tokens, out] fp32 (ytype 0) or bf16 (ytype 1)
+    int64_t out, in, tokens;
+    int64_t vstride, istride, xstride, ystride;  // row strides in elements
+    int32_t ytype;
+};
+
+hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s);
+
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_mask, hipStream_t s);
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);

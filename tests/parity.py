@@ -117,3 +117,16 @@ def l1_of(sample, prev, cand_bits):
     pb = np.where(p < K, bits[np.minimum(p, K - 1)], 0)
     x = s ^ pb
     return int(sum(((x >> j) & 1).sum() for j in range(8)))
+
+
+# --- product with the packed weights --------------------------------------------------------
+
+def spmm_check(gpu, ref, absterms, n_terms, bf16_out):
+    """fp32 accumulation of n_terms exact products (bf16 x bf16) in any order errs by at most
+    n_terms * 2^-24 * sum |x w| (the standard bound); a bf16 output adds its rounding, one unit
+    in the last place of 8 bits (2^-8 |y|, covering results that round either side of a tie)."""
+    gpu = np.asarray(gpu, np.float64)
+    bound = n_terms * 2.0**-24 * np.asarray(absterms, np.float64)
+    if bf16_out:
+        bound = bound + 2.0**-8 * np.abs(ref)
+    return _verdict(np.abs(gpu - ref), bound + 1e-30)

@@ -24,7 +24,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = S.lib()
     declared = _declared()
-    assert len(declared) >= 17
+    assert len(declared) >= 18
     for name in declared:
         assert hasattr(L, name), name
     assert set(declared) == set(S.EXPORTS)
@@ -173,6 +173,23 @@ def test_monitor_workspace_is_one_float_pair_per_block(n, m):
         groups = rows * cols // m
         blocks = -(-(-(-groups // P)) // 256)
         assert S.monitor_workspace_bytes(rows, cols, n, m) == 8 * blocks
+
+
+def test_sparse_matmul_is_validated_on_the_host():
+    L = S.lib()
+    sh = _shape(rows=256, cols=64, n=2, m=4, wtype=1)
+    ok = lambda shp, tokens=256, y=FAKE, ytype=1, v=FAKE: L.nm_sparse_matmul(shp, v, FAKE, FAKE, tokens, y, ytype, None)
+    assert ok(_shape(rows=256, cols=64, n=2, m=4, wtype=0)) == NM_EUNSUPPORTED   # fp32 weights
+    assert ok(_shape(rows=256, cols=64, n=1, m=4, wtype=1)) == NM_EUNSUPPORTED   # 1:4
+    assert ok(_shape(rows=128, cols=64, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED   # out % 256
+    assert ok(_shape(rows=256, cols=96, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED   # in % 64
+    assert ok(sh, tokens=128) == NM_EUNSUPPORTED
+    assert ok(sh, tokens=-1) == NM_EINVAL
+    assert ok(sh, ytype=5) == NM_EINVAL
+    assert ok(sh, y=None) == NM_EINVAL
+    assert ok(sh, v=ODD) == NM_EALIGN
+    assert ok(sh, tokens=0, y=None) == NM_OK
+    assert ok(_shape(rows=0, cols=64, n=2, m=4, wtype=1), y=None) == NM_OK
 
 
 def test_unsupported_helpers():

@@ -1,0 +1,95 @@
+"""GPU parity of the product with the packed 2:4 weights (nm_sparse_matmul, gfx950 sparse
+matrix cores) against the oracle's binary64 product, within the fp32 accumulation bound; the
+weights come from the path's own harden+pack, so the packed form feeds the product unchanged.
+Every call goes through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import nm_synth
+import oracle
+import semi_structured_sparsity_amd as S
+from parity import spmm_check
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _packed_layer(out, inn, seed, w_std=0.02):
+    w, L, _ = nm_synth.matrix_inputs(out, inn, 2, 4, torch.bfloat16, w_std, seed, logits="prior", device=DEV)
+    values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
+    return w, values, indices
+
+
+def _check(values, indices, x, y, rows=None, row_begin=0, bf16_out=False):
+    """Compare y (GPU, [tokens, out]) with the oracle over W rows row_begin .. + window."""
+    vw = values[row_begin:row_begin + rows] if rows else values
+    iw = indices[row_begin:row_begin + rows] if rows else indices
+    v, i, xc = vw.cpu(), iw.cpu().numpy().view(np.uint32), x.cpu()
+    total = values.shape[0]
+    ref = oracle.sparse_matmul(v, i, xc, 2, 4, rows=total, row_begin=row_begin)
+    ab = oracle.sparse_matmul(v.abs(), i, xc.abs(), 2, 4, rows=total, row_begin=row_begin)
+    got = y[:, row_begin:row_begin + ref.shape[1]].double().cpu().numpy()
+    n_terms = x.shape[1] // 2
+    ratio, bad = spmm_check(got, ref, ab, n_terms, bf16_out)
+    return ratio, bad
+
+
+@pytest.mark.parametrize("out,inn,tokens", [(256, 64, 256), (512, 192, 256), (256, 1024, 512), (768, 640, 768)])
+@pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
+def test_sparse_matmul_matches_oracle(out, inn, tokens, ytype):
+    _say("spmm", out, inn, tokens, ytype)
+    _, values, indices = _packed_layer(out, inn, 40 + out + inn, w_std=1.0)
+    x = nm_synth.normal((tokens, inn), 1.0, 41, torch.bfloat16, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=ytype)
+    ratio, bad = _check(values, indices, x, y, bf16_out=ytype == torch.bfloat16)
+    _say("  err/bound", ratio)
+    assert bad == 0
+
+
+@pytest.mark.parametrize("name_index,tokens", [(0, 512), (4, 256), (6, 256)])
+def test_sparse_matmul_llama7b_shapes_sampled_rows(name_index, tokens):
+    """Full LLaMA-7B-shaped weights (q 4096x4096, up 11008x4096, down 4096x11008); the oracle
+    checks three windows of 128 W rows against every token."""
+    name, out, inn = nm_synth.LLAMA2_7B_LAYER[name_index]
+    _say("spmm", name, out, inn, tokens)
+    _, values, indices = _packed_layer(out, inn, nm_synth.input_seed(2, 0, name_index))
+    x = nm_synth.normal((tokens, inn), 1.0, 42, torch.bfloat16, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32)
+    for rb in (0, out // 2 + 64, out - 128):
+        ratio, bad = _check(values, indices, x, y, rows=128, row_begin=rb)
+        _say("  rows", rb, "err/bound", ratio)
+        assert bad == 0
+
+
+def test_sparse_matmul_equals_dense_product_of_the_unpacked_weights():
+    """The path end to end: harden+pack on the GPU, then the sparse product, against torch's
+    dense fp32 product with the unpacked weights (same fp32 bound)."""
+    out, inn, tokens = 512, 1024, 512
+    _, values, indices = _packed_layer(out, inn, 43, w_std=1.0)
+    dense = S.nm_unpack(values, indices, inn, 2, 4)
+    x = nm_synth.normal((tokens, inn), 1.0, 44, torch.bfloat16, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32).double()
+    dt = dense.double().t().contiguous()
+    ref = x.double() @ dt
+    ab = x.double().abs() @ dt.abs()
+    assert bool(((y - ref).abs() <= (inn // 2) * 2.0**-24 * ab + 1e-30).all())
+    # deterministic: the same inputs give the same bits
+    assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32), y.float())
+
+
+def test_sparse_matmul_rejects_unsupported_shapes():
+    _, values, indices = _packed_layer(256, 64, 45)
+    x = torch.zeros((128, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(S.NMError) as e:
+        S.nm_sparse_matmul(values, indices, x)
+    assert e.value.status == S.NM_EUNSUPPORTED
+    x0 = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    assert S.nm_sparse_matmul(values, indices, x0).shape == (0, 256)
