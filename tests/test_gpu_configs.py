@@ -227,3 +227,43 @@ def test_config5_general_nm_4096x11008(n, m):
     _soft_properties(L, n, m, kappa, tau, seed, 0)
     _grad_properties(w, G, dl, n, m, kappa, tau)
     _check_pack_full(w, L, n, m)
+
+
+# ---------------------------------------------------------------------------------------------
+# largest size: element offsets beyond 2^31
+
+def test_forward_backward_pack_beyond_2_31_elements():
+    """A 4096 x 786432 bf16 weight (3.2 G elements, 12.9 G bytes of logits): every 64-bit offset
+    path of the forward, backward, pack and unpack, checked on sampled rows (the last one
+    included) against the oracle."""
+    n, m, kappa, tau = 2, 4, 100.0, 4.0
+    rows, cols = 4096, 786432
+    _say("beyond 2^31", rows, cols)
+    w = nm_synth.normal((rows, cols), 0.02, 91, torch.bfloat16, device=DEV)
+    L = nm_synth.gaussian_logits(rows, cols, n, m, 92, device=DEV)
+    out = S.nm_mask_forward(w, L, n, m, kappa, tau, 5, 1)
+    G = nm_synth.normal((rows, cols), 1.0, 93, torch.bfloat16, device=DEV)
+    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, 5, 1)
+    torch.cuda.synchronize()
+    for r in (0, 2730, rows - 1):
+        wr, Lr, Gr = w[r:r + 1].cpu(), L[r:r + 1].cpu(), G[r:r + 1].cpu()
+        ref = oracle.forward(wr, Lr, n, m, kappa, tau, 5, 1, rows=rows, row_begin=r)
+        soft = oracle.soft_mask(Lr, n, m, kappa, tau, 5, 1, rows=rows, row_begin=r)
+        _, bad = forward_check(out[r:r + 1].double().cpu().numpy(), ref, wr.double().numpy(), soft, m,
+                               TOL_FP32, True)
+        assert bad == 0, f"forward row {r}"
+        refb = oracle.backward(wr, Lr, Gr, n, m, kappa, tau, 5, 1, rows=rows, row_begin=r)
+        y = oracle.probs(Lr, n, m, kappa, tau, 5, 1, rows=rows, row_begin=r)
+        d = candidate_sums(wr.double().numpy(), Gr.double().numpy(), n, m, oracle.candidate_matrix(n, m))
+        _, bad = backward_check(dl[r:r + 1].double().cpu().numpy(), refb, y, d, kappa / tau, TOL_FP32)
+        assert bad == 0, f"backward row {r}"
+    del out, dl, G
+    values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+    dense = S.nm_unpack(values, indices, cols, n, m)
+    for r in (1, 3001, rows - 1):
+        rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)  # rows are independent
+        assert np.array_equal(hard[r:r + 1].cpu().numpy(), rh)
+        assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri)
+        assert np.array_equal(_bits(values[r:r + 1]), oracle._np(rv).view(np.int16))
+        rd = oracle.unpack(rv, ri, cols, n, m)
+        assert np.array_equal(_bits(dense[r:r + 1]), rd.view(np.int16))

@@ -17,7 +17,7 @@ from oracle import build as oracle_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_noise.py", "tests/test_oracle_layer.py", "tests/test_oracle_pack.py",
-        "tests/test_oracle_monitor.py", "tests/test_oracle_matmul.py"]
+        "tests/test_oracle_monitor.py", "tests/test_oracle_matmul.py", "tests/test_oracle_properties.py"]
 
 MUTANTS = {
     "philox_swaps_hi_and_lo": ("uint32_t n0 = hi1 ^ x1 ^ k0;", "uint32_t n0 = lo1 ^ x1 ^ k0;"),
