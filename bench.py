@@ -171,12 +171,13 @@ COPY_BYTES = 1 << 30  # the --copy-calibration copies
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources, so stored counter readings can be matched to the kernels."""
+    """Hash of the sources of the path's kernels (nm_kernels.hip and the device header it
+    includes), so stored counter readings can be matched to the kernels they were taken on."""
     import hashlib
     import semi_structured_sparsity_amd.build as b
     h = hashlib.sha256()
-    for path in sorted(b.SOURCES + b.HEADERS):
-        h.update(open(path, "rb").read())
+    for name in ("nm_kernels.hip", "nm_device.hpp"):
+        h.update(open(os.path.join(b.CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
 

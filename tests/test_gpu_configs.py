@@ -264,6 +264,6 @@ def test_forward_backward_pack_beyond_2_31_elements():
         rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)  # rows are independent
         assert np.array_equal(hard[r:r + 1].cpu().numpy(), rh)
         assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri)
-        assert np.array_equal(_bits(values[r:r + 1]), oracle._np(rv).view(np.int16))
+        assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), oracle._np(rv).view(np.int16))
         rd = oracle.unpack(rv, ri, cols, n, m)
-        assert np.array_equal(_bits(dense[r:r + 1]), rd.view(np.int16))
+        assert np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(), rd.view(np.int16))
