@@ -1,7 +1,9 @@
 /*
  * nm_mask.h -- C ABI of the MI355X (gfx950) library for learnable N:M semi-structured sparsity:
  * the differentiable Gumbel-softmax mask layer, its backward pass to the logits, hard-mask
- * extraction and the compressed N:M storage format.
+ * extraction and the compressed N:M storage format; around it, the magnitude-prior
+ * initialisation of the logits, the forward with the convergence monitors fused in, and the
+ * product of activations with the packed 2:4 weights on the sparse matrix cores.
  *
  * Method (MaskLLM project page, "MaskLLM: Learnable Semi-Structured Sparsity for Large Language
  * Models", Fig. 3 caption): each run of M consecutive weights owns a learnable categorical
