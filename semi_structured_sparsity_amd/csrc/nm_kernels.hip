@@ -20,15 +20,16 @@ __device__ __forceinline__ void load_f32(const float* __restrict__ p, bool vec, 
         if constexpr (ALIGN == 16 && CNT % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < CNT / 4; ++i) {
-                const float4 v = reinterpret_cast<const float4*>(p)[i];
-                out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+                const uint4 v = nt_load4(reinterpret_cast<const float4*>(p) + i);
+                out[4 * i] = __uint_as_float(v.x); out[4 * i + 1] = __uint_as_float(v.y);
+                out[4 * i + 2] = __uint_as_float(v.z); out[4 * i + 3] = __uint_as_float(v.w);
             }
         } else {
             static_assert(CNT % 2 == 0, "even count");
 #pragma unroll
             for (int i = 0; i < CNT / 2; ++i) {
-                const float2 v = reinterpret_cast<const float2*>(p)[i];
-                out[2 * i] = v.x; out[2 * i + 1] = v.y;
+                const uint2 v = nt_load2(reinterpret_cast<const float2*>(p) + i);
+                out[2 * i] = __uint_as_float(v.x); out[2 * i + 1] = __uint_as_float(v.y);
             }
         }
         return;
@@ -214,7 +215,15 @@ __device__ __forceinline__ void load_logits(const float* logits, int64_t g0, boo
         if (staged) {
             const V* src = reinterpret_cast<const V*>(logits + (int64_t)blockIdx.x * kThreads * PK);
 #pragma unroll
-            for (int i = 0; i < PER; ++i) tile[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
+            for (int i = 0; i < PER; ++i) {
+                if constexpr (sizeof(V) == 16) {
+                    const uint4 u = nt_load4(src + threadIdx.x + i * kThreads);
+                    tile[threadIdx.x + i * kThreads] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+                } else {
+                    const uint2 u = nt_load2(src + threadIdx.x + i * kThreads);
+                    tile[threadIdx.x + i * kThreads] = make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
+                }
+            }
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < PER; ++i) vec_to_floats(tile[threadIdx.x * PER + i], l + W * i);
