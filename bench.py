@@ -64,6 +64,12 @@ def parse():
     return p.parse_args()
 
 
+def kernel_prior(w, n, m):
+    """Prior candidate of every group from the library's own magnitude-prior kernel."""
+    import semi_structured_sparsity_amd as S
+    return S.nm_prior_init(w, n, m, 1.0, with_idx=True)[1]
+
+
 def make_layer(dev):
     import torch
 
@@ -72,7 +78,7 @@ def make_layer(dev):
     for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
         seed = nm_synth.input_seed(2, 0, i)
         w, L, G = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed,
-                                         logits="prior", device=dev)
+                                         logits="prior", device=dev, prior=kernel_prior)
         mats.append(dict(name=name, rows=rows, cols=cols, seed=seed, w=w, L=L, G=G,
                          out=torch.empty_like(w),
                          dl=torch.empty_like(L),
@@ -119,7 +125,8 @@ def cpu_baseline(min_seconds=10.0, max_passes=8):
     for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
         seed = nm_synth.input_seed(2, 0, i)
         w = nm_synth.normal((rows, cols), 0.02, 3 * seed, torch.bfloat16)
-        mats.append((seed, cols, w, nm_synth.prior_logits(w, N, M, 3 * seed + 1),
+        prior = torch.from_numpy(oracle.prior_init(w, N, M)[1].astype("int64"))
+        mats.append((seed, cols, w, nm_synth.prior_logits(prior, K, 3 * seed + 1),
                      nm_synth.normal((rows, cols), 1.0, 3 * seed + 2, torch.bfloat16)))
     total_w, elapsed, passes = 0, 0.0, 0
     while passes < max_passes and (passes == 0 or elapsed < min_seconds):
@@ -283,7 +290,7 @@ def workload_sweep32(args):
         for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
             seed = nm_synth.input_seed(3, layer, i)
             w, L, G = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed,
-                                             logits="prior", device=dev)
+                                             logits="prior", device=dev, prior=kernel_prior)
             mats.append(dict(rows=rows, cols=cols, seed=seed, w=w, L=L, G=G))
         layers.append(mats)
     outs = {}
@@ -493,7 +500,8 @@ def workload_spmm(args):
     mats = []
     for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
         seed = nm_synth.input_seed(2, 0, i)
-        w, L, _ = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed, logits="prior", device=dev)
+        w, L, _ = nm_synth.matrix_inputs(rows, cols, N, M, torch.bfloat16, 0.02, seed, logits="prior", device=dev,
+                                         prior=kernel_prior)
         values, indices = S.nm_mask_harden_pack(w, L, N, M)
         dense_t = S.nm_unpack(values, indices, cols, N, M).t().contiguous()  # [in, out], contiguous
         x = nm_synth.normal((tokens, cols), 1.0, seed + 7, torch.bfloat16, device=dev)
@@ -670,7 +678,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic: seeded Gaussian bf16 weights N(0,0.02) and grads N(0,1); fp32 logits "
-                "3*onehot(magnitude prior) + N(0,0.1); generated on the GPU",
+                "3*onehot(magnitude prior, from nm_prior_init) + N(0,0.1); generated on the GPU",
         "config": {"workload": "LLaMA-2-7B-shaped decoder layer, 7 matrices, 202,375,168 weights, "
                                "2:4, bf16 weights, fp32 logits, kappa=100, tau=4",
                    "passes_per_step": "fwd+bwd+harden_pack+unpack",

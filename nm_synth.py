@@ -1,16 +1,15 @@
 """Seeded synthetic inputs for the N:M mask layer: weights, logits and upstream gradients.
 
 This module is shared by the tests, the benchmark and the smoke check.  It generates inputs
-only; it contains none of the layer's arithmetic (no noise, softmax, masking or packing) and
-imports neither the HIP binding nor the oracle.  Every tensor comes from a torch CPU generator
-seeded explicitly, so the same call gives the same bits on any host.
+only; it contains none of the method's arithmetic (no noise of the method, softmax, masking,
+packing or magnitude prior) and imports neither the HIP binding nor the oracle.  Every tensor
+comes from a torch generator seeded explicitly.
 
 Shapes follow the model families the MaskLLM project page evaluates (LLaMA-2 7B, Nemotron-4
 15B).  Trained checkpoints are not available, so weights are Gaussian stand-ins with the
-standard deviations below.  The magnitude prior follows the magnitude-pruning rule of the
-"Accelerating Sparse Deep Neural Networks" page (section 4.1: keep the largest magnitudes of
-each group), used as the prior mask that initialises the logits (MaskLLM project page,
-Table 2 caption).
+standard deviations below.  Prior-initialised logits (MaskLLM project page, Table 2 caption)
+are assembled here from a prior candidate index that the caller computes: the tests take it
+from the oracle, the benchmark from the library's own prior kernel.
 """
 import itertools
 
@@ -53,29 +52,16 @@ def num_candidates(n, m):
     return len(list(itertools.combinations(range(m), n)))
 
 
-def magnitude_prior_index(w, n, m):
-    """Index, in lexicographic candidate order, of the mask that keeps the n largest |w| of
-    each group of m consecutive weights along the last dimension; ties keep the lower
-    position.  Returns int64 [rows, cols/m]."""
-    rows, cols = w.shape
-    a = w.float().abs().reshape(rows, cols // m, m)
-    # stable sort of -|w|: equal magnitudes keep their original (lower-first) order
-    order = torch.sort(-a, dim=-1, stable=True).indices[..., :n]
-    code = (torch.ones_like(order) << order).sum(-1)
-    lut = torch.full((1 << m,), -1, dtype=torch.int64, device=w.device)
-    for k, pos in enumerate(itertools.combinations(range(m), n)):
-        lut[sum(1 << p for p in pos)] = k
-    return lut[code]
+PRIOR_ALPHA = 3.0       # logit of the prior candidate
+PRIOR_NOISE_STD = 0.1   # N(0, 0.1) added to every logit
 
 
-def prior_logits(w, n, m, seed, alpha=3.0, noise_std=0.1):
-    """fp32 logits [rows, cols/m, K] on w's device: alpha on the magnitude-prior candidate,
-    0 elsewhere, plus N(0, noise_std^2)."""
-    rows, cols = w.shape
-    K = num_candidates(n, m)
-    idx = magnitude_prior_index(w, n, m)
-    L = normal((rows, cols // m, K), noise_std, seed, device=w.device)
-    L.scatter_add_(-1, idx.unsqueeze(-1), torch.full(idx.shape + (1,), alpha, device=w.device))
+def prior_logits(prior_idx, K, seed, alpha=PRIOR_ALPHA, noise_std=PRIOR_NOISE_STD):
+    """fp32 logits [rows, cols/m, K] on prior_idx's device: N(0, noise_std^2) everywhere plus
+    alpha on the prior candidate prior_idx [rows, cols/m] (computed by the caller)."""
+    idx = prior_idx.long()
+    L = normal(tuple(idx.shape) + (K,), noise_std, seed, device=idx.device)
+    L.scatter_add_(-1, idx.unsqueeze(-1), torch.full(tuple(idx.shape) + (1,), alpha, device=idx.device))
     return L
 
 
@@ -89,11 +75,14 @@ def input_seed(config, layer, matrix):
 
 
 def matrix_inputs(rows, cols, n, m, wtype, w_std, seed, logits="gaussian", with_grad=True,
-                  device="cpu"):
-    """(w, logits, grad) for one weight matrix; grad ~ N(0,1) in the weight type."""
+                  device="cpu", prior=None):
+    """(w, logits, grad) for one weight matrix; grad ~ N(0,1) in the weight type.  With
+    logits="prior", `prior(w, n, m)` must return the prior candidate index of every group."""
     w = normal((rows, cols), w_std, 3 * seed + 0, wtype, device)
     if logits == "prior":
-        L = prior_logits(w, n, m, 3 * seed + 1)
+        if prior is None:
+            raise ValueError("prior logits need the caller's prior(w, n, m)")
+        L = prior_logits(prior(w, n, m).to(w.device), num_candidates(n, m), 3 * seed + 1)
     else:
         L = gaussian_logits(rows, cols, n, m, 3 * seed + 1, device=device)
     G = normal((rows, cols), 1.0, 3 * seed + 2, wtype, device) if with_grad else None

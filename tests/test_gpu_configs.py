@@ -20,6 +20,7 @@ import torch
 import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
+from oracle_inputs import oracle_prior
 from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, soft_mask_check,
                     tol_for_tau)
 
@@ -139,7 +140,7 @@ def test_config2_llama7b_layer(i):
     seed = nm_synth.input_seed(2, 0, i)
     _say("config2", name, rows, cols)
     w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
-                                     device=DEV)
+                                     prior=oracle_prior, device=DEV)
     out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, 0)
     dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, 0)
     wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl)
@@ -148,7 +149,7 @@ def test_config2_llama7b_layer(i):
     _grad_properties(w, G, dl, n, m, kappa, tau)
     _check_pack_full(w, L, n, m)
     # the prior's candidate is the hard mask wherever the prior logit margin (3) dominates
-    prior = nm_synth.magnitude_prior_index(w, n, m)
+    prior = oracle_prior(w, n, m).to(DEV)
     _, _, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
     assert float((hard.long() == prior).double().mean()) > 0.999
     # the prior-initialisation kernel over the whole matrix, every element against the oracle
@@ -174,7 +175,7 @@ def test_config3_annealed_sweep_sampled(layer, step):
         seed = nm_synth.input_seed(3, layer, i)
         _say("config3", layer, step, name)
         w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
-                                         device=DEV)
+                                         prior=oracle_prior, device=DEV)
         out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, step)
         dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, step)
         _check_rows(w, L, G, n, m, kappa, tau, seed, step, out, dl)

@@ -12,6 +12,7 @@ import torch
 import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
+from oracle_inputs import oracle_prior
 from parity import l1_of, perturbed_scores, sample_bound, sample_check
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +116,8 @@ def test_monitor_full_llama7b_down_projection():
     name, rows, cols = nm_synth.LLAMA2_7B_LAYER[-1]
     seed = nm_synth.input_seed(2, 0, len(nm_synth.LLAMA2_7B_LAYER) - 1)
     _say("monitor full", name, rows, cols)
-    w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior", device=DEV)
+    w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior", device=DEV,
+                                     prior=oracle_prior)
     Lc = L.cpu()
     _, s0, st0 = S.nm_mask_forward_monitor(w, L, n, m, kappa, tau, seed, 0)
     nd0 = _check_step(Lc, n, m, kappa, tau, seed, 0, s0, st0)

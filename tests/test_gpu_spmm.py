@@ -11,6 +11,7 @@ import torch
 import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
+from oracle_inputs import oracle_prior
 from parity import spmm_check
 
 pytestmark = pytest.mark.gpu
@@ -23,7 +24,8 @@ def _say(*a):
 
 
 def _packed_layer(out, inn, seed, w_std=0.02):
-    w, L, _ = nm_synth.matrix_inputs(out, inn, 2, 4, torch.bfloat16, w_std, seed, logits="prior", device=DEV)
+    w, L, _ = nm_synth.matrix_inputs(out, inn, 2, 4, torch.bfloat16, w_std, seed, logits="prior", device=DEV,
+                                     prior=oracle_prior)
     values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
     return w, values, indices
 

@@ -135,23 +135,14 @@ def test_packed_size_matches_the_pages_storage_saving():
     assert (cols // 2 * 2 + words * 4) / (cols * 2) == 0.5625
 
 
-def test_magnitude_prior_keeps_the_largest_magnitudes():
-    """The input generator's prior (magnitude pruning, section 4.1 of the 2:4 page): brute force,
-    ties keep the lower position."""
+def test_prior_initialised_logits_harden_to_the_prior():
+    """Prior-initialised inputs: logit 3 on the oracle's prior candidate plus N(0, 0.1) noise;
+    the hard mask of such logits is the prior mask itself."""
     w = nm_synth.normal((6, 64), 0.02, 7, torch.bfloat16)
-    w[0, :4] = torch.tensor([0.5, -0.5, 0.5, 0.25])   # tie between positions 0, 1, 2
     for n, m in [(2, 4), (1, 4), (4, 8), (2, 8)]:
-        idx = nm_synth.magnitude_prior_index(w, n, m)
-        cand = list(itertools.combinations(range(m), n))
-        a = w.float().abs().numpy()
-        for r in range(6):
-            for q in range(64 // m):
-                grp = list(a[r, q * m:(q + 1) * m])
-                keep = tuple(sorted(sorted(range(m), key=lambda j: (-grp[j], j))[:n]))
-                assert cand[idx[r, q]] == keep
-    assert nm_synth.magnitude_prior_index(w, 2, 4)[0, 0] == 0   # keeps {0, 1}
-    L = nm_synth.prior_logits(w, 2, 4, seed=1)
-    np.testing.assert_array_equal(oracle.harden(L, 2, 4), nm_synth.magnitude_prior_index(w, 2, 4))
+        _, idx = oracle.prior_init(w, n, m)
+        L = nm_synth.prior_logits(torch.from_numpy(idx.astype(np.int64)), oracle.num_candidates(n, m), seed=1)
+        np.testing.assert_array_equal(oracle.harden(L, n, m), idx)
 
 
 # --- magnitude prior (the step before the path) ----------------------------------------------
@@ -181,8 +172,6 @@ def test_prior_init_keeps_the_largest_magnitudes(n, m, wtype):
             want = np.zeros(len(cand), np.float32)
             want[k] = 2.5
             assert logits[r, q].tobytes() == want.tobytes()
-    # the input generator's torch implementation of the same rule agrees
-    np.testing.assert_array_equal(idx, nm_synth.magnitude_prior_index(w, n, m).numpy())
     # and its logits are exactly alpha * onehot
     assert set(np.unique(logits)) <= {0.0, 2.5}
 
