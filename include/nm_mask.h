@@ -208,8 +208,8 @@ nm_status nm_debug_noise(const nm_shape *shape, const nm_sample *sample, uint32_
  * that the Gumbel sample is g = -ln(2) * (h + log2(ln 2)).  words and h hold count elements. */
 nm_status nm_debug_gumbel_log2(const uint32_t *words, float *h, int64_t count, void *stream);
 /* Plain device copy of `bytes` (a multiple of 16) with the access pattern of the path kernels
- * (one 16-byte vector per thread, non-temporal stores): the streaming ceiling the path's
- * bandwidth is compared with.  src and dst 16-byte aligned, not overlapping. */
+ * (one 16-byte vector per thread, non-temporal loads and stores): the streaming ceiling the
+ * path's bandwidth is compared with.  src and dst 16-byte aligned, not overlapping. */
 nm_status nm_debug_copy(const void *src, void *dst, int64_t bytes, void *stream);
 /* Soft mask [rows, cols] fp32 of a sample (the forward's m before the multiply). */
 nm_status nm_debug_soft_mask(const nm_shape *shape, const nm_sample *sample,

@@ -551,14 +551,14 @@ __device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, ui
 // of T, each zero-extended into a uint32.  vec: the caller guarantees 16-byte alignment, that
 // CNT * bytes is a multiple of 16 and that all CNT elements exist; otherwise element i is read
 // or written only if i < valid.
-template <typename T, int CNT>
+template <typename T, int CNT, bool NTL = false>
 __device__ __forceinline__ void load_raw(const typename T::storage* __restrict__ p, bool vec, int valid,
                                          uint32_t* out) {
     static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
     if (vec) {
 #pragma unroll
         for (int i = 0; i < CNT * T::bytes / 16; ++i) {
-            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+            const uint4 v = NTL ? nt_load4(reinterpret_cast<const uint4*>(p) + i) : reinterpret_cast<const uint4*>(p)[i];
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -843,17 +843,42 @@ struct ByteTiling {
     static_assert(N == 1 || N == 2, "one index byte holds whole groups");
 };
 
+// The logits of a full block's threads form one contiguous span of kThreads * CNT floats: it is
+// read with consecutive lanes on consecutive 16-byte vectors (non-temporally: each is read
+// once) and handed to the threads through an LDS tile.
+template <int CNT>
+__device__ __forceinline__ void load_block_logits(const float* __restrict__ block_base, float4* tile,
+                                                  float (&l)[CNT]) {
+    static_assert(CNT % 4 == 0, "whole float4 vectors per thread");
+    constexpr int PER = CNT / 4;
+    const float4* src = reinterpret_cast<const float4*>(block_base);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const uint4 u = nt_load4(src + threadIdx.x + i * kThreads);
+        tile[threadIdx.x + i * kThreads] =
+            make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) vec_to_floats(tile[threadIdx.x * PER + i], l + 4 * i);
+}
+
 template <int N, typename T>
 __global__ __launch_bounds__(kThreads) void k_pack_bytes(PackArgs a) {
     using BT = ByteTiling<N, T>;
     constexpr int M = 4, K = BT::K, U = BT::U;
+    __shared__ float4 tile[kThreads * U * K / 4];
+    const int64_t groups = a.rows * a.gpr;
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g0 = t * U;
-    if (g0 >= a.rows * a.gpr) return;  // groups come in whole bytes: no partial thread
+    const bool staged = ((int64_t)blockIdx.x + 1) * kThreads * U <= groups;  // uniform: a full block
+    if (g0 >= groups) return;  // only in the last block, which is not staged
     float l[U * K];
-    load_logit_unit<U * K>(a.logits + g0 * K, true, U * K, l);
+    if (staged) load_block_logits<U * K>(a.logits + (int64_t)blockIdx.x * kThreads * U * K, tile, l);
+    else load_logit_unit<U * K>(a.logits + g0 * K, true, U * K, l);
     uint32_t raw[U * M];
-    load_raw<T, U * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true, U * M, raw);
+    load_raw<T, U * M, U * M * T::bytes == 16>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true,
+                                                U * M, raw);
     uint32_t vals[U * N];
     uint32_t byte = 0u, hard = 0u;
 #pragma unroll
@@ -998,11 +1023,13 @@ __global__ __launch_bounds__(kThreads) void k_debug_noise(NoiseArgs a) {
 }
 
 // A plain flat copy with the path kernels' access pattern (one 16-byte vector per thread, one
-// tile per thread, non-temporal store): the streaming ceiling the path is compared with.
+// tile per thread, non-temporal load and store): the streaming ceiling the path is compared
+// with.  Of the copy shapes measured (1, 2, 4 or 8 vectors per thread, ordinary or
+// non-temporal loads), this one is the fastest on MI355X.
 __global__ __launch_bounds__(kThreads) void k_debug_copy(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         int64_t vecs) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < vecs) nt_store(dst + i, src[i]);
+    if (i < vecs) nt_store(dst + i, nt_load4(src + i));
 }
 
 __global__ __launch_bounds__(kThreads) void k_debug_gumbel(GumbelArgs a) {
