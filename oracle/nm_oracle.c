@@ -4,7 +4,7 @@
  * TEST INFRASTRUCTURE ONLY: loaded by the tests, the package smoke check and the CPU-baseline
  * leg of the benchmark, never by the product path.  It is written from the pages and from the
  * Philox paper, group by group, with no blocking, fusion or reordering beyond the definitions
- * quoted at each function; all floating point is IEEE binary64 and the file is compiled without
+ * stated at each function; all floating point is IEEE binary64 and the file is compiled without
  * fast-math and without floating-point contraction.  See nm_oracle.h for the sources.
  */
 #define _GNU_SOURCE
