@@ -251,9 +251,9 @@ nm_status nm_sparse_matmul(const nm_shape* w_shape, const void* values, const ui
     if (w_shape->n != 2 || w_shape->m != 4 || w_shape->wtype != NM_BF16) return NM_EUNSUPPORTED;
     const int64_t out = w_shape->rows, in = w_shape->cols;
     if (out == 0 || tokens == 0) return NM_OK;
-    if (in == 0 || in % 64 != 0 || out % 256 != 0 || tokens % 256 != 0) return NM_EUNSUPPORTED;
-    if ((out / 256) * (tokens / 256) > (int64_t)INT32_MAX - 8) return NM_EINVAL;  // one block per tile
+    if (in == 0 || in % 64 != 0 || out % 4 != 0) return NM_EUNSUPPORTED;
     if (tokens > INT64_MAX / 4 / (in > out ? in : out)) return NM_EINVAL;
+    if (((out + 255) / 256 + 8) * ((tokens + 255) / 256 + 4) > (int64_t)INT32_MAX) return NM_EINVAL;  // one block per tile
     if (!values || !indices || !x || !y) return NM_EINVAL;
     if (!aligned16(values) || !aligned16(indices) || !aligned16(x) || !aligned16(y)) return NM_EALIGN;
     nm::SpmmArgs a{static_cast<const uint16_t*>(values), indices, static_cast<const uint16_t*>(x), y,

@@ -17,7 +17,8 @@
 // So one lane's index operand is 16 consecutive bits of a packed row's index stream and its A
 // values are 8 consecutive packed values: the packed form feeds the instruction unchanged.
 //
-// Tiling: a block of 512 threads computes a 256 (out) x 256 (token) tile of Y^T, each of its 8
+// Tiling: a block of 512 threads computes a 256 (out) x 256 (token) tile of Y^T (the last tile
+// along either side may be partial), each of its 8
 // waves a 128 x 64 part as 4 x 2 instruction tiles with fp32 accumulators.  Per stage of 64
 // dense k the block stages the packed values (256 rows x 64 B), their index words (256 x 8 B)
 // and X (256 tokens x 128 B) in LDS, double buffered: the next stage is loaded from memory into
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     uint32_t* Is = reinterpret_cast<uint32_t*>(smem + 2 * SP_ABUF + 2 * SP_BBUF);  // [2][SP_BM*2]
 
     // XCD-aware tile order: block b runs on XCD b % 8 and takes tile (b % 8) * chunk + b / 8
-    const int64_t ntok = a.tokens / SP_BN, nout = a.out / SP_BM;
+    const int64_t ntok = (a.tokens + SP_BN - 1) / SP_BN, nout = (a.out + SP_BM - 1) / SP_BM;
     const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
     const int64_t rt = (ntok + C - 1) / C, ro = (nout + R - 1) / R;   // region size in tiles
     const int64_t x = blockIdx.x % 8, p = blockIdx.x / 8;
@@ -62,12 +63,18 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wo = (wv >> 2) * 128, wt = (wv & 3) * 64;
 
-    // staging: per thread 2 x 16 B of packed values, 4 B of index words, 4 x 16 B of X
-    const uint16_t* va = a.values + (bo + (tid >> 2)) * a.vstride + (tid & 3) * 8;
-    const int64_t vrow128 = 128 * a.vstride;                    // 128 rows further
-    const uint32_t* ia = a.indices + (bo + (tid >> 1)) * a.istride + (tid & 1);
-    const uint16_t* xa = a.x + (bt + (tid >> 3)) * a.xstride + (tid & 7) * 8;
-    const int64_t xrow64 = 64 * a.xstride;                      // 64 tokens further
+    // staging: per thread 2 x 16 B of packed values, 4 B of index words, 4 x 16 B of X.  In the
+    // last tile of a ragged count, W rows past the end read the last row and tokens past the end
+    // the last token; their outputs are computed but not stored.
+    const int64_t olast = a.out - 1, o0 = bo + (tid >> 2), o1 = bo + (tid >> 1);
+    const uint16_t* va0 = a.values + (o0 < olast ? o0 : olast) * a.vstride + (tid & 3) * 8;
+    const uint16_t* va1 = a.values + (o0 + 128 < olast ? o0 + 128 : olast) * a.vstride + (tid & 3) * 8;
+    const uint32_t* ia = a.indices + (o1 < olast ? o1 : olast) * a.istride + (tid & 1);
+    const int64_t tlast = a.tokens - 1, t0 = bt + (tid >> 3);
+    const uint16_t* xa0 = a.x + (t0 < tlast ? t0 : tlast) * a.xstride + (tid & 7) * 8;
+    const uint16_t* xa1 = a.x + (t0 + 64 < tlast ? t0 + 64 : tlast) * a.xstride + (tid & 7) * 8;
+    const uint16_t* xa2 = a.x + (t0 + 128 < tlast ? t0 + 128 : tlast) * a.xstride + (tid & 7) * 8;
+    const uint16_t* xa3 = a.x + (t0 + 192 < tlast ? t0 + 192 : tlast) * a.xstride + (tid & 7) * 8;
     const int la = (tid >> 2) * SP_AP + (tid & 3) * 8;          // + 128 * SP_AP for the second
     const int lx = (tid >> 3) * SP_BP + (tid & 7) * 8;          // + 64 * SP_BP per step
     uint4 ra0, ra1, rx0, rx1, rx2, rx3;
@@ -86,13 +93,13 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
 
 #define NM_SP_GLOAD(ks)                                                                 \
     do {                                                                                \
-        ra0 = *reinterpret_cast<const uint4*>(va + (ks) * 32);                          \
-        ra1 = *reinterpret_cast<const uint4*>(va + vrow128 + (ks) * 32);                \
+        ra0 = *reinterpret_cast<const uint4*>(va0 + (ks) * 32);                         \
+        ra1 = *reinterpret_cast<const uint4*>(va1 + (ks) * 32);                         \
         ri = ia[(ks) * 2];                                                              \
-        rx0 = *reinterpret_cast<const uint4*>(xa + (ks) * 64);                          \
-        rx1 = *reinterpret_cast<const uint4*>(xa + xrow64 + (ks) * 64);                 \
-        rx2 = *reinterpret_cast<const uint4*>(xa + 2 * xrow64 + (ks) * 64);             \
-        rx3 = *reinterpret_cast<const uint4*>(xa + 3 * xrow64 + (ks) * 64);             \
+        rx0 = *reinterpret_cast<const uint4*>(xa0 + (ks) * 64);                         \
+        rx1 = *reinterpret_cast<const uint4*>(xa1 + (ks) * 64);                         \
+        rx2 = *reinterpret_cast<const uint4*>(xa2 + (ks) * 64);                         \
+        rx3 = *reinterpret_cast<const uint4*>(xa3 + (ks) * 64);                         \
     } while (0)
 #define NM_SP_LSTORE(buf)                                                               \
     do {                                                                                \
@@ -151,9 +158,11 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t t = bt + wt + j * 32 + r32;
+            if (t >= a.tokens) continue;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t o = bo + wo + i * 32 + q * 8 + kg * 4;
+                const int64_t o = bo + wo + i * 32 + q * 8 + kg * 4;  // out % 4 == 0: o..o+3 all in or out
+                if (o >= a.out) continue;
                 const f32x16_t v = acc[i][j];
                 if (a.ytype == 0) {
                     *reinterpret_cast<float4*>(static_cast<float*>(a.y) + t * a.ystride + o) =
@@ -177,7 +186,7 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
     const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)SP_SMEM);
     if (e != hipSuccess) return e;
-    const int64_t ntok = a.tokens / SP_BN, nout = a.out / SP_BM;
+    const int64_t ntok = (a.tokens + SP_BN - 1) / SP_BN, nout = (a.out + SP_BM - 1) / SP_BM;
     const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
     const int64_t grid = 8 * ((ntok + C - 1) / C) * ((nout + R - 1) / R);
     k_spmm24<<<dim3((unsigned)grid), SP_THREADS, SP_SMEM, s>>>(a);

@@ -31,16 +31,31 @@ def to_f64(t):
     return t.detach().double().cpu().numpy()
 
 
+def _diff(gpu, ref):
+    """|gpu - ref|, taking equal infinities and NaN on both sides as agreement and a NaN on one
+    side only as an infinite error."""
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    with np.errstate(invalid="ignore"):
+        d = np.abs(gpu - ref)
+    same = (gpu == ref) | (np.isnan(gpu) & np.isnan(ref))
+    d[same] = 0.0
+    d[np.isnan(d)] = np.inf
+    return d
+
+
 def _verdict(err, bound):
-    """(largest err/bound, number of elements over their bound); a ratio <= 1 passes."""
-    ratio = err / np.maximum(bound, 1e-300)
-    return float(ratio.max(initial=0.0)), int((err > bound).sum())
+    """(largest err/bound, number of elements over their bound); a ratio <= 1 passes.  An exact
+    match always passes; any other error passes only under a bound that is not NaN."""
+    bad = (err != 0) & ~(err <= bound)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ratio = np.where(err == 0, 0.0, err / np.maximum(bound, 1e-300))
+    return float(np.nan_to_num(ratio, nan=np.inf).max(initial=0.0)), int(bad.sum())
 
 
 def soft_mask_check(gpu, ref, m, tol):
     g = np.asarray(gpu, np.float64).reshape(-1, m)
     r = np.asarray(ref, np.float64).reshape(-1, m)
-    return _verdict(np.abs(g - r).max(1), tol * np.abs(r).max(1))
+    return _verdict(_diff(g, r).max(1), tol * np.abs(r).max(1))
 
 
 def forward_check(gpu, ref, w, soft_ref, m, tol, bf16):
@@ -49,7 +64,7 @@ def forward_check(gpu, ref, w, soft_ref, m, tol, bf16):
     gpu = np.asarray(gpu, np.float64)
     mmax = np.repeat(np.abs(soft_ref).reshape(-1, m).max(1), m).reshape(ref.shape)
     out_round = (TOL_BF16 if bf16 else 2.0**-24) * np.abs(ref)
-    return _verdict(np.abs(gpu - ref), tol * mmax * np.abs(w) + out_round)
+    return _verdict(_diff(gpu, ref), tol * mmax * np.abs(w) + out_round)
 
 
 def backward_check(gpu, ref, y, d, c, tol):
@@ -58,7 +73,7 @@ def backward_check(gpu, ref, y, d, c, tol):
     ad = np.abs(d)
     terms = c * y * (ad + (y * ad).sum(-1, keepdims=True))
     floor = c * 1e-36 * ad.max(-1, keepdims=True)  # probabilities near the fp32 underflow
-    return _verdict(np.abs(gpu - ref), tol * terms + floor)
+    return _verdict(_diff(gpu, ref), tol * terms + floor)
 
 
 def candidate_sums(w, grad, n, m, cand_matrix):
@@ -129,4 +144,4 @@ def spmm_check(gpu, ref, absterms, n_terms, bf16_out):
     bound = n_terms * 2.0**-24 * np.asarray(absterms, np.float64)
     if bf16_out:
         bound = bound + 2.0**-8 * np.abs(ref)
-    return _verdict(np.abs(gpu - ref), bound + 1e-30)
+    return _verdict(_diff(gpu, ref), bound + 1e-30)

@@ -181,9 +181,9 @@ def test_sparse_matmul_is_validated_on_the_host():
     ok = lambda shp, tokens=256, y=FAKE, ytype=1, v=FAKE: L.nm_sparse_matmul(shp, v, FAKE, FAKE, tokens, y, ytype, None)
     assert ok(_shape(rows=256, cols=64, n=2, m=4, wtype=0)) == NM_EUNSUPPORTED   # fp32 weights
     assert ok(_shape(rows=256, cols=64, n=1, m=4, wtype=1)) == NM_EUNSUPPORTED   # 1:4
-    assert ok(_shape(rows=128, cols=64, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED   # out % 256
+    assert ok(_shape(rows=130, cols=64, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED   # out % 4
     assert ok(_shape(rows=256, cols=96, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED   # in % 64
-    assert ok(sh, tokens=128) == NM_EUNSUPPORTED
+    assert ok(sh, tokens=1 << 40) == NM_EINVAL                                    # grid beyond 2^31 blocks
     assert ok(sh, tokens=-1) == NM_EINVAL
     assert ok(sh, ytype=5) == NM_EINVAL
     assert ok(sh, y=None) == NM_EINVAL

@@ -308,3 +308,27 @@ def test_misaligned_views_are_refused():
     with pytest.raises(S.NMError) as e:
         S.nm_mask_forward(w, L, n, m, 1.0, 1.0, 0, 0)
     assert e.value.status == S.NM_EALIGN
+
+
+def test_usage_training_loop_then_deployment():
+    """The documented use: prior-initialised logits, a few optimizer steps through the
+    autograd mask (gradient reaches the logits only), then harden+pack and the sparse product."""
+    n, m = 2, 4
+    w = nm_synth.normal((256, 256), 0.5, 51, torch.bfloat16, device=DEV)
+    logits = S.nm_prior_init(w, n, m, 3.0).requires_grad_(True)
+    start = logits.detach().clone()
+    opt = torch.optim.SGD([logits], lr=0.1)
+    for step in range(3):
+        w_masked = S.mask(w, logits, n, m, 10.0, 1.0, 7, step)
+        loss = (w_masked.float() ** 2).sum()
+        loss.backward()
+        assert logits.grad is not None and torch.isfinite(logits.grad).all()
+        opt.step()
+        opt.zero_grad()
+    assert not torch.equal(logits.detach(), start)
+    values, indices = S.nm_mask_harden_pack(w, logits.detach(), n, m)
+    x = nm_synth.normal((256, 256), 1.0, 52, torch.bfloat16, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32)
+    dense = S.nm_unpack(values, indices, 256, n, m).float()
+    ref = x.float() @ dense.t().contiguous()
+    assert torch.allclose(y, ref, rtol=1e-4, atol=1e-3)

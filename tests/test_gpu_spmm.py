@@ -87,11 +87,29 @@ def test_sparse_matmul_equals_dense_product_of_the_unpacked_weights():
     assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32), y.float())
 
 
+@pytest.mark.parametrize("out,inn,tokens", [(4, 64, 1), (260, 64, 100), (516, 192, 300), (1028, 128, 513),
+                                             (252, 256, 255)])
+@pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
+def test_sparse_matmul_partial_tiles(out, inn, tokens, ytype):
+    """out and tokens not multiples of the 256 x 256 tile: the last tiles are partial, every
+    output inside matches the oracle and nothing past y's end is written."""
+    _say("spmm partial", out, inn, tokens, ytype)
+    _, values, indices = _packed_layer(out, inn, 50 + out + tokens, w_std=1.0)
+    x = nm_synth.normal((tokens, inn), 1.0, 51, torch.bfloat16, device=DEV)
+    buf = torch.full((tokens * out + 4096,), float("nan"), dtype=ytype, device=DEV)
+    y = buf[:tokens * out].view(tokens, out)
+    S.nm_sparse_matmul(values, indices, x, out_dtype=ytype, out=y)
+    ratio, bad = _check(values, indices, x, y, bf16_out=ytype == torch.bfloat16)
+    _say("  err/bound", ratio)
+    assert bad == 0
+    assert bool(buf[tokens * out:].isnan().all())
+
+
 def test_sparse_matmul_rejects_unsupported_shapes():
     _, values, indices = _packed_layer(256, 64, 45)
     x = torch.zeros((128, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(S.NMError) as e:
-        S.nm_sparse_matmul(values, indices, x)
+        S.nm_sparse_matmul(values[:254], indices[:254], x)   # out not a multiple of 4
     assert e.value.status == S.NM_EUNSUPPORTED
     x0 = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
     assert S.nm_sparse_matmul(values, indices, x0).shape == (0, 256)
