@@ -18,13 +18,21 @@
 // values are 8 consecutive packed values: the packed form feeds the instruction unchanged.
 //
 // Tiling: a block of 512 threads computes a 256 (out) x 256 (token) tile of Y^T (the last tile
-// along either side may be partial), each of its 8
-// waves a 128 x 64 part as 4 x 2 instruction tiles with fp32 accumulators.  Per stage of 64
-// dense k the block stages the packed values (256 rows x 64 B), their index words (256 x 8 B)
-// and X (256 tokens x 128 B) in LDS, double buffered: the next stage is loaded from memory into
-// registers while the current one runs on the matrix cores, then written to the other buffer,
-// with one barrier per stage.  Blocks are numbered so that each XCD (block id mod 8) works on a
-// contiguous run of tiles, which share W rows in that XCD's L2.
+// along either side may be partial), each of its 8 waves a 128 x 64 part as 4 x 2 instruction
+// tiles with fp32 accumulators.  A stage covers 64 dense k: the packed values (256 rows x 64 B),
+// their index words (256 x 8 B) and X (256 tokens x 128 B), 50 KB in LDS.  Three stages live in
+// LDS at once and are filled by LDS DMA loads (global_load_lds), which write LDS without passing
+// through registers: stage s + 3 is requested once stage s has been read, so memory has about
+// two stages of matrix work to answer, and the LDS fragment reads of each half stage overlap the
+// matrix instructions of the previous half.  One barrier per stage.  Blocks are numbered so that
+// each XCD (block id mod 8) works on a rectangle of tiles, which share W rows and X rows in that
+// XCD's L2.
+//
+// LDS layout.  A DMA load writes its 64 lanes' 16 B chunks to 1 KB of consecutive LDS, lane by
+// lane, so the layout in LDS is chosen through the global address each lane loads.  Rows are
+// stored unpadded with their 16 B chunks permuted by an XOR of row bits (swz_a, swz_x), so that
+// the fragment reads of 8 or 16 consecutive lanes (consecutive rows, one chunk column) fall on
+// distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,20 +44,24 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int SP_BM = 256;  // W rows (outputs) per block
-constexpr int SP_BN = 256;  // tokens per block
-constexpr int SP_AP = 40;   // LDS pitch of a packed-value row, in bf16 (32 kept + 8 padding)
-constexpr int SP_BP = 72;   // LDS pitch of an X row, in bf16 (64 + 8 padding)
-constexpr int SP_ABUF = SP_BM * SP_AP;
-constexpr int SP_BBUF = SP_BN * SP_BP;
+constexpr int SP_BM = 256;                       // W rows (outputs) per block
+constexpr int SP_BN = 256;                       // tokens per block
+constexpr int SP_ABYTES = SP_BM * 64;            // packed values of a stage: 32 kept bf16 per row
+constexpr int SP_XBYTES = SP_BN * 128;           // X of a stage: 64 bf16 per token
+constexpr int SP_IBYTES = SP_BM * 8;             // index words of a stage: 2 per row
+constexpr int SP_STAGE = SP_ABYTES + SP_XBYTES + SP_IBYTES;  // 51,200 B
+constexpr int SP_NBUF = 3;
+constexpr size_t SP_SMEM = (size_t)SP_NBUF * SP_STAGE;       // 153,600 B of the 160 KB
 
 constexpr int SP_THREADS = 512;  // 8 waves: 2 along W rows x 4 along tokens, 128 x 64 each
 
+// chunk permutations: 16 B chunk c of packed-value row r sits at chunk c ^ swz_a(r); chunk c of
+// X row t at c ^ swz_x(t)
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_x(int t) { return (t ^ (t >> 3)) & 7; }
+
 __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t* As = smem;                                          // [2][SP_ABUF]
-    uint16_t* Bs = smem + 2 * SP_ABUF;                            // [2][SP_BBUF]
-    uint32_t* Is = reinterpret_cast<uint32_t*>(smem + 2 * SP_ABUF + 2 * SP_BBUF);  // [2][SP_BM*2]
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     // XCD-aware tile order: block b runs on XCD b % 8 and takes tile (b % 8) * chunk + b / 8
     const int64_t ntok = (a.tokens + SP_BN - 1) / SP_BN, nout = (a.out + SP_BM - 1) / SP_BM;
@@ -63,22 +75,58 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wo = (wv >> 2) * 128, wt = (wv & 3) * 64;
 
-    // staging: per thread 2 x 16 B of packed values, 4 B of index words, 4 x 16 B of X.  In the
-    // last tile of a ragged count, W rows past the end read the last row and tokens past the end
-    // the last token; their outputs are computed but not stored.
-    const int64_t olast = a.out - 1, o0 = bo + (tid >> 2), o1 = bo + (tid >> 1);
-    const uint16_t* va0 = a.values + (o0 < olast ? o0 : olast) * a.vstride + (tid & 3) * 8;
-    const uint16_t* va1 = a.values + (o0 + 128 < olast ? o0 + 128 : olast) * a.vstride + (tid & 3) * 8;
-    const uint32_t* ia = a.indices + (o1 < olast ? o1 : olast) * a.istride + (tid & 1);
-    const int64_t tlast = a.tokens - 1, t0 = bt + (tid >> 3);
-    const uint16_t* xa0 = a.x + (t0 < tlast ? t0 : tlast) * a.xstride + (tid & 7) * 8;
-    const uint16_t* xa1 = a.x + (t0 + 64 < tlast ? t0 + 64 : tlast) * a.xstride + (tid & 7) * 8;
-    const uint16_t* xa2 = a.x + (t0 + 128 < tlast ? t0 + 128 : tlast) * a.xstride + (tid & 7) * 8;
-    const uint16_t* xa3 = a.x + (t0 + 192 < tlast ? t0 + 192 : tlast) * a.xstride + (tid & 7) * 8;
-    const int la = (tid >> 2) * SP_AP + (tid & 3) * 8;          // + 128 * SP_AP for the second
-    const int lx = (tid >> 3) * SP_BP + (tid & 7) * 8;          // + 64 * SP_BP per step
-    uint4 ra0, ra1, rx0, rx1, rx2, rx3;
-    uint32_t ri;
+    // DMA sources.  Per stage each wave fills 2 KB of packed values, 4 KB of X and 256 B of
+    // index words; lane `lane` of the wave's k-th 1 KB piece fills 16 B slot piece * 64 + lane
+    // of the region.  In the last tile of a ragged count, W rows past the end load the last row
+    // and tokens past the end the last token; their outputs are computed but not stored.
+    const int64_t olast = a.out - 1, tlast = a.tokens - 1;
+    auto orow = [&](int r) { const int64_t o = bo + r; return o < olast ? o : olast; };
+    auto trow = [&](int t) { const int64_t u = bt + t; return u < tlast ? u : tlast; };
+    auto asrc = [&](int s) {  // slot = row * 4 + stored chunk
+        return a.values + orow(s >> 2) * a.vstride + (((s & 3) ^ swz_a(s >> 2)) << 3);
+    };
+    auto xsrc = [&](int s) {  // slot = token * 8 + stored chunk
+        return a.x + trow(s >> 3) * a.xstride + (((s & 7) ^ swz_x(s >> 3)) << 3);
+    };
+    const int sa = wv * 128 + lane, sx = wv * 256 + lane, si = wv * 64 + lane;
+    const uint16_t* ga0 = asrc(sa);
+    const uint16_t* ga1 = asrc(sa + 64);
+    const uint16_t* gx0 = xsrc(sx);
+    const uint16_t* gx1 = xsrc(sx + 64);
+    const uint16_t* gx2 = xsrc(sx + 128);
+    const uint16_t* gx3 = xsrc(sx + 192);
+    const uint32_t* gi = a.indices + orow(si >> 1) * a.istride + (si & 1);  // word slot = row * 2 + word
+
+    // LDS destinations of this wave's pieces, relative to a stage
+    const int da = wv * 2048, dx = SP_ABYTES + wv * 4096, di = SP_ABYTES + SP_XBYTES + wv * 256;
+
+#define NM_SP_DMA(ks, buf)                                                                         \
+    do {                                                                                           \
+        unsigned char* st_ = smem + (buf) * SP_STAGE;                                              \
+        __builtin_amdgcn_global_load_lds(ga0 + (ks) * 32, st_ + da, 16, 0, 0);                     \
+        __builtin_amdgcn_global_load_lds(ga1 + (ks) * 32, st_ + da + 1024, 16, 0, 0);              \
+        __builtin_amdgcn_global_load_lds(gx0 + (ks) * 64, st_ + dx, 16, 0, 0);                     \
+        __builtin_amdgcn_global_load_lds(gx1 + (ks) * 64, st_ + dx + 1024, 16, 0, 0);              \
+        __builtin_amdgcn_global_load_lds(gx2 + (ks) * 64, st_ + dx + 2048, 16, 0, 0);              \
+        __builtin_amdgcn_global_load_lds(gx3 + (ks) * 64, st_ + dx + 3072, 16, 0, 0);              \
+        __builtin_amdgcn_global_load_lds(gi + (ks) * 2, st_ + di, 4, 0, 0);                        \
+    } while (0)
+
+    // fragment offsets within a stage (lane constants; the rest folds into immediates)
+    const int r32 = lane & 31, kg = lane >> 5;
+    const int sw = swz_a(r32);  // rows wo + 32 i + r32 share r32's bits 1-4
+    int aoff[2], xoff[2][2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        aoff[h] = (wo + r32) * 64 + (((2 * h + kg) ^ sw) << 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = wt + j * 32 + r32, s = swz_x(t);
+            xoff[h][j][0] = SP_ABYTES + t * 128 + (((4 * h + kg) ^ s) << 4);
+            xoff[h][j][1] = SP_ABYTES + t * 128 + (((4 * h + 2 + kg) ^ s) << 4);
+        }
+    }
+    const int ioff = SP_ABYTES + SP_XBYTES + (wo + r32) * 8;
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -88,68 +136,89 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // fragments of one instruction column (32 dense k) of a stage: 4 A tiles with their index
+    // words and 2 B tiles
+    struct Frag {
+        bf16x8_t a[4], lo[2], hi[2];
+        uint32_t i[4];  // the index word of the tile's rows; this lane's half is taken at use
+    };
+#define NM_SP_READ(F, st, h)                                                                       \
+    do {                                                                                           \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
+            (F).a[i_] = *reinterpret_cast<const bf16x8_t*>((st) + aoff[h] + i_ * 32 * 64);         \
+            (F).i[i_] = *reinterpret_cast<const uint32_t*>((st) + ioff + i_ * 32 * 8 + (h) * 4);   \
+        }                                                                                          \
+        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_) {                                         \
+            (F).lo[j_] = *reinterpret_cast<const bf16x8_t*>((st) + xoff[h][j_][0]);                \
+            (F).hi[j_] = *reinterpret_cast<const bf16x8_t*>((st) + xoff[h][j_][1]);                \
+        }                                                                                          \
+    } while (0)
+#define NM_SP_MMA(F)                                                                               \
+    do {                                                                                           \
+        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_) {                                         \
+            const bf16x16_t bf_ = __builtin_shufflevector((F).lo[j_], (F).hi[j_], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15); \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                       \
+                acc[i_][j_] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16((F).a[i_], bf_, acc[i_][j_],     \
+                                                                        (int)((F).i[i_] >> (kg * 16)), 0, 0); \
+        }                                                                                          \
+    } while (0)
+
+    // Pipeline.  Stages s, s + 1 and s + 2 occupy the three buffers.  While the first half (32
+    // dense k) of stage s is multiplied, the second half's fragments are read from LDS; then,
+    // after one barrier, the buffer of stage s is refilled with stage s + 3 and the first half of
+    // stage s + 1 is read while the second half of stage s is multiplied.  The barrier carries
+    // no fence (a fence would wait for every outstanding DMA load, the later stages' too): each
+    // wave waits explicitly for its own loads of stage s + 1 (7 per stage; those of stage s + 2
+    // may stay in flight) and for its own LDS reads, then all waves meet.
     const int64_t nk = a.in / 64;
-    const int r32 = lane & 31, kg = lane >> 5;
+    NM_SP_DMA(0, 0);
+    if (nk > 1) NM_SP_DMA(1, 1);
+    if (nk > 2) NM_SP_DMA(2, 2);
+    if (nk > 2)
+        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else if (nk > 1)
+        asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-#define NM_SP_GLOAD(ks)                                                                 \
-    do {                                                                                \
-        ra0 = *reinterpret_cast<const uint4*>(va0 + (ks) * 32);                         \
-        ra1 = *reinterpret_cast<const uint4*>(va1 + (ks) * 32);                         \
-        ri = ia[(ks) * 2];                                                              \
-        rx0 = *reinterpret_cast<const uint4*>(xa0 + (ks) * 64);                         \
-        rx1 = *reinterpret_cast<const uint4*>(xa1 + (ks) * 64);                         \
-        rx2 = *reinterpret_cast<const uint4*>(xa2 + (ks) * 64);                         \
-        rx3 = *reinterpret_cast<const uint4*>(xa3 + (ks) * 64);                         \
-    } while (0)
-#define NM_SP_LSTORE(buf)                                                               \
-    do {                                                                                \
-        uint16_t* as_ = As + (buf) * SP_ABUF + la;                                      \
-        uint16_t* bs_ = Bs + (buf) * SP_BBUF + lx;                                      \
-        *reinterpret_cast<uint4*>(as_) = ra0;                                           \
-        *reinterpret_cast<uint4*>(as_ + 128 * SP_AP) = ra1;                             \
-        Is[(buf) * SP_BM * 2 + tid] = ri; /* row tid/2, word tid%2 */                   \
-        *reinterpret_cast<uint4*>(bs_) = rx0;                                           \
-        *reinterpret_cast<uint4*>(bs_ + 64 * SP_BP) = rx1;                              \
-        *reinterpret_cast<uint4*>(bs_ + 128 * SP_BP) = rx2;                             \
-        *reinterpret_cast<uint4*>(bs_ + 192 * SP_BP) = rx3;                             \
-    } while (0)
-
-    NM_SP_GLOAD(0);
-    NM_SP_LSTORE(0);
-    __syncthreads();
-    if (nk > 1) NM_SP_GLOAD(1);
-    for (int64_t ks = 0; ks < nk; ++ks) {
-        const int cur = (int)(ks & 1);
-        const uint16_t* A = As + cur * SP_ABUF;
-        const uint16_t* B = Bs + cur * SP_BBUF;
-        const uint32_t* I = Is + cur * SP_BM * 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {  // two instructions of 32 dense k per stage
-            bf16x8_t af[4];
-            int ai[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wo + i * 32 + r32;
-                af[i] = *reinterpret_cast<const bf16x8_t*>(A + row * SP_AP + h * 16 + kg * 8);
-                ai[i] = (int)(I[row * 2 + h] >> (kg * 16));
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int tok = wt + j * 32 + r32;
-                const bf16x8_t lo = *reinterpret_cast<const bf16x8_t*>(B + tok * SP_BP + h * 32 + kg * 8);
-                const bf16x8_t hi = *reinterpret_cast<const bf16x8_t*>(B + tok * SP_BP + h * 32 + 16 + kg * 8);
-                const bf16x16_t bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(af[i], bf, acc[i][j], ai[i], 0, 0);
-            }
-        }
-        if (ks + 1 < nk) NM_SP_LSTORE(cur ^ 1);
-        if (ks + 2 < nk) NM_SP_GLOAD(ks + 2);
-        __syncthreads();
+    // the loop runs every stage but the last, the same instructions each time (no merge of paths
+    // with different LDS reads in flight, which would force a wait for all of them); the
+    // scheduling barriers keep each half stage's fragment reads ahead of the matrix instructions
+    // they overlap
+    // the epilogue's scalars are loaded before the loop: a scalar load still in flight at the
+    // loop head would make every wait there a wait for all LDS reads (scalar loads return out of
+    // order on the same counter)
+    int64_t ystride = a.ystride;
+    int32_t ytype = a.ytype;
+    void* yp = a.y;
+    asm volatile("" : "+s"(ystride), "+s"(ytype), "+s"(yp));
+    Frag f0, f1;
+    NM_SP_READ(f0, smem, 0);
+    int cur = 0;  // buffer of stage ks
+    for (int64_t ks = 0; ks + 1 < nk; ++ks) {
+        NM_SP_READ(f1, smem + cur * SP_STAGE, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        NM_SP_MMA(f0);
+        if (ks + 2 < nk)
+            asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (ks + 3 < nk) NM_SP_DMA(ks + 3, cur);
+        cur = cur == 2 ? 0 : cur + 1;
+        NM_SP_READ(f0, smem + cur * SP_STAGE, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        NM_SP_MMA(f1);
     }
-#undef NM_SP_GLOAD
-#undef NM_SP_LSTORE
+    NM_SP_READ(f1, smem + cur * SP_STAGE, 1);
+    NM_SP_MMA(f0);
+    NM_SP_MMA(f1);
+#undef NM_SP_READ
+#undef NM_SP_MMA
+#undef NM_SP_DMA
 
     // epilogue: element r of tile (i, j) is W row bo + wo + 32 i + 8 (r/4) + 4 (lane/32) + r%4 and
     // token bt + wt + 32 j + lane%32; four consecutive r are consecutive outputs of one Y row
@@ -164,25 +233,23 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
                 const int64_t o = bo + wo + i * 32 + q * 8 + kg * 4;  // out % 4 == 0: o..o+3 all in or out
                 if (o >= a.out) continue;
                 const f32x16_t v = acc[i][j];
-                if (a.ytype == 0) {
-                    *reinterpret_cast<float4*>(static_cast<float*>(a.y) + t * a.ystride + o) =
+                if (ytype == 0) {
+                    *reinterpret_cast<float4*>(static_cast<float*>(yp) + t * ystride + o) =
                         make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
                 } else {
                     const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q]) |
                                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 1]) << 16);
                     const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 2]) |
                                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 3]) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + t * a.ystride + o) = make_uint2(lo, hi);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(yp) + t * ystride + o) = make_uint2(lo, hi);
                 }
             }
         }
     }
 }
 
-constexpr size_t SP_SMEM = (2 * SP_ABUF + 2 * SP_BBUF) * sizeof(uint16_t) + 2 * SP_BM * 2 * sizeof(uint32_t);
-
 hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
-    // the block's LDS (116 KB) is above the default dynamic limit: allow it for this kernel
+    // the block's LDS (150 KB) is above the default dynamic limit: allow it for this kernel
     const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)SP_SMEM);
     if (e != hipSuccess) return e;
