@@ -935,19 +935,65 @@ __global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
         const uint2 d = reinterpret_cast<const uint2*>(vp)[0];
         v[0] = d.x & 0xFFFFu; v[1] = d.x >> 16; v[2] = d.y & 0xFFFFu; v[3] = d.y >> 16;
     }
-    uint32_t dense[U * M];
+    if constexpr (T::bytes == 2) {
+        // a group's four bf16 outputs form one 64-bit word: each kept value is shifted to its
+        // position, clearing what an earlier field put there (later field wins)
+        uint32_t w[2 * U];
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
+        for (int q = 0; q < U; ++q) {
+            uint64_t o = 0u;  // +0.0 where nothing is kept
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            uint32_t o = 0u;  // +0.0 where nothing is kept
-#pragma unroll
-            for (int tt = 0; tt < N; ++tt)
-                o = ((byte >> (2 * (q * N + tt))) & 3u) == (uint32_t)j ? v[q * N + tt] : o;  // later field wins
-            dense[q * M + j] = o;
+            for (int tt = 0; tt < N; ++tt) {
+                const uint32_t sh = 16u * ((byte >> (2 * (q * N + tt))) & 3u);
+                o = (o & ~(0xFFFFull << sh)) | ((uint64_t)v[q * N + tt] << sh);
+            }
+            w[2 * q] = (uint32_t)o;
+            w[2 * q + 1] = (uint32_t)(o >> 32);
         }
+        auto* dp = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.dense) + g0 * M);
+#pragma unroll
+        for (int i = 0; i < U / 2; ++i) nt_store(dp + i, make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]));
+    } else {
+        uint32_t dense[U * M];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                uint32_t o = 0u;  // +0.0 where nothing is kept
+#pragma unroll
+                for (int tt = 0; tt < N; ++tt)
+                    o = ((byte >> (2 * (q * N + tt))) & 3u) == (uint32_t)j ? v[q * N + tt] : o;  // later field wins
+                dense[q * M + j] = o;
+            }
+        }
+        store_raw<T, U * M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, U * M, dense);
     }
-    store_raw<T, U * M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, U * M, dense);
+}
+
+// 1:4 unpack with 16 bytes of dense output per thread (two bf16 groups or one fp32 group), so
+// that every store instruction writes one contiguous span: a whole index byte per thread (the
+// byte kernel's tiling) would give each thread 32 or 64 bytes in strided 16-byte pieces.  The
+// rows' 2-bit fields form one flat stream here (each row fills whole words), so group g's field
+// is bits 2g mod 8 of byte g / 4.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_unpack_1of4(UnpackArgs a) {
+    constexpr int G = 16 / (4 * T::bytes);  // groups per thread
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t g0 = t * G;
+    if (g0 >= a.rows * a.gpr) return;
+    const uint32_t byte = reinterpret_cast<const uint8_t*>(a.indices)[g0 >> 2];
+    const uint32_t f = byte >> (2 * (g0 & 3));  // field of group g0 + q at bits 2q
+    auto* dp = reinterpret_cast<uint4*>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * 4);
+    if constexpr (T::bytes == 2) {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(a.values)[t];  // the two kept values
+        const uint64_t o0 = (uint64_t)(v & 0xFFFFu) << (16u * (f & 3u));
+        const uint64_t o1 = (uint64_t)(v >> 16) << (16u * ((f >> 2) & 3u));
+        nt_store(dp, make_uint4((uint32_t)o0, (uint32_t)(o0 >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32)));
+    } else {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(a.values)[t];
+        const uint32_t p = f & 3u;
+        nt_store(dp, make_uint4(p == 0 ? v : 0u, p == 1 ? v : 0u, p == 2 ? v : 0u, p == 3 ? v : 0u));
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1085,7 +1131,14 @@ static hipError_t pack_nmt(PackArgs a, hipStream_t s) {
 }
 template <int N, int M, typename T>
 static hipError_t unpack_nmt(UnpackArgs a, hipStream_t s) {
-    if constexpr (M == 4 && (N == 1 || N == 2)) {
+    if constexpr (M == 4 && N == 1) {
+        if (byte_path<N, M>(a.gpr)) {
+            constexpr int G = 16 / (4 * T::bytes);
+            k_unpack_1of4<T><<<grid_for(a.rows * a.gpr / G), kThreads, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (M == 4 && N == 2) {
         if (byte_path<N, M>(a.gpr)) {
             k_unpack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
             return hipGetLastError();

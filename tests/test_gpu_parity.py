@@ -221,16 +221,20 @@ def _bits_t(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (3, 8)])
-def test_unpack_of_malformed_metadata_matches_oracle(n, m):
-    rows, gpr = 6, 19
+@pytest.mark.parametrize("n,m,gpr", [(2, 4, 19), (4, 8, 19), (3, 8, 19),
+                                     (2, 4, 64), (1, 4, 64)])   # gpr 64: one thread per index byte
+@pytest.mark.parametrize("wtype", [torch.bfloat16, torch.float32])
+def test_unpack_of_malformed_metadata_matches_oracle(n, m, gpr, wtype):
+    """Random index words: positions repeat within a group (the later field wins) and, for
+    m = 8, fall past the group (skipped)."""
+    rows = 6
     wpr = S.index_words_per_row(gpr * m, n, m)
     rng = np.random.default_rng(3)
     idx = rng.integers(0, 2**32, size=(rows, wpr), dtype=np.uint64).astype(np.uint32)
-    vals = nm_synth.normal((rows, gpr * n), 1.0, 8, torch.bfloat16)
+    vals = nm_synth.normal((rows, gpr * n), 1.0, 8, wtype)
     got = S.nm_unpack(vals.to(DEV), torch.from_numpy(idx.view(np.int32)).to(DEV), gpr * m, n, m)
     want = oracle.unpack(vals, idx, gpr * m, n, m)
-    np.testing.assert_array_equal(_bits(got), want.view(np.int16))
+    np.testing.assert_array_equal(_bits(got), want.view(np.int16 if wtype == torch.bfloat16 else np.int32))
 
 
 # ---------------------------------------------------------------------------------------------
