@@ -186,6 +186,31 @@ def test_config3_annealed_sweep_sampled(layer, step):
     torch.cuda.empty_cache()
 
 
+def _report_round_trip(layer, name, w, L, n, m, values, indices, hard, dense, keep):
+    """Say which output of a failed round trip is wrong: the pass repeated on the same inputs,
+    and the first mismatching rows against the oracle."""
+    rows, cols = w.shape
+    argmax = torch.argmax(L, dim=-1)
+    bad_hard = (hard.long() != argmax).nonzero()
+    want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
+    bad_dense = (_bits(dense) != want).nonzero()
+    _say("round trip failed:", "layer", layer, name, rows, cols,
+         "hard mismatches", bad_hard.shape[0], bad_hard[:4].tolist(),
+         "dense mismatches", bad_dense.shape[0], bad_dense[:4].tolist())
+    v2, i2, h2 = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+    d2 = S.nm_unpack(values, indices, cols, n, m)
+    _say("  repeat: values equal", torch.equal(_bits(v2), _bits(values)), "indices equal", torch.equal(i2, indices),
+         "hard equal", torch.equal(h2, hard), "unpack of the first pack equal", torch.equal(_bits(d2), _bits(dense)))
+    for r in sorted({int(x) for x in bad_dense[:4, 0].tolist()} | {int(x) for x in bad_hard[:4, 0].tolist()}):
+        rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
+        _say("  row", r, "values ok", np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16)),
+             "indices ok", np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri),
+             "hard ok", np.array_equal(hard[r:r + 1].cpu().numpy(), rh),
+             "unpack ok", np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(),
+                                         oracle.unpack(values[r:r + 1].cpu(), indices[r:r + 1].cpu().numpy().view(np.uint32),
+                                                       cols, n, m).view(np.int16)))
+
+
 def test_config4_nemotron15b_every_matrix_round_trip():
     n, m = 2, 4
     total = 0
@@ -196,12 +221,15 @@ def test_config4_nemotron15b_every_matrix_round_trip():
                                              with_grad=False, device=DEV)
             values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
             dense = S.nm_unpack(values, indices, cols, n, m)
+            # hard mask = first argmax of the logits
+            hard_ok = torch.equal(hard.long(), torch.argmax(L, dim=-1))
             keep = _keep_mask(hard, n, m)
             # round trip: exactly the selected weights survive, +0.0 elsewhere
-            assert torch.equal(_bits(dense), torch.where(keep, _bits(w), torch.zeros_like(_bits(w))))
+            trip_ok = torch.equal(_bits(dense), torch.where(keep, _bits(w), torch.zeros_like(_bits(w))))
+            if not (hard_ok and trip_ok):
+                _report_round_trip(layer, name, w, L, n, m, values, indices, hard, dense, keep)
+            assert hard_ok and trip_ok
             assert int(keep.view(-1, m).sum(1).min()) == n == int(keep.view(-1, m).sum(1).max())
-            # hard mask = first argmax of the logits
-            assert torch.equal(hard.long(), torch.argmax(L, dim=-1))
             if i in (0, 4):  # the oracle on sampled rows of a square and a rectangular matrix
                 for r in (0, rows - 1):
                     rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
