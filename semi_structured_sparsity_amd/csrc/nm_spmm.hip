@@ -248,7 +248,112 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     }
 }
 
+// Few tokens (a decode-sized batch): the 256 x 256 tiles above would leave most CUs idle, and
+// the product is bound by reading W once.  This path uses v_smfmac_f32_16x16x64_bf16, whose
+// operands were measured the same way as above (random integer operands, exact comparison):
+//   A (16 x 64 dense = 16 x 32 kept): lane L holds row L%16 and the 8 kept values of the dense
+//     groups 4*(L/16) .. 4*(L/16)+3; index bits [4g + 2u, 4g + 2u + 2) give the position of kept
+//     value u of the lane's group g (the upper 16 bits are not read);
+//   B (64 x 16): lane l holds column l%16; element e < 8 is k = 8*(l/16) + e, element e >= 8 is
+//     k = 32 + 8*(l/16) + e - 8;
+//   D (16 x 16): lane l, element r is row 4*(l/16) + r, column l%16.
+// A block owns 16 W rows x 16 J tokens; its waves split k (wave w takes the 64-k blocks w,
+// w + WAVES, ...) and load their fragments straight from memory into registers, U blocks ahead
+// (the packed rows feed the instruction as laid out; X, small, comes from L2).  The block then
+// sums the waves' partial tiles in LDS in a fixed order, so the result is deterministic.
+template <int J, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_spmm24_skinny(SpmmArgs a) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int THREADS = 64 * WAVES;
+    __shared__ float part[WAVES * J * 4 * 64];  // the waves' partial tiles
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t bo = (int64_t)blockIdx.x * 16, bt = (int64_t)blockIdx.y * 16 * J;
+    const int64_t olast = a.out - 1, tlast = a.tokens - 1;
+    const int64_t orow = bo + r16 < olast ? bo + r16 : olast;  // rows past the end: the last row
+    const uint16_t* va = a.values + orow * a.vstride + q * 8;    // + 32 per 64-k block
+    const uint32_t* ia = a.indices + orow * a.istride + (q >> 1);  // + 2 words per 64-k block
+    const int ish = 16 * (q & 1);
+    const uint16_t* xb[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t t = bt + 16 * j + r16;
+        xb[j] = a.x + (t < tlast ? t : tlast) * a.xstride + q * 8;  // + 64 per 64-k block
+    }
+    f32x4_t acc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int64_t nkb = a.in / 64;
+    for (int64_t kb0 = wv; kb0 < nkb; kb0 += U * WAVES) {
+        bf16x8_t av[U], lo[U][J], hi[U][J];
+        uint32_t iv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kb = kb0 + u * WAVES;
+            if (kb < nkb) {
+                av[u] = *reinterpret_cast<const bf16x8_t*>(va + kb * 32);
+                iv[u] = ia[kb * 2];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    lo[u][j] = *reinterpret_cast<const bf16x8_t*>(xb[j] + kb * 64);
+                    hi[u][j] = *reinterpret_cast<const bf16x8_t*>(xb[j] + kb * 64 + 32);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kb0 + u * WAVES < nkb) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const bf16x16_t bf = __builtin_shufflevector(lo[u][j], hi[u][j], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10,
+                                                                 11, 12, 13, 14, 15);
+                    acc[j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(av[u], bf, acc[j], (int)(iv[u] >> ish), 0, 0);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[((wv * J + j) * 4 + r) * 64 + lane] = acc[j][r];
+    __syncthreads();
+    // output (token bt + tl, row bo + ol), rows fastest so that consecutive threads store
+    // consecutive outputs; element r of lane l holds row 4 (l/16) + r, token l%16
+    for (int e = tid; e < 16 * 16 * J; e += THREADS) {
+        const int ol = e & 15, tl = e >> 4, j = tl >> 4;
+        const int l = (tl & 15) + 16 * (ol >> 2), r = ol & 3;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) sum += part[((w * J + j) * 4 + r) * 64 + l];
+        const int64_t t = bt + tl, o = bo + ol;
+        if (t < a.tokens && o < a.out) {
+            if (a.ytype == 0)
+                static_cast<float*>(a.y)[t * a.ystride + o] = sum;
+            else
+                static_cast<__bf16*>(a.y)[t * a.ystride + o] = (__bf16)sum;
+        }
+    }
+}
+
+// Up to this many tokens the skinny kernel runs; above it the 256 x 256 tiles.
+constexpr int64_t SP_SKINNY_MAX_TOKENS = 128;
+
 hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
+    if (a.tokens <= SP_SKINNY_MAX_TOKENS) {
+        const unsigned gx = (unsigned)((a.out + 15) / 16);
+        if (a.tokens <= 16) {
+            k_spmm24_skinny<1, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
+        } else if (a.tokens <= 32) {
+            k_spmm24_skinny<2, 8, 2><<<dim3(gx, 1), 512, 0, s>>>(a);
+        } else if (a.tokens <= 64) {
+            k_spmm24_skinny<4, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
+        } else {
+            k_spmm24_skinny<8, 8, 2><<<dim3(gx, (unsigned)((a.tokens + 127) / 128)), 512, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
     // the block's LDS (150 KB) is above the default dynamic limit: allow it for this kernel
     const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)SP_SMEM);

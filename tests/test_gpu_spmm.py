@@ -105,6 +105,40 @@ def test_sparse_matmul_partial_tiles(out, inn, tokens, ytype):
     assert bool(buf[tokens * out:].isnan().all())
 
 
+@pytest.mark.parametrize("out,inn,tokens", [(36, 64, 1), (100, 128, 7), (256, 4160, 32), (68, 192, 33),
+                                             (132, 256, 64), (64, 320, 65), (96, 1024, 128), (4, 64, 128)])
+@pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
+def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
+    """Up to 128 tokens the product runs on blocks of 32 W rows whose waves split k (fewer
+    k blocks than waves included); every output against the oracle, nothing written past y."""
+    _say("spmm few tokens", out, inn, tokens, ytype)
+    _, values, indices = _packed_layer(out, inn, 60 + out + tokens, w_std=1.0)
+    x = nm_synth.normal((tokens, inn), 1.0, 61, torch.bfloat16, device=DEV)
+    buf = torch.full((tokens * out + 4096,), float("nan"), dtype=ytype, device=DEV)
+    y = buf[:tokens * out].view(tokens, out)
+    S.nm_sparse_matmul(values, indices, x, out_dtype=ytype, out=y)
+    ratio, bad = _check(values, indices, x, y, bf16_out=ytype == torch.bfloat16)
+    _say("  err/bound", ratio)
+    assert bad == 0
+    assert bool(buf[tokens * out:].isnan().all())
+    # deterministic: the waves' partial tiles are summed in a fixed order
+    assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=ytype), y)
+
+
+@pytest.mark.parametrize("name_index,tokens", [(4, 1), (6, 16), (0, 128)])
+def test_sparse_matmul_llama7b_decode_batches(name_index, tokens):
+    """Decode-sized batches on full LLaMA-7B-shaped weights, three windows of 128 W rows."""
+    name, out, inn = nm_synth.LLAMA2_7B_LAYER[name_index]
+    _say("spmm decode", name, out, inn, tokens)
+    _, values, indices = _packed_layer(out, inn, nm_synth.input_seed(2, 0, name_index))
+    x = nm_synth.normal((tokens, inn), 1.0, 62, torch.bfloat16, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32)
+    for rb in (0, out // 2 + 64, out - 128):
+        ratio, bad = _check(values, indices, x, y, rows=128, row_begin=rb)
+        _say("  rows", rb, "err/bound", ratio)
+        assert bad == 0
+
+
 def test_sparse_matmul_rejects_unsupported_shapes():
     _, values, indices = _packed_layer(256, 64, 45)
     x = torch.zeros((128, 64), dtype=torch.bfloat16, device=DEV)
