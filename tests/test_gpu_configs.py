@@ -75,10 +75,35 @@ def _check_pack_full(w, L, n, m):
     assert np.array_equal(hard.cpu().numpy(), rh)
     assert np.array_equal(indices.cpu().numpy().view(np.uint32), ri)
     assert np.array_equal(_bits(values).cpu().numpy(), rv.view(_bits(values).cpu().numpy().dtype))
+    # the copied-back dense weights against the oracle's unpack, and the selection on the GPU
+    rd = oracle.unpack(rv, ri, w.shape[1], n, m)
+    dense_ok = np.array_equal(_bits(dense).cpu().numpy(), rd.view(_bits(dense).cpu().numpy().dtype))
     keep = _keep_mask(hard, n, m)
     want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
-    assert torch.equal(_bits(dense), want)
+    select_ok = torch.equal(_bits(dense), want)
+    if not (dense_ok and select_ok):
+        _report_unpack(w, n, m, values, indices, dense, rd, want)
+    assert dense_ok and select_ok
     return values, indices, hard, dense
+
+
+def _report_unpack(w, n, m, values, indices, dense, rd, want):
+    """Say where an unpack disagrees: the copied-back output against the oracle, the same output
+    against the selection computed on the GPU, a second copy of the output, and a repeated unpack
+    of the same packed inputs into a fresh buffer."""
+    cols = w.shape[1]
+    it = np.int16 if w.dtype == torch.bfloat16 else np.int32
+    got = _bits(dense).cpu().numpy()
+    ref = rd.view(it)
+    bad = np.argwhere(got != ref)
+    _say("unpack mismatch vs oracle:", bad.shape[0], "elements; first",
+         [(int(r), int(c), int(got[r, c]), int(ref[r, c])) for r, c in bad[:8]])
+    bad_gpu = (_bits(dense) != want).nonzero()
+    _say("  vs selection on the GPU:", bad_gpu.shape[0], "elements; first", bad_gpu[:8].tolist())
+    again = _bits(dense).cpu().numpy()
+    _say("  second copy of the output equals the first:", bool(np.array_equal(again, got)))
+    d2 = S.nm_unpack(values, indices, cols, n, m)
+    _say("  repeated unpack equals the oracle:", bool(np.array_equal(_bits(d2).cpu().numpy(), ref)))
 
 
 def _keep_mask(hard, n, m):
