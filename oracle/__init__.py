@@ -46,6 +46,7 @@ def lib():
             "ref_soft_mask": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, i32]),
             "ref_forward": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, P, i32]),
             "ref_backward": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, P, P, i32]),
+            "ref_backward_wreg": (i32, [P, dbl, dbl, u64, u64, dbl, i64, i64, P, P, P, P, i32]),
             "ref_probs": (i32, [P, dbl, dbl, u64, u64, i64, i64, P, P, i32]),
             "ref_index_words_per_row": (i64, [P]),
             "ref_harden": (i32, [P, i64, i64, P, P, i32]),
@@ -237,6 +238,30 @@ def backward(w, logits, grad, n, m, kappa, tau, seed, offset, rows=None, row_beg
                             _window(wr, row_begin, rows), _ptr(W), _ptr(L), _ptr(G), _ptr(out),
                             nthreads)
     _check(rc, "backward")
+    return out
+
+
+def backward_wreg(w, logits, grad, n, m, kappa, tau, seed, offset, lam, rows=None, row_begin=0,
+                  nthreads=0):
+    """float64 logit gradient [window_rows, cols/m, K] of the task loss (upstream grad, or None
+    for none) plus lam * sum (w * soft_mask)^2 (MaskLLM project page, Table 3: weight
+    regularisation; the squared norm of the masked weights is a reading, the page gives no
+    formula)."""
+    W = _contig(w)
+    L = _contig(logits, np.float32)
+    G = None
+    if grad is not None:
+        G = _contig(grad)
+        if G.dtype != W.dtype or G.shape != W.shape:
+            raise TypeError("grad must match w in shape and type")
+    wr, cols = W.shape
+    rows = wr if rows is None else rows
+    out = _unwritten(L.shape, np.float64)
+    s = _shape(rows, cols, n, m, _wtype_of(W))
+    rc = lib().ref_backward_wreg(ctypes.byref(s), kappa, tau, seed, offset, float(lam), row_begin,
+                                 _window(wr, row_begin, rows), _ptr(W), _ptr(L),
+                                 None if G is None else _ptr(G), _ptr(out), nthreads)
+    _check(rc, "backward_wreg")
     return out
 
 

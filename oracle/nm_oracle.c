@@ -215,6 +215,7 @@ struct job {
     int64_t tokens;  /* sparse product: rows of X */
     int64_t ystride; /* sparse product: row stride of Y (the window's W rows) */
     int32_t xtype;   /* sparse product: element type of X */
+    double lambda;   /* regularised backward: weight of sum (w_masked)^2 in the loss */
     row_fn fn;
 };
 
@@ -380,11 +381,24 @@ int32_t ref_probs(const ref_shape *shape, double kappa, double tau, uint64_t see
  *     softmax:  dL/dz_k = y_k (d_k - s),  s = sum_i y_i d_i,
  *     dz_k/dl_k = kappa / tau,
  * and the weights get no gradient (they are frozen). */
+/* From a_j = dL/dm_j of one group to its logit gradient. */
+static void group_backward(const group_ctx *c, const double *y, const double *a, double *out) {
+    double d[MAX_K];
+    double sdot = 0.0;
+    for (int32_t k = 0; k < c->K; ++k) {
+        d[k] = 0.0;
+        for (int32_t j = 0; j < c->m; ++j)
+            if (c->cand[k] >> j & 1u) d[k] += a[j];
+        sdot += y[k] * d[k];
+    }
+    for (int32_t k = 0; k < c->K; ++k) out[k] = (c->kappa / c->tau) * y[k] * (d[k] - sdot);
+}
+
 static void row_backward(const job *jb, int64_t r) {
     const ref_shape *s = jb->s;
     const group_ctx *c = &jb->ctx;
     int64_t gpr = s->cols / s->m;
-    double y[MAX_K], a[MAX_M], d[MAX_K];
+    double y[MAX_K], a[MAX_M];
     for (int64_t q = 0; q < gpr; ++q) {
         int64_t g = r * gpr + q;
         int64_t local = (r - jb->rb) * gpr + q;
@@ -392,15 +406,7 @@ static void row_backward(const job *jb, int64_t r) {
         int64_t base = (r - jb->rb) * s->cols + q * s->m;
         for (int32_t j = 0; j < s->m; ++j)
             a[j] = load_w(jb->grad, s->wtype, base + j) * load_w(jb->w, s->wtype, base + j);
-        double sdot = 0.0;
-        for (int32_t k = 0; k < c->K; ++k) {
-            d[k] = 0.0;
-            for (int32_t j = 0; j < s->m; ++j)
-                if (c->cand[k] >> j & 1u) d[k] += a[j];
-            sdot += y[k] * d[k];
-        }
-        double *out = (double *)jb->out + local * c->K;
-        for (int32_t k = 0; k < c->K; ++k) out[k] = (c->kappa / c->tau) * y[k] * (d[k] - sdot);
+        group_backward(c, y, a, (double *)jb->out + local * c->K);
     }
 }
 
@@ -419,6 +425,56 @@ int32_t ref_backward(const ref_shape *shape, double kappa, double tau, uint64_t 
     jb.grad = grad;
     jb.out = dlogits;
     jb.fn = row_backward;
+    run_rows(&jb, row_begin, row_end, nthreads);
+    return 0;
+}
+
+/* Backward with a weight regulariser in the loss (MaskLLM project page, Table 3: weight
+ * regularisation helps mask learning).  The page states no formula; the reading here is the
+ * squared norm of the masked weights, R = lambda * sum_j (w_j m_j)^2, whose gradient with
+ * respect to w_masked_j is 2 lambda w_j m_j.  The loss is then the caller's task loss (upstream
+ * gradient G, or none) plus R, and dL/dm_j = (G_j + 2 lambda w_j m_j) w_j; from there the
+ * chain through the softmax is the one of the plain backward.  A negative lambda rewards large
+ * kept weights, a positive one penalises them. */
+static void row_backward_wreg(const job *jb, int64_t r) {
+    const ref_shape *s = jb->s;
+    const group_ctx *c = &jb->ctx;
+    int64_t gpr = s->cols / s->m;
+    double y[MAX_K], mask[MAX_M], a[MAX_M];
+    for (int64_t q = 0; q < gpr; ++q) {
+        int64_t g = r * gpr + q;
+        int64_t local = (r - jb->rb) * gpr + q;
+        group_probs(c, g, jb->logits + local * c->K, y);
+        group_soft_mask(c, y, mask);
+        int64_t base = (r - jb->rb) * s->cols + q * s->m;
+        for (int32_t j = 0; j < s->m; ++j) {
+            double wj = load_w(jb->w, s->wtype, base + j);
+            double gj = jb->grad ? load_w(jb->grad, s->wtype, base + j) : 0.0;
+            double up = gj + 2.0 * jb->lambda * wj * mask[j]; /* dL/dw_masked_j */
+            a[j] = up * wj;                                   /* dL/dm_j */
+        }
+        group_backward(c, y, a, (double *)jb->out + local * c->K);
+    }
+}
+
+int32_t ref_backward_wreg(const ref_shape *shape, double kappa, double tau, uint64_t seed,
+                          uint64_t offset, double lambda, int64_t row_begin, int64_t row_end,
+                          const void *w, const float *logits, const void *grad, double *dlogits,
+                          int32_t nthreads) {
+    job jb;
+    memset(&jb, 0, sizeof jb);
+    if (!window_ok(shape, row_begin, row_end) || !init_ctx(&jb.ctx, shape, kappa, tau, seed, offset))
+        return -1;
+    if (!isfinite(lambda)) return -1;
+    if (row_end > row_begin && (!w || !logits || !dlogits)) return -1;
+    jb.s = shape;
+    jb.rb = row_begin;
+    jb.w = w;
+    jb.logits = logits;
+    jb.grad = grad; /* NULL: no task loss, the regulariser alone */
+    jb.lambda = lambda;
+    jb.out = dlogits;
+    jb.fn = row_backward_wreg;
     run_rows(&jb, row_begin, row_end, nthreads);
     return 0;
 }

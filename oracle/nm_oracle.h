@@ -96,6 +96,12 @@ int32_t ref_forward(const ref_shape *shape, double kappa, double tau, uint64_t s
 int32_t ref_backward(const ref_shape *shape, double kappa, double tau, uint64_t seed,
                      uint64_t offset, int64_t row_begin, int64_t row_end, const void *w,
                      const float *logits, const void *grad, double *dlogits, int32_t nthreads);
+/* dlogits of the task loss (upstream grad, may be NULL for none) plus the weight regulariser
+ * lambda * sum (w * soft_mask)^2: the upstream gradient becomes grad + 2 lambda w_masked. */
+int32_t ref_backward_wreg(const ref_shape *shape, double kappa, double tau, uint64_t seed,
+                          uint64_t offset, double lambda, int64_t row_begin, int64_t row_end,
+                          const void *w, const float *logits, const void *grad, double *dlogits,
+                          int32_t nthreads);
 /* Per-group probabilities y [groups, K] (a by-product of the soft mask, used for statistics). */
 int32_t ref_probs(const ref_shape *shape, double kappa, double tau, uint64_t seed,
                   uint64_t offset, int64_t row_begin, int64_t row_end, const float *logits,

@@ -17,7 +17,8 @@ from oracle import build as oracle_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_noise.py", "tests/test_oracle_layer.py", "tests/test_oracle_pack.py",
-        "tests/test_oracle_monitor.py", "tests/test_oracle_matmul.py", "tests/test_oracle_properties.py"]
+        "tests/test_oracle_monitor.py", "tests/test_oracle_matmul.py", "tests/test_oracle_properties.py",
+        "tests/test_oracle_wreg.py"]
 
 MUTANTS = {
     "philox_swaps_hi_and_lo": ("uint32_t n0 = hi1 ^ x1 ^ k0;", "uint32_t n0 = lo1 ^ x1 ^ k0;"),
@@ -41,6 +42,12 @@ MUTANTS = {
                                 "a[j] = load_w(jb->grad, s->wtype, base + j);"),
     "backward_inverse_scale": ("(c->kappa / c->tau) * y[k]", "(c->tau / c->kappa) * y[k]"),
     "backward_drops_softmax_centre": ("sdot += y[k] * d[k];", ""),
+    "wreg_drops_factor_two": ("double up = gj + 2.0 * jb->lambda * wj * mask[j];",
+                              "double up = gj + jb->lambda * wj * mask[j];"),
+    "wreg_unmasked_weight": ("double up = gj + 2.0 * jb->lambda * wj * mask[j];",
+                             "double up = gj + 2.0 * jb->lambda * wj;"),
+    "wreg_sign": ("double up = gj + 2.0 * jb->lambda", "double up = gj - 2.0 * jb->lambda"),
+    "wreg_missing_outer_weight": ("a[j] = up * wj;", "a[j] = up;"),
     "harden_last_max": ("if (l[k] > l[best]) best = k;", "if (l[k] >= l[best]) best = k;"),
     "pack_field_stride": ("put_bits(idx, (q * s->n + t) * nb, (uint32_t)j, nb);",
                           "put_bits(idx, (q * s->m + t) * nb, (uint32_t)j, nb);"),
