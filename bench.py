@@ -43,13 +43,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama7b_layer",
                    choices=["llama7b_layer", "sweep32", "general_nm", "nemotron_pack", "single256",
-                            "prior_init", "monitor", "spmm"],
+                            "prior_init", "monitor", "spmm", "wreg"],
                    help="llama7b_layer (default): one LLaMA-2-7B-shaped layer per step; sweep32: 32 such "
                         "layers x 10 annealed steps of fwd+bwd+pack; general_nm: 4096x11008 with 1:4, 2:8, "
                         "4:8; nemotron_pack: pack+unpack of every Nemotron-15B-shaped matrix; single256: "
                         "one 256x256 fp32 weight (latency-bound); prior_init: magnitude-prior "
                         "logit initialisation; monitor: forward with the fused Fig. 5 monitors; spmm: "
-                        "sparse x dense product on the packed weights")
+                        "sparse x dense product on the packed weights; wreg: backward with the fused "
+                        "weight regulariser")
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -172,18 +173,18 @@ def copy_ceiling(dev, reps=10):
 # ---------------------------------------------------------------------------------------------
 # rocprofv3 summaries (run on the CSV output of the commands printed in profiles/)
 
-KERNELS = {"fwd": "k_forward<2, 4, nm::BF16, 0>", "bwd": "k_backward<2, 4, nm::BF16>",
+KERNELS = {"fwd": "k_forward<2, 4, nm::BF16, 0>", "bwd": "k_backward<2, 4, nm::BF16, 0>",
            "harden_pack": "k_pack_bytes<2, nm::BF16>", "unpack": "k_unpack_bytes<2, nm::BF16>"}
 COPY_BYTES = 1 << 30  # the --copy-calibration copies
 
 
 def kernel_source_hash():
-    """Hash of the sources of the path's kernels (nm_kernels.hip and the device header it
-    includes), so stored counter readings can be matched to the kernels they were taken on."""
+    """Hash of the sources of the path's kernels (their translation units and the device headers
+    they include), so stored counter readings can be matched to the kernels they were taken on."""
     import hashlib
     import semi_structured_sparsity_amd.build as b
     h = hashlib.sha256()
-    for name in ("nm_kernels.hip", "nm_device.hpp"):
+    for name in ("nm_forward.hip", "nm_backward.hip", "nm_pack.hip", "nm_layer.hpp", "nm_device.hpp"):
         h.update(open(os.path.join(b.CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -483,6 +484,62 @@ def workload_monitor(args):
             "results": res, "monitor_means_last_call": [[round(a, 6), round(b, 6)] for a, b in means]}
 
 
+WREG_LAMBDA = -0.05
+
+
+def workload_wreg(args):
+    """Backward of one LLaMA-7B-shaped layer (2:4, kappa 100, tau 4, prior logits) with the fused
+    weight regulariser lambda*sum(w_masked^2), next to the plain backward and to the unfused way
+    of getting the same gradient (a torch pass forming G + 2*lambda*w_masked from the forward's
+    output, then the plain backward).  Algorithmic bytes: the fused pass moves what the plain
+    backward moves (16 B per weight; 14 without a task gradient, which is then not read)."""
+    import torch
+
+    import nm_synth
+    import semi_structured_sparsity_amd as S
+    dev = torch.device("cuda:0")
+    mats = make_layer(dev)
+    for mt in mats:
+        run_pass(S, mt, "fwd", 0)
+        mt["G2"] = torch.empty_like(mt["G"])
+    weights = nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
+
+    def plain(r):
+        for mt in mats:
+            run_pass(S, mt, "bwd", 0)
+
+    def fused(r):
+        for mt in mats:
+            S.nm_mask_backward_wreg(mt["w"], mt["L"], mt["G"], N, M, KAPPA, TAU, mt["seed"], 0, WREG_LAMBDA,
+                                    out=mt["dl"])
+
+    def alone(r):
+        for mt in mats:
+            S.nm_mask_backward_wreg(mt["w"], mt["L"], None, N, M, KAPPA, TAU, mt["seed"], 0, WREG_LAMBDA,
+                                    out=mt["dl"])
+
+    def unfused(r):
+        for mt in mats:
+            torch.add(mt["G"], mt["out"], alpha=2 * WREG_LAMBDA, out=mt["G2"])
+            S.nm_mask_backward(mt["w"], mt["L"], mt["G2"], N, M, KAPPA, TAU, mt["seed"], 0, out=mt["dl"])
+
+    bpw = bytes_per_weight()["bwd"]
+    res = {}
+    for label, fn, b in (("bwd", plain, bpw), ("bwd+wreg fused", fused, bpw),
+                         ("wreg alone", alone, bpw - WB), ("bwd+wreg unfused (torch add + bwd)", unfused, bpw)):
+        t = _elapsed_ms(fn, reps=args.kernel_reps)
+        gbps = b * weights / (t * 1e-3) / 1e9
+        res[label] = {"ms_per_pass": round(t, 4), "avg_call_us": round(t * 1e3 / len(mats), 2),
+                      "bytes_per_weight": b, "GBps": round(gbps, 1),
+                      "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+    res["fused_speedup_over_unfused"] = round(res["bwd+wreg unfused (torch add + bwd)"]["ms_per_pass"]
+                                              / res["bwd+wreg fused"]["ms_per_pass"], 3)
+    return {"metric": "backward with the fused weight regulariser vs plain and unfused", "unit": "GB/s",
+            "config": {"workload": "LLaMA-2-7B-shaped decoder layer, 7 matrices, 202,375,168 bf16 weights, "
+                                   f"2:4, kappa=100, tau=4, prior logits, lambda={WREG_LAMBDA}"},
+            "results": res}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity factor)
 
 
@@ -607,7 +664,7 @@ def main():
         fn = {"sweep32": workload_sweep32, "general_nm": workload_general_nm,
               "nemotron_pack": workload_nemotron_pack, "single256": workload_single256,
               "prior_init": workload_prior_init, "monitor": workload_monitor,
-              "spmm": workload_spmm}[args.workload]
+              "spmm": workload_spmm, "wreg": workload_wreg}[args.workload]
         out = fn(args)
         out.update({"n_gpus": 1, "data": "synthetic, seeded, generated on the GPU", "dtype": "f32"})
         print(json.dumps(out), flush=True)

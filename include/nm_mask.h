@@ -136,6 +136,20 @@ nm_status nm_mask_backward(const nm_shape *shape, const nm_sample *sample, const
                            const float *logits, const void *grad_w_masked, float *grad_logits,
                            void *stream);
 
+/* Backward with a weight regulariser in the loss (MaskLLM project page, Table 3: weight
+ * regularisation helps mask learning).  The page gives no formula; this entry point takes it as
+ * R = lambda * sum_j (w_j m_j)^2 over the masked weights, added to the caller's task loss.  The
+ * gradient of R on w_masked is 2 lambda w_masked, so the result is nm_mask_backward's with the
+ * upstream gradient G_j + 2 lambda w_j m_j, m the step's soft mask (regenerated here, as the
+ * noise is).  It saves the caller a pass that would read w_masked and G and write G + 2 lambda
+ * w_masked.  A negative lambda rewards large kept weights, a positive one penalises them.
+ *   lambda         finite (NM_EINVAL otherwise); 0 gives the plain backward up to signed zeros
+ *   grad_w_masked  [rows, cols] wtype, read; may be NULL: the regulariser alone (no task loss)
+ *   w, logits, grad_logits, errors  as nm_mask_backward */
+nm_status nm_mask_backward_wreg(const nm_shape *shape, const nm_sample *sample, float lambda,
+                                const void *w, const float *logits, const void *grad_w_masked,
+                                float *grad_logits, void *stream);
+
 /* Hard mask and compressed storage ("Accelerating Sparse Deep Neural Networks" summary page,
  * section 3.1).  Per group: k* = first argmax of its logits; the kept weights of candidate k*
  * go to `values` and their positions to `indices` (layout above).

@@ -9,13 +9,16 @@ or if a tensor is not on a ROCm device.
 Entry points, named as in the C ABI:
     nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset)        -> w_masked
     nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset) -> grad_logits
+    nm_mask_backward_wreg(w, logits, grad_or_None, n, m, kappa, tau, seed, offset, lam)
+                                                                      -> grad_logits
     nm_mask_harden_pack(w, logits, n, m, with_hard=False)             -> values, indices[, hard]
     nm_unpack(values, indices, cols, n, m)                            -> w_dense
     nm_prior_init(w, n, m, alpha, with_idx=False)                     -> logits[, prior_idx]
     nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None)
                                                                       -> w_masked, sample, stats
-and `mask(...)`, the autograd function whose backward is nm_mask_backward (the weights are frozen
-and get no gradient).
+and `mask(...)`, the autograd function whose backward is nm_mask_backward, or
+nm_mask_backward_wreg when a weight-regulariser strength is given (the weights are frozen and get
+no gradient).
 """
 import ctypes
 import os
@@ -52,6 +55,7 @@ _P = ctypes.c_void_p
 _SIGNATURES = {
     "nm_mask_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     "nm_mask_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "nm_mask_backward_wreg": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P]),
     "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
@@ -225,6 +229,23 @@ def nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset, out=None):
     return out
 
 
+def nm_mask_backward_wreg(w, logits, grad, n, m, kappa, tau, seed, offset, lam, out=None):
+    """Logit gradient of the task loss (upstream `grad`, or None for none) plus the weight
+    regulariser lam * sum (w * m)^2 (MaskLLM project page, Table 3; the squared norm of the
+    masked weights is the reading taken, the page gives no formula)."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    lshape = _logit_shape(rows, cols, n, m)
+    out = torch.empty(lshape, dtype=torch.float32, device=w.device) if out is None else out
+    st = lib().nm_mask_backward_wreg(
+        ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)), float(lam), _dev(w, "w"),
+        _dev(logits, "logits", torch.float32, lshape),
+        None if grad is None else _dev(grad, "grad", w.dtype, w.shape),
+        _dev(out, "out", torch.float32, lshape), _stream(w.device))
+    _check(st, "nm_mask_backward_wreg")
+    return out
+
+
 def nm_mask_harden_pack(w, logits, n, m, with_hard=False, out=None):
     """Hard argmax mask packed as (values, indices[, hard]) ("Accelerating Sparse Deep Neural
     Networks" summary page, section 3.1)."""
@@ -354,25 +375,31 @@ def nm_debug_soft_mask(logits, n, m, kappa, tau, seed, offset):
 # autograd
 
 class NMMask(torch.autograd.Function):
-    """w_masked = w * softmask(logits); gradient to the logits only (frozen weights)."""
+    """w_masked = w * softmask(logits); gradient to the logits only (frozen weights).  With
+    wreg != 0 the gradient also carries the regulariser wreg * sum(w_masked^2), which the caller
+    then leaves out of its own loss."""
 
     @staticmethod
-    def forward(ctx, w, logits, n, m, kappa, tau, seed, offset):
+    def forward(ctx, w, logits, n, m, kappa, tau, seed, offset, wreg=0.0):
         ctx.save_for_backward(w, logits)
-        ctx.params = (n, m, kappa, tau, seed, offset)
+        ctx.params = (n, m, kappa, tau, seed, offset, wreg)
         return nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset)
 
     @staticmethod
     def backward(ctx, grad):
         w, logits = ctx.saved_tensors
-        n, m, kappa, tau, seed, offset = ctx.params
-        dl = nm_mask_backward(w, logits, grad.contiguous(), n, m, kappa, tau, seed, offset)
-        return None, dl, None, None, None, None, None, None
+        n, m, kappa, tau, seed, offset, wreg = ctx.params
+        if wreg != 0.0:
+            dl = nm_mask_backward_wreg(w, logits, grad.contiguous(), n, m, kappa, tau, seed, offset, wreg)
+        else:
+            dl = nm_mask_backward(w, logits, grad.contiguous(), n, m, kappa, tau, seed, offset)
+        return None, dl, None, None, None, None, None, None, None
 
 
-def mask(w, logits, n, m, kappa, tau, seed, offset):
-    """Differentiable N:M mask layer; `offset` is the training step (fresh noise per step)."""
-    return NMMask.apply(w, logits, n, m, kappa, tau, seed, offset)
+def mask(w, logits, n, m, kappa, tau, seed, offset, wreg=0.0):
+    """Differentiable N:M mask layer; `offset` is the training step (fresh noise per step).
+    `wreg` adds the gradient of wreg * sum(w_masked^2) in the backward (fused: no extra pass)."""
+    return NMMask.apply(w, logits, n, m, kappa, tau, seed, offset, wreg)
 
 
 def packed_bytes(rows, cols, n, m, elem_bytes):
@@ -380,7 +407,7 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
     return rows * cols // m * n * elem_bytes + rows * index_words_per_row(cols, n, m) * 4
 
 
-__all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_harden_pack", "nm_unpack",
+__all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_backward_wreg", "nm_mask_harden_pack", "nm_unpack",
            "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise",
            "nm_debug_copy", "nm_sparse_matmul", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",

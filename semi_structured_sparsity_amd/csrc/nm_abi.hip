@@ -192,6 +192,26 @@ nm_status nm_mask_backward(const nm_shape* shape, const nm_sample* sample, const
     return launched(nm::launch_backward(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
+nm_status nm_mask_backward_wreg(const nm_shape* shape, const nm_sample* sample, float lambda,
+                                const void* w, const float* logits, const void* grad_w_masked,
+                                float* grad_logits, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    const float lam2 = 2.0f * lambda;
+    if (!isfinite(lambda) || !isfinite(lam2)) return NM_EINVAL;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !grad_logits) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(grad_logits) ||
+        (grad_w_masked && !aligned16(grad_w_masked)))
+        return NM_EALIGN;
+    nm::BwdArgs a{w, logits, grad_w_masked, grad_logits, groups, A, B, C, noise_key(sample), lam2};
+    return launched(nm::launch_backward_wreg(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
 nm_status nm_mask_harden_pack(const nm_shape* shape, const void* w, const float* logits, void* values,
                               uint32_t* indices, uint8_t* hard_idx, void* stream) {
     int64_t groups;

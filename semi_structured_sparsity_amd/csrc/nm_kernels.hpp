@@ -33,11 +33,12 @@ struct MonitorArgs {
 struct BwdArgs {
     const void* w;
     const float* logits;
-    const void* grad;
+    const void* grad;    // null: regulariser only (launch_backward_wreg)
     float* dlogits;
     int64_t groups;
     float A, B, C;       // C = kappa/tau
     NoiseKey nk;
+    float lam2;          // 2 * lambda of the weight regulariser (launch_backward_wreg only)
 };
 
 struct PackArgs {
@@ -95,6 +96,7 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s);
 
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_mask, hipStream_t s);
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
+hipError_t launch_backward_wreg(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
 hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a, hipStream_t s);

@@ -1,0 +1,461 @@
+// nm_layer.hpp -- device code shared by the kernels of the N:M mask layer (internal).
+//
+// Every kernel is a single coalesced pass over HBM with one tile per thread and a flat grid
+// (no grid-stride loop): the layer is bandwidth-bound and independent per group, nothing is
+// contracted, so there is no MFMA work.  Noise is regenerated in registers from a counter-based
+// generator in both passes and is never stored.  The kernels live in nm_forward.hip (forward,
+// monitored forward, magnitude prior), nm_backward.hip and nm_pack.hip (hard mask, pack,
+// unpack, diagnostics); each translation unit instantiates only what its launchers use.
+#pragma once
+#include "nm_device.hpp"
+#include "nm_kernels.hpp"
+
+namespace nm {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------------------------------------
+// Loads of logits / stores of logit gradients: CNT floats, 16- or 8-byte vectors.
+
+template <int CNT, int ALIGN>
+__device__ __forceinline__ void load_f32(const float* __restrict__ p, bool vec, int valid, float (&out)[CNT]) {
+    if (vec) {
+        if constexpr (ALIGN == 16 && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i) {
+                const uint4 v = nt_load4(reinterpret_cast<const float4*>(p) + i);
+                out[4 * i] = __uint_as_float(v.x); out[4 * i + 1] = __uint_as_float(v.y);
+                out[4 * i + 2] = __uint_as_float(v.z); out[4 * i + 3] = __uint_as_float(v.w);
+            }
+        } else {
+            static_assert(CNT % 2 == 0, "even count");
+#pragma unroll
+            for (int i = 0; i < CNT / 2; ++i) {
+                const uint2 v = nt_load2(reinterpret_cast<const float2*>(p) + i);
+                out[2 * i] = __uint_as_float(v.x); out[2 * i + 1] = __uint_as_float(v.y);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) out[i] = i < valid ? p[i] : 0.0f;
+}
+
+template <int CNT, int ALIGN>
+__device__ __forceinline__ void store_f32(float* __restrict__ p, bool vec, int valid, const float (&in)[CNT]) {
+    if (vec) {
+        if constexpr (ALIGN == 16 && CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i)
+                nt_store(reinterpret_cast<uint4*>(p) + i,
+                         make_uint4(__float_as_uint(in[4 * i]), __float_as_uint(in[4 * i + 1]),
+                                    __float_as_uint(in[4 * i + 2]), __float_as_uint(in[4 * i + 3])));
+        } else {
+#pragma unroll
+            for (int i = 0; i < CNT / 2; ++i) reinterpret_cast<float2*>(p)[i] = make_float2(in[2 * i], in[2 * i + 1]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i)
+        if (i < valid) p[i] = in[i];
+}
+
+// ------------------------------------------------------------------------------------------
+// The sample of a thread's P groups: probabilities up to the normaliser.
+//
+// MaskLLM project page, Fig. 3 caption (Gumbel softmax over the candidates of each group) and
+// Fig. 5 caption (kappa scales the logits): y_k = softmax_k((kappa*l_k + g_k)/tau).  In base 2,
+// z'_k = A*l_k - B*h_k (see gumbel_log2).  A*|l| reaches several hundred at kappa = 100 while the
+// differences between candidates that matter are small, so z'_k is carried as an fp32 head
+// hi_k = fl(A*l_k - B*h_k) plus the remainder rem_k = (A*l_k - hi_k) - B*h_k that the fma leaves
+// (exact up to the rounding of B*h_k).  With mu = max_k hi_k, e_k = 2^((hi_k - mu) + rem_k): the
+// rounding errors are relative to |z'_k - mu| rather than to |A*l_k|, and mu cancels in y.
+
+template <int N, int M>
+struct Sample {
+    static constexpr int K = Candidates<N, M>::K;
+    static constexpr int P = SlotTiling<K>::P;
+    static constexpr int PK = P * K;
+    static constexpr int PH = SlotTiling<K>::phased ? 2 : 0;  // extra words of a phased tile
+    static constexpr int NB = (PK + PH + 3) / 4;              // Philox blocks per thread
+    static constexpr int LALIGN = (PK * 4) % 16 == 0 ? 16 : 8; // byte alignment of a thread's logits
+    // Stage a block's logits (and logit gradients) through LDS when a thread's share is more than
+    // one vector: then neighbouring lanes are more than a vector apart and direct accesses leave
+    // partly used cache lines in every instruction.  Tile: kThreads * PK floats (<= 70 KB).
+    static constexpr bool STAGE = PK * 4 > LALIGN;
+};
+
+template <int VW> struct StageVec;
+template <> struct StageVec<16> { using type = float4; };
+template <> struct StageVec<8> { using type = float2; };
+
+// h[i] for the thread's slots i = 0 .. PK-1 (slot index relative to g0*K).  Each Philox block
+// is turned into Gumbel exponents as soon as it is generated; only the last two words of the
+// previous block are carried, for a phased tile (K = 70) whose first slot may sit at word 2.
+template <int N, int M>
+__device__ __forceinline__ void thread_noise(const NoiseKey& nk, int64_t g0, float (&h)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    const uint64_t slot0 = (uint64_t)g0 * S::K;
+    const uint64_t b0 = slot0 >> 2;
+    const bool shifted = S::PH != 0 && (slot0 & 3) != 0;  // K = 70, odd group: starts at word 2
+    uint32_t carry2 = 0u, carry3 = 0u;
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+        const Philox4 blk = noise_block(nk, b0 + j);
+#pragma unroll
+        for (int i = 0; i < S::PK; ++i) {
+            if ((i + S::PH) / 4 != j) continue;  // slot i becomes available with block j
+            uint32_t x;
+            if constexpr (S::PH == 0) {
+                x = blk.v[i - 4 * j];
+            } else {
+                // shifted: word i+2, always in this block; else word i, in this block or the last
+                const uint32_t own = i >= 4 * j ? blk.v[i - 4 * j] : (i - 4 * j + 4 == 2 ? carry2 : carry3);
+                x = shifted ? blk.v[i + 2 - 4 * j] : own;
+            }
+            h[i] = gumbel_log2(x);
+        }
+        carry2 = blk.v[2];
+        carry3 = blk.v[3];
+    }
+}
+
+// For group p of the thread: t[k] = z'_k - mu, the base-2 scores relative to their maximum.
+template <int N, int M>
+__device__ __forceinline__ void group_scores(const float* l, const float* h, float A, float B,
+                                             float (&t)[Candidates<N, M>::K]) {
+    constexpr int K = Candidates<N, M>::K;
+    float hi[K], rem[K];
+    float mu = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float bh = B * h[k];
+        hi[k] = fmaf(A, l[k], -bh);
+        rem[k] = fmaf(A, l[k], -hi[k]) - bh;
+        mu = fmaxf(mu, hi[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) t[k] = (hi[k] - mu) + rem[k];
+}
+
+// e[k] = 2^(z'_k - mu) (unnormalised probabilities).
+template <int N, int M>
+__device__ __forceinline__ void group_exp(const float* l, const float* h, float A, float B,
+                                          float (&e)[Candidates<N, M>::K]) {
+    constexpr int K = Candidates<N, M>::K;
+    float t[K];
+    group_scores<N, M>(l, h, A, B, t);
+#pragma unroll
+    for (int k = 0; k < K; ++k) e[k] = exp2_fast(t[k]);
+}
+
+// Soft-mask sums s_j = sum over candidates k keeping j of e_k, and 1/S with S = sum_k e_k:
+// every candidate keeps N positions, so sum_j s_j = N * S.
+template <int N, int M>
+__device__ __forceinline__ float group_soft(const float (&e)[Candidates<N, M>::K], float (&sj)[M]) {
+    constexpr int K = Candidates<N, M>::K;
+    float tot = 0.0f;
+    static_for<0, M>([&](auto jc) NM_INLINE {
+        constexpr int j = decltype(jc)::value;
+        float acc = 0.0f;
+        static_for<0, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
+            if constexpr ((cand_keep<N, M, k>() >> j) & 1u) acc += e[k];
+        });
+        sj[j] = acc;
+        tot += acc;
+    });
+    return __builtin_amdgcn_rcpf(tot * (1.0f / N));  // S >= 1 (the largest e_k is ~1): rcp within 1 ulp
+}
+
+// ------------------------------------------------------------------------------------------
+// Block staging of logits and logit gradients through LDS.  A thread's PK floats are contiguous,
+// but lanes are PK*4 bytes apart, so direct 16-byte accesses would touch partly used cache lines
+// in every instruction.  In a block whose tiles are all present, the block's logits are moved as
+// one contiguous span with every lane on consecutive 16-byte vectors, and exchanged through an
+// LDS tile.  Partial blocks (the last one) use direct accesses.
+
+template <int N, int M>
+struct StageTile {
+    using S = Sample<N, M>;
+    using vec = typename StageVec<S::LALIGN>::type;
+    static constexpr int PER = S::PK * 4 / S::LALIGN;               // vectors per thread
+    static constexpr int VEC = S::STAGE ? kThreads * PER : 1;       // vectors per tile
+};
+
+template <int N, int M>
+__device__ __forceinline__ bool block_full(int64_t groups) {
+    return ((int64_t)blockIdx.x + 1) * kThreads * Sample<N, M>::P <= groups;
+}
+
+template <typename V>
+__device__ __forceinline__ void vec_to_floats(const V& v, float* out) {
+    if constexpr (sizeof(V) == 16) { out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w; }
+    else { out[0] = v.x; out[1] = v.y; }
+}
+template <typename V>
+__device__ __forceinline__ V floats_to_vec(const float* in) {
+    if constexpr (sizeof(V) == 16) return make_float4(in[0], in[1], in[2], in[3]);
+    else return make_float2(in[0], in[1]);
+}
+template <typename V>
+__device__ __forceinline__ void nt_store_vec(V* p, const V& v) {
+    if constexpr (sizeof(V) == 16)
+        nt_store(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+    else
+        nt_store(p, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
+}
+
+template <int N, int M>
+__device__ __forceinline__ void load_logits(const float* logits, int64_t g0, bool full, int nvalid, bool staged,
+                                            typename StageTile<N, M>::vec* tile, float (&l)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    using ST = StageTile<N, M>;
+    using V = typename ST::vec;
+    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
+    if constexpr (S::STAGE) {
+        if (staged) {
+            const V* src = reinterpret_cast<const V*>(logits + (int64_t)blockIdx.x * kThreads * PK);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if constexpr (sizeof(V) == 16) {
+                    const uint4 u = nt_load4(src + threadIdx.x + i * kThreads);
+                    tile[threadIdx.x + i * kThreads] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+                } else {
+                    const uint2 u = nt_load2(src + threadIdx.x + i * kThreads);
+                    tile[threadIdx.x + i * kThreads] = make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PER; ++i) vec_to_floats(tile[threadIdx.x * PER + i], l + W * i);
+            return;
+        }
+    }
+    load_f32<PK, S::LALIGN>(logits + g0 * S::K, full, nvalid * S::K, l);
+}
+
+template <int N, int M>
+__device__ __forceinline__ void store_dlogits(float* dlogits, int64_t g0, bool full, int nvalid, bool staged,
+                                              typename StageTile<N, M>::vec* tile,
+                                              const float (&dl)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    using ST = StageTile<N, M>;
+    using V = typename ST::vec;
+    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
+    if constexpr (S::STAGE) {
+        if (staged) {
+            __syncthreads();  // every thread has read its logits out of the tile
+#pragma unroll
+            for (int i = 0; i < PER; ++i) tile[threadIdx.x * PER + i] = floats_to_vec<V>(dl + W * i);
+            __syncthreads();
+            V* dst = reinterpret_cast<V*>(dlogits + (int64_t)blockIdx.x * kThreads * PK);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) nt_store_vec(dst + threadIdx.x + i * kThreads, tile[threadIdx.x + i * kThreads]);
+            return;
+        }
+    }
+    store_f32<PK, S::LALIGN>(dlogits + g0 * S::K, full, nvalid * S::K, dl);
+}
+
+// ------------------------------------------------------------------------------------------
+// Hard mask and compressed storage ("Accelerating Sparse Deep Neural Networks" summary page,
+// section 3.1).  A thread owns a chunk of consecutive groups of one row whose index fields fill
+// whole 32-bit words (2:4: 8 groups -> 1 word; 2:8 and 4:8: 16 and 8 groups -> 3 words), so the
+// metadata is written with plain stores and no atomics.
+
+template <int N, int M>
+struct PackTiling {
+    static constexpr int BITS = M <= 2 ? 1 : (M <= 4 ? 2 : (M <= 8 ? 3 : 4));  // ceil(log2 M)
+};
+
+// Groups per 16-byte-multiple unit when a group occupies `bytes` bytes (8 B -> 2 groups).
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int unit_groups(int bytes) { return 16 / gcd_c(16, bytes); }
+
+// One element's raw bits (zero-extended to 32 for bf16).
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(const typename T::storage* p, int64_t i) {
+    if constexpr (T::bytes == 4) return reinterpret_cast<const uint32_t*>(p)[i];
+    else return (uint32_t)p[i];
+}
+template <typename T>
+__device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, uint32_t v) {
+    if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = v;
+    else p[i] = (uint16_t)v;
+}
+
+// Raw element bits (bit copies: packed values keep NaN payloads and signed zeros).  CNT elements
+// of T, each zero-extended into a uint32.  vec: the caller guarantees 16-byte alignment, that
+// CNT * bytes is a multiple of 16 and that all CNT elements exist; otherwise element i is read
+// or written only if i < valid.
+template <typename T, int CNT, bool NTL = false>
+__device__ __forceinline__ void load_raw(const typename T::storage* __restrict__ p, bool vec, int valid,
+                                         uint32_t* out) {
+    static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < CNT * T::bytes / 16; ++i) {
+            const uint4 v = NTL ? nt_load4(reinterpret_cast<const uint4*>(p) + i) : reinterpret_cast<const uint4*>(p)[i];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (T::bytes == 4) {
+                    out[4 * i + q] = d[q];
+                } else {
+                    out[8 * i + 2 * q] = d[q] & 0xFFFFu;
+                    out[8 * i + 2 * q + 1] = d[q] >> 16;
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) out[i] = i < valid ? reinterpret_cast<const uint32_t*>(p)[i] : 0u;
+        else out[i] = i < valid ? (uint32_t)p[i] : 0u;
+    }
+}
+
+template <typename T, int CNT>
+__device__ __forceinline__ void store_raw(typename T::storage* __restrict__ p, bool vec, int valid,
+                                          const uint32_t* in) {
+    static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < CNT * T::bytes / 16; ++i) {
+            uint32_t d[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (T::bytes == 4) d[q] = in[4 * i + q];
+                else d[q] = in[8 * i + 2 * q] | (in[8 * i + 2 * q + 1] << 16);
+            }
+            nt_store(reinterpret_cast<uint4*>(p) + i, make_uint4(d[0], d[1], d[2], d[3]));
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if (i < valid) {
+            if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = in[i];
+            else p[i] = (uint16_t)in[i];
+        }
+    }
+}
+
+// Logits of `cnt` groups starting at p (scalar path reads only the first `valid` floats).
+template <int CNT>
+__device__ __forceinline__ void load_logit_unit(const float* __restrict__ p, bool vec, int valid, float* out) {
+    if (vec) {
+        if constexpr (CNT % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < CNT / 4; ++i) {
+                const float4 v = reinterpret_cast<const float4*>(p)[i];
+                out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CNT / 2; ++i) {
+                const float2 v = reinterpret_cast<const float2*>(p)[i];
+                out[2 * i] = v.x; out[2 * i + 1] = v.y;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) out[i] = i < valid ? p[i] : 0.0f;
+}
+
+// One group's raw weights (M elements) and the store of N kept values / M dense values, with
+// the widest single access the group's byte size allows when `vec` (rows 16-byte aligned, so a
+// group of 2^i bytes is 2^i-byte aligned); element accesses otherwise.
+template <typename T, int CNT>
+__device__ __forceinline__ void load_group_raw(const typename T::storage* __restrict__ p, bool vec, uint32_t* out) {
+    constexpr int BYTES = CNT * T::bytes;
+    if constexpr (BYTES % 16 == 0) {
+        if (vec) {
+            load_raw<T, CNT>(p, true, CNT, out);
+            return;
+        }
+    } else if constexpr (BYTES == 8) {
+        if (vec) {
+            const uint2 d = *reinterpret_cast<const uint2*>(p);
+            if constexpr (T::bytes == 2) {
+                out[0] = d.x & 0xFFFFu; out[1] = d.x >> 16; out[2] = d.y & 0xFFFFu; out[3] = d.y >> 16;
+            } else {
+                out[0] = d.x; out[1] = d.y;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) out[i] = reinterpret_cast<const uint32_t*>(p)[i];
+        else out[i] = (uint32_t)p[i];
+    }
+}
+
+template <typename T, int CNT>
+__device__ __forceinline__ void store_group_raw(typename T::storage* __restrict__ p, bool vec, const uint32_t* in) {
+    constexpr int BYTES = CNT * T::bytes;
+    if constexpr (BYTES % 16 == 0) {
+        if (vec) {
+            store_raw<T, CNT>(p, true, CNT, in);
+            return;
+        }
+    } else if constexpr (BYTES == 8) {
+        if (vec) {
+            if constexpr (T::bytes == 2) nt_store(p, make_uint2(in[0] | (in[1] << 16), in[2] | (in[3] << 16)));
+            else nt_store(p, make_uint2(in[0], in[1]));
+            return;
+        }
+    } else if constexpr (BYTES == 4) {
+        if (vec) {
+            if constexpr (T::bytes == 2) nt_store(p, in[0] | (in[1] << 16));
+            else nt_store(p, in[0]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = in[i];
+        else p[i] = (uint16_t)in[i];
+    }
+}
+
+// General pack/unpack: a block owns a tile of consecutive groups of one row (grid x = tile within
+// the row, grid y = row, looping over rows beyond the grid's y limit).  A thread owns GT
+// consecutive groups, GT chosen so that its weights / dense output are one 16-byte vector
+// (2 groups of four bf16, else 1), so weights, packed values, hard indices and dense output of
+// neighbouring lanes are contiguous.  Index fields, which straddle words for 3-bit positions,
+// are assembled in LDS (ds_or of at most two words per thread) and stored as whole words after
+// a barrier; every tile starts on a word boundary because kThreads * GT * N * BITS is a
+// multiple of 32.  The host sets `aligned` when every row of w, logits, values and dense starts
+// on a 16-byte boundary (then every thread's vector is aligned to its size).
+
+// ------------------------------------------------------------------------------------------
+// Launch helpers.  Grids are flat, one tile per thread; the host has checked that every count fits.
+
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + kThreads - 1) / kThreads); }
+
+// (n, m, wtype) -> template instance.  The caller has validated the triple.
+#define NM_DISPATCH(FN, n, m, wt, ...)                                            \
+    do {                                                                          \
+        const bool bf = (wt) == 1;                                                \
+        switch ((m) * 16 + (n)) {                                                 \
+        case 4 * 16 + 1: return bf ? FN<1, 4, BF16>(__VA_ARGS__) : FN<1, 4, F32>(__VA_ARGS__); \
+        case 4 * 16 + 2: return bf ? FN<2, 4, BF16>(__VA_ARGS__) : FN<2, 4, F32>(__VA_ARGS__); \
+        case 4 * 16 + 3: return bf ? FN<3, 4, BF16>(__VA_ARGS__) : FN<3, 4, F32>(__VA_ARGS__); \
+        case 8 * 16 + 1: return bf ? FN<1, 8, BF16>(__VA_ARGS__) : FN<1, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 2: return bf ? FN<2, 8, BF16>(__VA_ARGS__) : FN<2, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 3: return bf ? FN<3, 8, BF16>(__VA_ARGS__) : FN<3, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 4: return bf ? FN<4, 8, BF16>(__VA_ARGS__) : FN<4, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 5: return bf ? FN<5, 8, BF16>(__VA_ARGS__) : FN<5, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 6: return bf ? FN<6, 8, BF16>(__VA_ARGS__) : FN<6, 8, F32>(__VA_ARGS__); \
+        case 8 * 16 + 7: return bf ? FN<7, 8, BF16>(__VA_ARGS__) : FN<7, 8, F32>(__VA_ARGS__); \
+        default: return hipErrorInvalidValue;                                     \
+        }                                                                         \
+    } while (0)
+
+}  // namespace nm

@@ -83,6 +83,18 @@ def candidate_sums(w, grad, n, m, cand_matrix):
     return a.reshape(rows, cols // m, m) @ cand_matrix.T
 
 
+def candidate_sums_wreg_abs(w, grad, soft, lam, n, m, cand_matrix):
+    """Size of the terms of the regularised candidate sums: per candidate k, the sum over kept
+    positions j of |G_j w_j| + |2 lam w_j m_j w_j| (grad None: the regulariser alone).  The
+    backward bound is relative to these magnitudes, as it is to |d| without the regulariser."""
+    w = np.asarray(w, np.float64)
+    a = np.abs(2.0 * lam * w * np.asarray(soft, np.float64) * w)
+    if grad is not None:
+        a = a + np.abs(np.asarray(grad, np.float64) * w)
+    rows, cols = a.shape
+    return a.reshape(rows, cols // m, m) @ cand_matrix.T
+
+
 # --- convergence monitors -------------------------------------------------------------------
 
 LN2 = 0.6931471805599453

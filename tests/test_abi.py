@@ -53,6 +53,7 @@ def test_bad_shapes_are_rejected_on_the_host(kw, status):
     sh = _shape(**kw)
     assert L.nm_mask_forward(sh, _sample(), FAKE, FAKE, FAKE, None) == status
     assert L.nm_mask_backward(sh, _sample(), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert L.nm_mask_backward_wreg(sh, _sample(), 0.5, FAKE, FAKE, FAKE, FAKE, None) == status
     assert L.nm_mask_harden_pack(sh, FAKE, FAKE, FAKE, FAKE, None, None) == status
     assert L.nm_unpack(sh, FAKE, FAKE, FAKE, None) == status
     assert L.nm_debug_noise(sh, _sample(), FAKE, None) == status
@@ -71,6 +72,7 @@ def test_bad_samples_are_rejected_on_the_host(kappa, tau):
     L = S.lib()
     assert L.nm_mask_forward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_mask_backward(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_backward_wreg(_shape(), _sample(kappa, tau), 0.5, FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_debug_soft_mask(_shape(), _sample(kappa, tau), FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_mask_forward_monitor(_shape(), _sample(kappa, tau), FAKE, FAKE, FAKE, None, None,
                                      FAKE, FAKE, 1 << 20, None) == NM_EINVAL
@@ -205,3 +207,24 @@ def test_binding_refuses_cpu_tensors():
     L = torch.zeros(4, 4, 6)
     with pytest.raises(ValueError):
         S.nm_mask_forward(w, L, 2, 4, 1.0, 1.0, 0, 0)
+
+
+@pytest.mark.parametrize("lam", [float("nan"), float("inf"), -float("inf"), 3e38])
+def test_regulariser_strength_must_be_finite(lam):
+    """lambda and 2*lambda must be finite fp32 numbers (3e38 doubles past the fp32 range)."""
+    L = S.lib()
+    assert L.nm_mask_backward_wreg(_shape(), _sample(), lam, FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_backward_wreg(_shape(), _sample(), lam, FAKE, FAKE, None, FAKE, None) == NM_EINVAL
+
+
+def test_regulariser_backward_pointer_rules():
+    """grad_w_masked may be NULL (the regulariser alone); every other pointer is required, and
+    every non-NULL pointer must be 16-byte aligned.  An empty matrix launches nothing."""
+    L = S.lib()
+    sh, smp = _shape(), _sample()
+    for args in [(None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, FAKE, None)]:
+        assert L.nm_mask_backward_wreg(sh, smp, 0.5, *args, None) == NM_EINVAL
+    for args in [(ODD, FAKE, FAKE, FAKE), (FAKE, ODD, FAKE, FAKE), (FAKE, FAKE, ODD, FAKE),
+                 (FAKE, FAKE, FAKE, ODD), (FAKE, FAKE, None, ODD)]:
+        assert L.nm_mask_backward_wreg(sh, smp, 0.5, *args, None) == NM_EALIGN
+    assert L.nm_mask_backward_wreg(_shape(rows=0), smp, 0.5, None, None, None, None, None) == NM_OK
