@@ -584,12 +584,13 @@ def workload_spmm(args):
                       "pct_dense_bf16_peak_useful": round(100 * useful / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 1)}
     res["speedup_vs_dense"] = round(res["dense_torch"]["ms_per_layer"] / res["sparse_smfmac"]["ms_per_layer"], 3)
 
-    # decode-sized batches: bound by reading the weights once (packed: 1.125 B per weight,
-    # dense bf16: 2 B); HIP-event times per call include the host's launch cost, which is of
-    # the order of the kernels here (the rocprofv3 trace gives the kernels alone)
+    # smaller batches, from decode (bound by reading the weights once: packed 1.125 B per
+    # weight, dense bf16 2 B) through prefill sizes; HIP-event times per call include the host's
+    # launch cost, which is of the order of the kernels at the smallest sizes (the rocprofv3
+    # trace gives the kernels alone)
     weights = sum(mt["rows"] * mt["cols"] for mt in mats)
-    decode = {}
-    for tk in (1, 16):
+    batches = {}
+    for tk in (1, 16, 64, 128, 256, 512, 1024, 2048):
         for mt in mats:
             mt["xd"] = nm_synth.normal((tk, mt["cols"]), 1.0, 11 + tk, torch.bfloat16, device=dev)
             mt["yd"] = torch.empty((tk, mt["rows"]), dtype=torch.bfloat16, device=dev)
@@ -602,11 +603,14 @@ def workload_spmm(args):
             for mt in mats:
                 torch.mm(mt["xd"], mt["dense_t"], out=mt["yd"])
 
-        ts, td = _elapsed_ms(sparse_d, reps=10 * args.kernel_reps), _elapsed_ms(dense_d, reps=10 * args.kernel_reps)
-        decode[f"{tk}_tokens"] = {"sparse_ms_per_layer": round(ts, 4), "dense_ms_per_layer": round(td, 4),
-                                  "sparse_weight_GBps": round(1.125 * weights / (ts * 1e-3) / 1e9, 1),
-                                  "speedup_vs_dense": round(td / ts, 3)}
-    res["decode"] = decode
+        reps = 10 * args.kernel_reps if tk <= 128 else 2 * args.kernel_reps
+        ts, td = _elapsed_ms(sparse_d, reps=reps), _elapsed_ms(dense_d, reps=reps)
+        u = weights * tk  # useful flops: 2 * tokens * (kept weights = weights / 2)
+        batches[f"{tk}_tokens"] = {"sparse_ms_per_layer": round(ts, 4), "dense_ms_per_layer": round(td, 4),
+                                   "sparse_useful_TFLOPs": round(u / (ts * 1e-3) / 1e12, 1),
+                                   "sparse_weight_GBps": round(1.125 * weights / (ts * 1e-3) / 1e9, 1),
+                                   "speedup_vs_dense": round(td / ts, 3)}
+    res["batches"] = batches
     return {"metric": "2:4 sparse x dense product on the packed weights vs dense bf16 GEMM", "unit": "TFLOP/s",
             "config": {"workload": "LLaMA-2-7B-shaped layer (7 matrices) packed 2:4, X 4096 tokens bf16, "
                                    "Y bf16, fp32 accumulation"},

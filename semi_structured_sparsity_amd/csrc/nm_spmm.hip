@@ -17,10 +17,12 @@
 // So one lane's index operand is 16 consecutive bits of a packed row's index stream and its A
 // values are 8 consecutive packed values: the packed form feeds the instruction unchanged.
 //
-// Tiling: a block of 512 threads computes a 256 (out) x 256 (token) tile of Y^T (the last tile
-// along either side may be partial), each of its 8 waves a 128 x 64 part as 4 x 2 instruction
-// tiles with fp32 accumulators.  A stage covers 64 dense k: the packed values (256 rows x 64 B),
-// their index words (256 x 8 B) and X (256 tokens x 128 B), 50 KB in LDS.  Three stages live in
+// Tiling (the largest tile of the family, SpTile<8>): a block of 512 threads computes a 256 (out)
+// x 256 (token) tile of Y^T (the last tile along either side may be partial), each of its 8 waves
+// a 128 x 64 part as 4 x 2 instruction tiles with fp32 accumulators.  A stage covers 64 dense k:
+// the packed values (256 rows x 64 B), their index words (256 x 8 B) and X (256 tokens x 128 B),
+// 50 KB in LDS.  The 4- and 2-wave tiles (128 and 64 square) scale every stage region with the
+// tile, so each wave's share of the loads stays the same.  Three stages live in
 // LDS at once and are filled by LDS DMA loads (global_load_lds), which write LDS without passing
 // through registers: stage s + 3 is requested once stage s has been read, so memory has about
 // two stages of matrix work to answer, and the LDS fragment reads of each half stage overlap the
@@ -44,36 +46,48 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int SP_BM = 256;                       // W rows (outputs) per block
-constexpr int SP_BN = 256;                       // tokens per block
-constexpr int SP_ABYTES = SP_BM * 64;            // packed values of a stage: 32 kept bf16 per row
-constexpr int SP_XBYTES = SP_BN * 128;           // X of a stage: 64 bf16 per token
-constexpr int SP_IBYTES = SP_BM * 8;             // index words of a stage: 2 per row
-constexpr int SP_STAGE = SP_ABYTES + SP_XBYTES + SP_IBYTES;  // 51,200 B
-constexpr int SP_NBUF = 3;
-constexpr size_t SP_SMEM = (size_t)SP_NBUF * SP_STAGE;       // 153,600 B of the 160 KB
-
-constexpr int SP_THREADS = 512;  // 8 waves: 2 along W rows x 4 along tokens, 128 x 64 each
+// Tile family.  A block of WAVES waves owns a T x T tile of Y^T with T = 32 * WAVES (256, 128
+// or 64), so that every wave's share of a stage's DMA loads is the same: 2 KB of packed values,
+// 4 KB of X and 256 B of index words (7 loads).  Waves are laid out WR along W rows by WT along
+// tokens, each computing TI x TJ instruction tiles of 32 x 32.
+template <int WAVES>
+struct SpTile {
+    static constexpr int T = 32 * WAVES;             // W rows and tokens per block
+    static constexpr int WR = 2;                     // waves along W rows
+    static constexpr int WT = WAVES / 2;             // waves along tokens
+    static constexpr int TI = T / (32 * WR);         // instruction tiles per wave along W rows
+    static constexpr int TJ = T / (32 * WT);         // ... along tokens
+    static constexpr int ABYTES = T * 64;            // packed values of a stage: 32 kept bf16 per row
+    static constexpr int XBYTES = T * 128;           // X of a stage: 64 bf16 per token
+    static constexpr int IBYTES = T * 8;             // index words of a stage: 2 per row
+    static constexpr int STAGE = ABYTES + XBYTES + IBYTES;
+    static constexpr size_t SMEM = 3 * (size_t)STAGE;  // three stages: 150, 75 or 37.5 KB
+    static_assert(WAVES == 2 || WAVES == 4 || WAVES == 8, "tile family");
+};
 
 // chunk permutations: 16 B chunk c of packed-value row r sits at chunk c ^ swz_a(r); chunk c of
 // X row t at c ^ swz_x(t)
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_x(int t) { return (t ^ (t >> 3)) & 7; }
 
-__global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
+    using TL = SpTile<WAVES>;
+    constexpr int T = TL::T, TI = TL::TI, TJ = TL::TJ;
+    constexpr int SP_ABYTES = TL::ABYTES, SP_XBYTES = TL::XBYTES, SP_STAGE = TL::STAGE;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     // XCD-aware tile order: block b runs on XCD b % 8 and takes tile (b % 8) * chunk + b / 8
-    const int64_t ntok = (a.tokens + SP_BN - 1) / SP_BN, nout = (a.out + SP_BM - 1) / SP_BM;
+    const int64_t ntok = (a.tokens + T - 1) / T, nout = (a.out + T - 1) / T;
     const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
     const int64_t rt = (ntok + C - 1) / C, ro = (nout + R - 1) / R;   // region size in tiles
     const int64_t x = blockIdx.x % 8, p = blockIdx.x / 8;
     const int64_t ot = (x / C) * ro + p / rt, tt = (x % C) * rt + p % rt;
     if (p >= ro * rt || ot >= nout || tt >= ntok) return;  // whole block
-    const int64_t bo = ot * SP_BM, bt = tt * SP_BN;
+    const int64_t bo = ot * T, bt = tt * T;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wo = (wv >> 2) * 128, wt = (wv & 3) * 64;
+    const int wo = (wv / TL::WT) * (32 * TI), wt = (wv % TL::WT) * (32 * TJ);
 
     // DMA sources.  Per stage each wave fills 2 KB of packed values, 4 KB of X and 256 B of
     // index words; lane `lane` of the wave's k-th 1 KB piece fills 16 B slot piece * 64 + lane
@@ -115,12 +129,12 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     // fragment offsets within a stage (lane constants; the rest folds into immediates)
     const int r32 = lane & 31, kg = lane >> 5;
     const int sw = swz_a(r32);  // rows wo + 32 i + r32 share r32's bits 1-4
-    int aoff[2], xoff[2][2][2];
+    int aoff[2], xoff[2][TJ][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         aoff[h] = (wo + r32) * 64 + (((2 * h + kg) ^ sw) << 4);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             const int t = wt + j * 32 + r32, s = swz_x(t);
             xoff[h][j][0] = SP_ABYTES + t * 128 + (((4 * h + kg) ^ s) << 4);
             xoff[h][j][1] = SP_ABYTES + t * 128 + (((4 * h + 2 + kg) ^ s) << 4);
@@ -128,36 +142,36 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     }
     const int ioff = SP_ABYTES + SP_XBYTES + (wo + r32) * 8;
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // fragments of one instruction column (32 dense k) of a stage: 4 A tiles with their index
     // words and 2 B tiles
     struct Frag {
-        bf16x8_t a[4], lo[2], hi[2];
-        uint32_t i[4];  // the index word of the tile's rows; this lane's half is taken at use
+        bf16x8_t a[TI], lo[TJ], hi[TJ];
+        uint32_t i[TI];  // the index word of the tile's rows; this lane's half is taken at use
     };
 #define NM_SP_READ(F, st, h)                                                                       \
     do {                                                                                           \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < TI; ++i_) {                                        \
             (F).a[i_] = *reinterpret_cast<const bf16x8_t*>((st) + aoff[h] + i_ * 32 * 64);         \
             (F).i[i_] = *reinterpret_cast<const uint32_t*>((st) + ioff + i_ * 32 * 8 + (h) * 4);   \
         }                                                                                          \
-        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_) {                                         \
+        _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) {                                        \
             (F).lo[j_] = *reinterpret_cast<const bf16x8_t*>((st) + xoff[h][j_][0]);                \
             (F).hi[j_] = *reinterpret_cast<const bf16x8_t*>((st) + xoff[h][j_][1]);                \
         }                                                                                          \
     } while (0)
 #define NM_SP_MMA(F)                                                                               \
     do {                                                                                           \
-        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_) {                                         \
+        _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) {                                        \
             const bf16x16_t bf_ = __builtin_shufflevector((F).lo[j_], (F).hi[j_], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15); \
-            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < TI; ++i_)                                      \
                 acc[i_][j_] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16((F).a[i_], bf_, acc[i_][j_],     \
                                                                         (int)((F).i[i_] >> (kg * 16)), 0, 0); \
         }                                                                                          \
@@ -223,9 +237,9 @@ __global__ __launch_bounds__(SP_THREADS) void k_spmm24(SpmmArgs a) {
     // epilogue: element r of tile (i, j) is W row bo + wo + 32 i + 8 (r/4) + 4 (lane/32) + r%4 and
     // token bt + wt + 32 j + lane%32; four consecutive r are consecutive outputs of one Y row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             const int64_t t = bt + wt + j * 32 + r32;
             if (t >= a.tokens) continue;
 #pragma unroll
@@ -337,32 +351,47 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24_skinny(SpmmArgs a) {
     }
 }
 
-// Up to this many tokens the skinny kernel runs; above it the 256 x 256 tiles.
-constexpr int64_t SP_SKINNY_MAX_TOKENS = 128;
+template <int WAVES>
+static hipError_t launch_tile(const SpmmArgs& a, hipStream_t s) {
+    using TL = SpTile<WAVES>;
+    // the 150 KB of the largest tile are above the default dynamic LDS limit: allow the size
+    const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24<WAVES>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::SMEM);
+    if (e != hipSuccess) return e;
+    const int64_t ntok = (a.tokens + TL::T - 1) / TL::T, nout = (a.out + TL::T - 1) / TL::T;
+    const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
+    const int64_t grid = 8 * ((ntok + C - 1) / C) * ((nout + R - 1) / R);
+    k_spmm24<WAVES><<<dim3((unsigned)grid), 64 * WAVES, TL::SMEM, s>>>(a);
+    return hipGetLastError();
+}
+
+// Up to this many tokens the skinny kernel runs; above it the tiles.
+constexpr int64_t SP_SKINNY_MAX_TOKENS = 64;
 
 hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
     if (a.tokens <= SP_SKINNY_MAX_TOKENS) {
         const unsigned gx = (unsigned)((a.out + 15) / 16);
-        if (a.tokens <= 16) {
+        if (a.tokens <= 16)
             k_spmm24_skinny<1, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
-        } else if (a.tokens <= 32) {
+        else if (a.tokens <= 32)
             k_spmm24_skinny<2, 8, 2><<<dim3(gx, 1), 512, 0, s>>>(a);
-        } else if (a.tokens <= 64) {
+        else
             k_spmm24_skinny<4, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
-        } else {
-            k_spmm24_skinny<8, 8, 2><<<dim3(gx, (unsigned)((a.tokens + 127) / 128)), 512, 0, s>>>(a);
-        }
         return hipGetLastError();
     }
-    // the block's LDS (150 KB) is above the default dynamic limit: allow it for this kernel
-    const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)SP_SMEM);
-    if (e != hipSuccess) return e;
-    const int64_t ntok = (a.tokens + SP_BN - 1) / SP_BN, nout = (a.out + SP_BM - 1) / SP_BM;
-    const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
-    const int64_t grid = 8 * ((ntok + C - 1) / C) * ((nout + R - 1) / R);
-    k_spmm24<<<dim3((unsigned)grid), SP_THREADS, SP_SMEM, s>>>(a);
-    return hipGetLastError();
+    // Tile size.  Each CU moves its blocks' stages from L2 into LDS at a roughly fixed rate, so a
+    // product takes about (bytes a CU stages) / (that rate): the largest tile that still gives
+    // every CU a block is taken (256 x 256, 128 x 128 or 64 x 64).  With 256 x 256 tiles only,
+    // mid-size batches would leave most CUs idle (16 blocks for 4096 W rows at 256 tokens).
+    // Deeper pipelines (6 or 9 stages per block instead of 3) were measured no faster.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;  // MI355X
+    auto tiles = [&](int64_t t) { return ((a.out + t - 1) / t) * ((a.tokens + t - 1) / t); };
+    if (tiles(256) >= cus) return launch_tile<8>(a, s);
+    if (tiles(128) >= cus) return launch_tile<4>(a, s);
+    return launch_tile<2>(a, s);
 }
 
 }  // namespace nm

@@ -56,10 +56,11 @@ def test_sparse_matmul_matches_oracle(out, inn, tokens, ytype):
     assert bad == 0
 
 
-@pytest.mark.parametrize("name_index,tokens", [(0, 512), (4, 256), (6, 256)])
+@pytest.mark.parametrize("name_index,tokens", [(0, 512), (4, 256), (6, 256), (0, 4096), (6, 2048)])
 def test_sparse_matmul_llama7b_shapes_sampled_rows(name_index, tokens):
     """Full LLaMA-7B-shaped weights (q 4096x4096, up 11008x4096, down 4096x11008); the oracle
-    checks three windows of 128 W rows against every token."""
+    checks three windows of 128 W rows against every token.  The batches select each tile size
+    (64 x 64 up to 512 tokens here, 128 x 128 for down at 2048, 256 x 256 for q at 4096)."""
     name, out, inn = nm_synth.LLAMA2_7B_LAYER[name_index]
     _say("spmm", name, out, inn, tokens)
     _, values, indices = _packed_layer(out, inn, nm_synth.input_seed(2, 0, name_index))
@@ -91,8 +92,8 @@ def test_sparse_matmul_equals_dense_product_of_the_unpacked_weights():
                                              (252, 256, 255)])
 @pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
 def test_sparse_matmul_partial_tiles(out, inn, tokens, ytype):
-    """out and tokens not multiples of the 256 x 256 tile: the last tiles are partial, every
-    output inside matches the oracle and nothing past y's end is written."""
+    """out and tokens not multiples of the tile (64 x 64 at these sizes): the last tiles are
+    partial, every output inside matches the oracle and nothing past y's end is written."""
     _say("spmm partial", out, inn, tokens, ytype)
     _, values, indices = _packed_layer(out, inn, 50 + out + tokens, w_std=1.0)
     x = nm_synth.normal((tokens, inn), 1.0, 51, torch.bfloat16, device=DEV)
@@ -105,12 +106,43 @@ def test_sparse_matmul_partial_tiles(out, inn, tokens, ytype):
     assert bool(buf[tokens * out:].isnan().all())
 
 
+def _tile_of(out, tokens, cus=256):
+    """The tile the library picks: the largest that still gives every CU a block."""
+    tiles = lambda t: -(-out // t) * -(-tokens // t)
+    return 256 if tiles(256) >= cus else (128 if tiles(128) >= cus else 64)
+
+
+@pytest.mark.parametrize("out,inn,tokens,tile", [(6148, 128, 2600, 256), (4100, 192, 2049, 128),
+                                                  (4000, 320, 1000, 128), (2052, 128, 1100, 64),
+                                                  (1092, 256, 700, 64), (68, 64, 65, 64)])
+def test_sparse_matmul_each_tile_size_with_ragged_edges(out, inn, tokens, tile):
+    """Every tile size of the product (256, 128 and 64 rows and tokens per block) on shapes
+    whose last tiles are partial along both sides: windows of W rows (the ragged last one
+    included) against every token, and nothing written past y's end.  Fewer k stages than the
+    three in flight are covered by inn = 64 and 128."""
+    assert _tile_of(out, tokens, torch.cuda.get_device_properties(0).multi_processor_count) == tile
+    _say("spmm tile", tile, out, inn, tokens)
+    _, values, indices = _packed_layer(out, inn, 70 + out + tokens, w_std=1.0)
+    x = nm_synth.normal((tokens, inn), 1.0, 71, torch.bfloat16, device=DEV)
+    buf = torch.full((tokens * out + 4096,), float("nan"), dtype=torch.float32, device=DEV)
+    y = buf[:tokens * out].view(tokens, out)
+    S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32, out=y)
+    win = min(132, out)
+    for rb in sorted({0, (out // 2) // 4 * 4, out - win}):
+        ratio, bad = _check(values, indices, x, y, rows=min(win, out - rb), row_begin=rb)
+        _say("  rows", rb, "err/bound", ratio)
+        assert bad == 0
+    assert bool(buf[tokens * out:].isnan().all())
+    assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32), y)
+
+
 @pytest.mark.parametrize("out,inn,tokens", [(36, 64, 1), (100, 128, 7), (256, 4160, 32), (68, 192, 33),
                                              (132, 256, 64), (64, 320, 65), (96, 1024, 128), (4, 64, 128)])
 @pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
 def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
-    """Up to 128 tokens the product runs on blocks of 32 W rows whose waves split k (fewer
-    k blocks than waves included); every output against the oracle, nothing written past y."""
+    """Up to 64 tokens the product runs on blocks of 16 W rows whose waves split k (fewer k
+    blocks than waves included), above it on the 64 x 64 tiles; every output against the
+    oracle, nothing written past y."""
     _say("spmm few tokens", out, inn, tokens, ytype)
     _, values, indices = _packed_layer(out, inn, 60 + out + tokens, w_std=1.0)
     x = nm_synth.normal((tokens, inn), 1.0, 61, torch.bfloat16, device=DEV)
