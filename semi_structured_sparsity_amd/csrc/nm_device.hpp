@@ -248,7 +248,7 @@ __device__ __forceinline__ void load_as_float(const typename T::storage* __restr
 
 // Store CNT floats rounded to T.  Same `vec` / `valid` contract as load_as_float.
 template <typename T, int CNT>
-__device__ __forceinline__ void store_from_float(typename T::storage* __restrict__ p, bool vec,
+__device__ __forceinline__ void store_from_float(typename T::storage* p, bool vec,
                                                  int valid, const float (&in)[CNT]) {
     if constexpr (T::bytes == 4) {
         if (vec && CNT % 4 == 0) {

@@ -42,7 +42,7 @@ __device__ __forceinline__ void load_f32(const float* __restrict__ p, bool vec, 
 }
 
 template <int CNT, int ALIGN>
-__device__ __forceinline__ void store_f32(float* __restrict__ p, bool vec, int valid, const float (&in)[CNT]) {
+__device__ __forceinline__ void store_f32(float* p, bool vec, int valid, const float (&in)[CNT]) {
     if (vec) {
         if constexpr (ALIGN == 16 && CNT % 4 == 0) {
 #pragma unroll
@@ -282,8 +282,10 @@ __device__ __forceinline__ uint32_t load_bits(const typename T::storage* p, int6
 }
 template <typename T>
 __device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, uint32_t v) {
-    if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = v;
-    else p[i] = (uint16_t)v;
+    // non-temporal like the vector stores: where the compiler merges the two paths into one
+    // store, it keeps the non-temporal hint only if both paths carry it
+    if constexpr (T::bytes == 4) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p) + i);
+    else __builtin_nontemporal_store((uint16_t)v, reinterpret_cast<uint16_t*>(p) + i);
 }
 
 // Raw element bits (bit copies: packed values keep NaN payloads and signed zeros).  CNT elements
@@ -319,7 +321,7 @@ __device__ __forceinline__ void load_raw(const typename T::storage* __restrict__
 }
 
 template <typename T, int CNT>
-__device__ __forceinline__ void store_raw(typename T::storage* __restrict__ p, bool vec, int valid,
+__device__ __forceinline__ void store_raw(typename T::storage* p, bool vec, int valid,
                                           const uint32_t* in) {
     static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
     if (vec) {
@@ -397,7 +399,7 @@ __device__ __forceinline__ void load_group_raw(const typename T::storage* __rest
 }
 
 template <typename T, int CNT>
-__device__ __forceinline__ void store_group_raw(typename T::storage* __restrict__ p, bool vec, const uint32_t* in) {
+__device__ __forceinline__ void store_group_raw(typename T::storage* p, bool vec, const uint32_t* in) {
     constexpr int BYTES = CNT * T::bytes;
     if constexpr (BYTES % 16 == 0) {
         if (vec) {
@@ -418,10 +420,7 @@ __device__ __forceinline__ void store_group_raw(typename T::storage* __restrict_
         }
     }
 #pragma unroll
-    for (int i = 0; i < CNT; ++i) {
-        if constexpr (T::bytes == 4) reinterpret_cast<uint32_t*>(p)[i] = in[i];
-        else p[i] = (uint16_t)in[i];
-    }
+    for (int i = 0; i < CNT; ++i) store_bits<T>(p, i, in[i]);
 }
 
 // General pack/unpack: a block owns a tile of consecutive groups of one row (grid x = tile within

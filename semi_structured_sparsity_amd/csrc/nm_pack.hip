@@ -9,32 +9,45 @@ struct TileShape {
     static constexpr int BITS = PackTiling<N, M>::BITS;
     static constexpr int GT = M * T::bytes >= 16 ? 1 : 16 / (M * T::bytes);  // groups per thread
     static constexpr int TILE = kThreads * GT;                               // groups per block
-    static constexpr int WORDS = TILE * N * BITS / 32;                        // index words per tile
     static constexpr int TBITS = GT * N * BITS;                               // a thread's index bits
     static_assert(TILE * N * BITS % 32 == 0 && TBITS <= 32, "tiles start on words; <= 2 words per thread");
 };
 
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
+    // Index fields are assembled per wave: a wave's 64 * GT groups fill whole 32-bit words, so
+    // each wave ORs its lanes' fields into its own LDS word tile and stores those words itself.
+    // LDS operations of one wave complete in order, so wave-scope fences replace block barriers.
     using TS = TileShape<N, M, T>;
     constexpr int K = TS::K, GT = TS::GT, BITS = TS::BITS;
-    __shared__ uint32_t words[TS::WORDS];
+    constexpr int WW = 64 * GT * N * BITS / 32;                // index words of a wave's groups
+    static_assert(64 * GT * N * BITS % 32 == 0, "a wave's fields fill whole words");
+    __shared__ uint32_t words[kThreads / 64 * WW];
+    const int lane = threadIdx.x & 63, wq = (threadIdx.x >> 6) * 64 * GT;  // wave's first group
+    uint32_t* ww = words + (threadIdx.x >> 6) * WW;
     const int64_t q_begin = (int64_t)blockIdx.x * TS::TILE;
     const int ng = (int)(a.gpr - q_begin < TS::TILE ? a.gpr - q_begin : TS::TILE);
-    const int nwords = (ng * N * BITS + 31) / 32;
+    const int ngw = ng - wq < 0 ? 0 : (ng - wq < 64 * GT ? ng - wq : 64 * GT);
+    if (ngw == 0) return;  // a whole wave past the row's end (no block barrier is used)
+    const int nwords = (ngw * N * BITS + 31) / 32;
     const int lq = threadIdx.x * GT;                        // first group of this thread in the tile
     const int mine = ng - lq < 0 ? 0 : (ng - lq < GT ? ng - lq : GT);
     const bool vec = a.aligned != 0 && mine == GT;
+    const int lb = lane * GT * N * BITS;                    // the thread's first bit in the wave's words
     for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
-        for (int i = threadIdx.x; i < TS::WORDS; i += kThreads) words[i] = 0u;
-        __syncthreads();
+        const int64_t g0 = r * a.gpr + q_begin + lq;        // flat index of the thread's first group
+        float l[GT * K];
+        uint32_t raw[GT * M];
         if (mine > 0) {
-            const int64_t g0 = r * a.gpr + q_begin + lq;    // flat index of the thread's first group
-            float l[GT * K];
             if (vec) load_logit_unit<GT * K>(a.logits + g0 * K, true, GT * K, l);
             else load_logit_unit<GT * K>(a.logits + g0 * K, false, mine * K, l);
-            uint32_t raw[GT * M], v[GT * N], hard[GT];
             load_group_raw<T, GT * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, vec, raw);
+        }
+        for (int i = lane; i < WW; i += 64) ww[i] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (mine > 0) {
+            uint32_t v[GT * N], hard[GT];
             uint64_t acc = 0;
 #pragma unroll
             for (int i = 0; i < GT; ++i) {
@@ -71,69 +84,68 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
             if (a.hard) {
 #pragma unroll
                 for (int i = 0; i < GT; ++i)
-                    if (i < mine) a.hard[g0 + i] = (uint8_t)hard[i];
+                    if (i < mine) __builtin_nontemporal_store((uint8_t)hard[i], a.hard + g0 + i);
             }
-            const int lb = lq * N * BITS;                   // the thread's first bit in the tile
-            atomicOr(&words[lb / 32], (uint32_t)(acc << (lb % 32)));
-            if ((lb % 32) + TS::TBITS > 32) atomicOr(&words[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
+            atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
+            if ((lb % 32) + TS::TBITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
         }
-        __syncthreads();
-        uint32_t* idx = a.indices + r * a.words_per_row + q_begin * N * BITS / 32;
-        for (int i = threadIdx.x; i < nwords; i += kThreads) nt_store(idx + i, words[i]);
-        __syncthreads();  // the next row reuses the tile
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t* idx = a.indices + r * a.words_per_row + (q_begin + wq) * N * BITS / 32;
+        for (int i = lane; i < nwords; i += 64) nt_store(idx + i, ww[i]);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the words are read before the next row clears them
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
+    // Each thread reads the one or two index words that hold its fields straight from memory
+    // (a wave's fields are a few consecutive words, so its lanes share cache lines): no LDS tile
+    // and no barrier.  The second word is read only when the fields straddle into it, so every
+    // read stays within the row's words.
     using TS = TileShape<N, M, T>;
     constexpr int GT = TS::GT, BITS = TS::BITS;
-    __shared__ uint32_t words[TS::WORDS];
     const int64_t q_begin = (int64_t)blockIdx.x * TS::TILE;
     const int ng = (int)(a.gpr - q_begin < TS::TILE ? a.gpr - q_begin : TS::TILE);
-    const int nwords = (ng * N * BITS + 31) / 32;
     const int lq = threadIdx.x * GT;
     const int mine = ng - lq < 0 ? 0 : (ng - lq < GT ? ng - lq : GT);
+    if (mine == 0) return;
     const bool vec = a.aligned != 0 && mine == GT;
+    const int64_t lb = (q_begin + lq) * N * BITS;  // the thread's first bit in its row's stream
     for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
-        const uint32_t* idx = a.indices + r * a.words_per_row + q_begin * N * BITS / 32;
-        for (int i = threadIdx.x; i < nwords; i += kThreads) words[i] = idx[i];
-        __syncthreads();
-        if (mine > 0) {
-            const int64_t g0 = r * a.gpr + q_begin + lq;
-            const int lb = lq * N * BITS;
-            uint64_t acc = words[lb / 32];
-            if ((lb % 32) + TS::TBITS > 32) acc |= (uint64_t)words[lb / 32 + 1] << 32;
-            acc >>= lb % 32;
-            uint32_t v[GT * N], o[GT * M];
-            const auto* vp = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
-            if (vec) {
-                load_group_raw<T, GT * N>(vp, true, v);
-            } else {
+        const int64_t g0 = r * a.gpr + q_begin + lq;
+        uint32_t v[GT * N], o[GT * M];
+        const auto* vp = reinterpret_cast<const typename T::storage*>(a.values) + g0 * N;
+        if (vec) {
+            load_group_raw<T, GT * N>(vp, true, v);
+        } else {
 #pragma unroll
-                for (int e = 0; e < GT * N; ++e) v[e] = e < mine * N ? load_bits<T>(vp, e) : 0u;
-            }
+            for (int e = 0; e < GT * N; ++e) v[e] = e < mine * N ? load_bits<T>(vp, e) : 0u;
+        }
+        const uint32_t* idx = a.indices + r * a.words_per_row + lb / 32;
+        uint64_t acc = idx[0];
+        if ((lb % 32) + mine * N * BITS > 32) acc |= (uint64_t)idx[1] << 32;
+        acc >>= lb % 32;
 #pragma unroll
-            for (int i = 0; i < GT; ++i) {
-                uint32_t pos[N];
+        for (int i = 0; i < GT; ++i) {
+            uint32_t pos[N];
 #pragma unroll
-                for (int tt = 0; tt < N; ++tt) pos[tt] = (uint32_t)(acc >> ((i * N + tt) * BITS)) & ((1u << BITS) - 1u);
+            for (int tt = 0; tt < N; ++tt) pos[tt] = (uint32_t)(acc >> ((i * N + tt) * BITS)) & ((1u << BITS) - 1u);
 #pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    uint32_t x = 0u;  // +0.0 where nothing is kept
+            for (int j = 0; j < M; ++j) {
+                uint32_t x = 0u;  // +0.0 where nothing is kept
 #pragma unroll
-                    for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[i * N + tt] : x;  // later field wins
-                    o[i * M + j] = x;
-                }
-            }
-            auto* dp = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
-            if (vec) {
-                store_group_raw<T, GT * M>(dp, true, o);
-            } else {
-                for (int e = 0; e < mine * M; ++e) store_bits<T>(dp, e, o[e]);
+                for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[i * N + tt] : x;  // later field wins
+                o[i * M + j] = x;
             }
         }
-        __syncthreads();  // the next row reuses the tile
+        auto* dp = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
+        if (vec) {
+            store_group_raw<T, GT * M>(dp, true, o);
+        } else {
+            for (int e = 0; e < mine * M; ++e) store_bits<T>(dp, e, o[e]);
+        }
     }
 }
 
