@@ -150,6 +150,19 @@ nm_status nm_mask_backward_wreg(const nm_shape *shape, const nm_sample *sample, 
                                 const void *w, const float *logits, const void *grad_w_masked,
                                 float *grad_logits, void *stream);
 
+/* Forward and hard-mask pack of the same weights and logits in one call, for a step that needs
+ * both (for instance a training step that also exports the current hard mask): the outputs are
+ * exactly those of nm_mask_forward and nm_mask_harden_pack with the same arguments.  For 2:4
+ * with cols/4 a multiple of 8 (every row's index bits fill whole words) one kernel reads w and
+ * the logits once for both, moving 2*wb + 6 + wb/2 + 1/8 bytes per weight instead of
+ * 3*wb + 12 + wb/2 + 1/8; other shapes run the two passes one after the other.
+ *   w, logits, w_masked           as nm_mask_forward
+ *   values, indices, hard_idx     as nm_mask_harden_pack (hard_idx may be NULL)
+ * Errors: those of both entry points, checked before anything is launched. */
+nm_status nm_mask_forward_pack(const nm_shape *shape, const nm_sample *sample, const void *w,
+                               const float *logits, void *w_masked, void *values, uint32_t *indices,
+                               uint8_t *hard_idx, void *stream);
+
 /* Hard mask and compressed storage ("Accelerating Sparse Deep Neural Networks" summary page,
  * section 3.1).  Per group: k* = first argmax of its logits; the kept weights of candidate k*
  * go to `values` and their positions to `indices` (layout above).

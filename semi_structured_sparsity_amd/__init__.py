@@ -12,6 +12,8 @@ Entry points, named as in the C ABI:
     nm_mask_backward_wreg(w, logits, grad_or_None, n, m, kappa, tau, seed, offset, lam)
                                                                       -> grad_logits
     nm_mask_harden_pack(w, logits, n, m, with_hard=False)             -> values, indices[, hard]
+    nm_mask_forward_pack(w, logits, n, m, kappa, tau, seed, offset, with_hard=False)
+                                                                      -> w_masked, values, indices[, hard]
     nm_unpack(values, indices, cols, n, m)                            -> w_dense
     nm_prior_init(w, n, m, alpha, with_idx=False)                     -> logits[, prior_idx]
     nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None)
@@ -56,6 +58,7 @@ _SIGNATURES = {
     "nm_mask_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     "nm_mask_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_mask_backward_wreg": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P]),
+    "nm_mask_forward_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
@@ -271,6 +274,27 @@ def nm_mask_harden_pack(w, logits, n, m, with_hard=False, out=None):
     return (values, indices, hard) if with_hard else (values, indices)
 
 
+def nm_mask_forward_pack(w, logits, n, m, kappa, tau, seed, offset, with_hard=False, out=None):
+    """(w_masked, values, indices[, hard]): nm_mask_forward and nm_mask_harden_pack of the same
+    inputs in one call (one pass over w and the logits for 2:4 when cols/4 is a multiple of 8)."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    wpr = index_words_per_row(cols, n, m)
+    lshape = _logit_shape(rows, cols, n, m)
+    if out is None:
+        out = (torch.empty_like(w), torch.empty((rows, cols // m * n), dtype=w.dtype, device=w.device),
+               torch.empty((rows, wpr), dtype=torch.int32, device=w.device),
+               torch.empty((rows, cols // m), dtype=torch.uint8, device=w.device) if with_hard else None)
+    w_masked, values, indices, hard = out
+    st = lib().nm_mask_forward_pack(
+        ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)), _dev(w, "w"),
+        _dev(logits, "logits", torch.float32, lshape), _dev(w_masked, "w_masked", w.dtype, w.shape),
+        _dev(values, "values", w.dtype, (rows, cols // m * n)), _dev(indices, "indices", torch.int32, (rows, wpr)),
+        None if hard is None else _dev(hard, "hard", torch.uint8, (rows, cols // m)), _stream(w.device))
+    _check(st, "nm_mask_forward_pack")
+    return (w_masked, values, indices, hard) if hard is not None else (w_masked, values, indices)
+
+
 def nm_unpack(values, indices, cols, n, m, out=None):
     """Dense weights with +0.0 at dropped positions."""
     rows = values.shape[0]
@@ -407,7 +431,8 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
     return rows * cols // m * n * elem_bytes + rows * index_words_per_row(cols, n, m) * 4
 
 
-__all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_backward_wreg", "nm_mask_harden_pack", "nm_unpack",
+__all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_backward_wreg", "nm_mask_harden_pack",
+           "nm_mask_forward_pack", "nm_unpack",
            "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise",
            "nm_debug_copy", "nm_sparse_matmul", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",

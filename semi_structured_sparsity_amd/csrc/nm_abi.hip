@@ -231,6 +231,30 @@ nm_status nm_mask_harden_pack(const nm_shape* shape, const void* w, const float*
     return launched(nm::launch_pack(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
+nm_status nm_mask_forward_pack(const nm_shape* shape, const nm_sample* sample, const void* w,
+                               const float* logits, void* w_masked, void* values, uint32_t* indices,
+                               uint8_t* hard_idx, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !w_masked || !values || !indices) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked) || !aligned16(values) ||
+        !aligned16(indices) || (hard_idx && !aligned16(hard_idx)))
+        return NM_EALIGN;
+    const int64_t gpr = shape->cols / shape->m;
+    if (shape->n == 2 && shape->m == 4 && gpr % 8 == 0) {
+        nm::FwdArgs a{w, logits, w_masked, groups, A, B, noise_key(sample), values, indices, hard_idx};
+        return launched(nm::launch_forward_pack(shape->wtype, a, (hipStream_t)stream));
+    }
+    // other shapes: the two passes one after the other, with the same results
+    if ((st = nm_mask_forward(shape, sample, w, logits, w_masked, stream)) != NM_OK) return st;
+    return nm_mask_harden_pack(shape, w, logits, values, indices, hard_idx, stream);
+}
+
 nm_status nm_unpack(const nm_shape* shape, const void* values, const uint32_t* indices, void* w_dense,
                     void* stream) {
     int64_t groups;

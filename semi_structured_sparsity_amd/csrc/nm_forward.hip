@@ -6,6 +6,10 @@ namespace nm {
 // ------------------------------------------------------------------------------------------
 // Forward: w_masked = w * m (MODE 0), or the soft mask m itself in fp32 (MODE 1, diagnostic).
 // Soft mask (Fig. 3 caption, weighted averaging): m_j = sum over candidates k keeping j of y_k.
+// MODE 2 (2:4 only) also writes the packed form of the hard mask from the weights and logits the
+// forward has already loaded, so a step that needs both reads them once: per thread two groups,
+// whose 2-bit fields make one index byte ("Accelerating Sparse Deep Neural Networks" summary
+// page, section 3.1), with the hard mask the first argmax of the logits, as nm_mask_harden_pack.
 
 template <int N, int M, typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
@@ -22,7 +26,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     float l[PK];
     load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
     float w[P * M];
-    if constexpr (MODE == 0)
+    if constexpr (MODE != 1)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     float h[PK];
     thread_noise<N, M>(a.nk, g0, h);
@@ -36,13 +40,52 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < M; ++j) {
             const float mj = sj[j] * inv;
-            out[p * M + j] = MODE == 0 ? w[p * M + j] * mj : mj;
+            out[p * M + j] = MODE != 1 ? w[p * M + j] * mj : mj;
         }
     }
-    if constexpr (MODE == 0)
+    if constexpr (MODE != 1)
         store_from_float<T, P * M>(reinterpret_cast<typename T::storage*>(a.out) + g0 * M, full, nvalid * M, out);
     else
         store_f32<P * M, (P * M * 4) % 16 == 0 ? 16 : 8>(reinterpret_cast<float*>(a.out) + g0 * M, full, nvalid * M, out);
+    if constexpr (MODE == 2) {
+        static_assert(N == 2 && M == 4 && P == 2, "two groups of four fill one index byte");
+        // every thread is full here: the host takes this path only when cols/4 is a multiple of 8
+        uint32_t vals[P * N], byte = 0u, hard = 0u;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const float* lp = l + p * K;
+            float best = lp[0];
+            int bk = 0;
+            uint32_t keep = cand_keep<N, M, 0>();
+            static_for<1, K>([&](auto kc) NM_INLINE {
+                constexpr int k = decltype(kc)::value;
+                const bool up = lp[k] > best;  // a NaN never wins: candidate 0 keeps its place
+                best = up ? lp[k] : best;
+                bk = up ? k : bk;
+                keep = up ? cand_keep<N, M, k>() : keep;
+            });
+            hard |= (uint32_t)bk << (8 * p);
+#pragma unroll
+            for (int tt = 0; tt < N; ++tt) {
+                const int pos = __builtin_ctz(keep);  // kept positions in ascending order
+                keep &= keep - 1;
+                float x = w[p * M];
+#pragma unroll
+                for (int j = 1; j < M; ++j) x = pos == j ? w[p * M + j] : x;
+                // the weight's own bits: a bf16 widened to fp32 keeps them in the upper half
+                vals[p * N + tt] = T::bytes == 2 ? __float_as_uint(x) >> 16 : __float_as_uint(x);
+                byte |= (uint32_t)pos << (2 * (p * N + tt));
+            }
+        }
+        if constexpr (T::bytes == 2) {
+            nt_store(reinterpret_cast<uint16_t*>(a.values) + g0 * N,
+                     make_uint2(vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)));
+        } else {
+            nt_store(reinterpret_cast<uint32_t*>(a.values) + g0 * N, make_uint4(vals[0], vals[1], vals[2], vals[3]));
+        }
+        __builtin_nontemporal_store((uint8_t)byte, reinterpret_cast<uint8_t*>(a.indices) + t);  // byte t
+        if (a.hard) __builtin_nontemporal_store((uint16_t)hard, reinterpret_cast<uint16_t*>(a.hard + g0));
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -284,6 +327,12 @@ static hipError_t fwd_nmt(const FwdArgs& a, bool soft, hipStream_t s) {
 }
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft, hipStream_t s) {
     NM_DISPATCH(fwd_nmt, n, m, wtype, a, soft, s);
+}
+hipError_t launch_forward_pack(int wtype, const FwdArgs& a, hipStream_t s) {
+    const int64_t threads = (a.groups + Sample<2, 4>::P - 1) / Sample<2, 4>::P;
+    if (wtype == 1) k_forward<2, 4, BF16, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
+    else k_forward<2, 4, F32, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
+    return hipGetLastError();
 }
 int64_t monitor_parts(int n, int m, int64_t groups) {
     const int P = groups_per_thread(n, m);

@@ -19,6 +19,10 @@ struct FwdArgs {
     int64_t groups;      // rows * cols / m
     float A, B;          // kappa*log2(e)/tau, 1/tau
     NoiseKey nk;
+    // forward + pack in one pass (launch_forward_pack): the packed form of the hard mask
+    void* values;
+    uint32_t* indices;
+    uint8_t* hard;       // may be null
 };
 
 struct MonitorArgs {
@@ -95,6 +99,8 @@ struct SpmmArgs {
 hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s);
 
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_mask, hipStream_t s);
+// 2:4 only, rows whose index bits fill whole words (cols/4 a multiple of 8)
+hipError_t launch_forward_pack(int wtype, const FwdArgs& a, hipStream_t s);
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backward_wreg(int n, int m, int wtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);

@@ -55,6 +55,7 @@ def test_bad_shapes_are_rejected_on_the_host(kw, status):
     assert L.nm_mask_backward(sh, _sample(), FAKE, FAKE, FAKE, FAKE, None) == status
     assert L.nm_mask_backward_wreg(sh, _sample(), 0.5, FAKE, FAKE, FAKE, FAKE, None) == status
     assert L.nm_mask_harden_pack(sh, FAKE, FAKE, FAKE, FAKE, None, None) == status
+    assert L.nm_mask_forward_pack(sh, _sample(), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == status
     assert L.nm_unpack(sh, FAKE, FAKE, FAKE, None) == status
     assert L.nm_debug_noise(sh, _sample(), FAKE, None) == status
     assert L.nm_debug_soft_mask(sh, _sample(), FAKE, FAKE, None) == status
@@ -228,3 +229,20 @@ def test_regulariser_backward_pointer_rules():
                  (FAKE, FAKE, FAKE, ODD), (FAKE, FAKE, None, ODD)]:
         assert L.nm_mask_backward_wreg(sh, smp, 0.5, *args, None) == NM_EALIGN
     assert L.nm_mask_backward_wreg(_shape(rows=0), smp, 0.5, None, None, None, None, None) == NM_OK
+
+
+def test_forward_pack_pointer_rules():
+    """Every pointer but hard_idx is required; all must be 16-byte aligned; a bad sample is
+    refused; an empty matrix launches nothing."""
+    L = S.lib()
+    sh, smp = _shape(), _sample()
+    args = [FAKE] * 5
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert L.nm_mask_forward_pack(sh, smp, *a, None, None) == NM_EINVAL
+        a[i] = ODD
+        assert L.nm_mask_forward_pack(sh, smp, *a, None, None) == NM_EALIGN
+    assert L.nm_mask_forward_pack(sh, smp, *args, ODD, None) == NM_EALIGN
+    assert L.nm_mask_forward_pack(sh, _sample(1.0, 0.0), *args, None, None) == NM_EINVAL
+    assert L.nm_mask_forward_pack(_shape(rows=0), smp, None, None, None, None, None, None, None) == NM_OK
