@@ -98,6 +98,104 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
     }
 }
 
+// Groups of eight whose rows' index bits fill whole 32-bit words: one group per thread on a flat
+// grid.  A full block reads its logits as one coalesced span through the sampling kernels' LDS
+// tile (lanes on consecutive vectors instead of 112- or 280-byte runs per lane), and each wave
+// assembles its 64 groups' fields, 6N whole words, in its own LDS words.  Lanes past the end take
+// part in the wave's word assembly with no fields; only the last block has such lanes, and it is
+// not staged, so no block barrier is reached by a subset of the block.
+template <int N, typename T>
+__global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
+    constexpr int M = 8, BITS = 3;
+    using S = Sample<N, M>;
+    constexpr int K = S::K;
+    static_assert(S::P == 1 && S::PK == K, "one group per thread");
+    constexpr int WW = 64 * N * BITS / 32;
+    static_assert(64 * N * BITS % 32 == 0, "a wave's fields fill whole words");
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
+    __shared__ uint32_t words[kThreads / 64 * WW];
+    const int64_t groups = a.rows * a.gpr;
+    const int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int nvalid = g0 < groups ? 1 : 0;
+    const bool full = nvalid == 1;
+    const bool staged = block_full<N, M>(groups);  // uniform over the block
+    float l[K];
+    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+    uint32_t raw[M];
+    if (full) load_group_raw<T, M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true, raw);
+    const int lane = threadIdx.x & 63;
+    uint32_t* ww = words + (threadIdx.x >> 6) * WW;
+    for (int i = lane; i < WW; i += 64) ww[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (full) {
+        // first largest logit; a NaN never compares greater, so it never displaces candidate 0
+        float best = l[0];
+        int bk = 0;
+        uint32_t keep = cand_keep<N, M, 0>();
+        static_for<1, K>([&](auto kc) NM_INLINE {
+            constexpr int k = decltype(kc)::value;
+            const bool up = l[k] > best;
+            best = up ? l[k] : best;
+            bk = up ? k : bk;
+            keep = up ? cand_keep<N, M, k>() : keep;
+        });
+        uint32_t v[N];
+        uint64_t acc = 0;
+#pragma unroll
+        for (int tt = 0; tt < N; ++tt) {
+            const int p = __builtin_ctz(keep);  // kept positions in ascending order
+            keep &= keep - 1;
+            uint32_t x = raw[0];
+#pragma unroll
+            for (int j = 1; j < M; ++j) x = p == j ? raw[j] : x;
+            v[tt] = x;
+            acc |= (uint64_t)p << (tt * BITS);
+        }
+        store_group_raw<T, N>(reinterpret_cast<typename T::storage*>(a.values) + g0 * N, true, v);
+        if (a.hard) __builtin_nontemporal_store((uint8_t)bk, a.hard + g0);
+        const int lb = lane * N * BITS;  // the thread's first bit in the wave's words
+        atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
+        if ((lb % 32) + N * BITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int64_t gw0 = g0 - lane;  // the wave's first group, a multiple of 64
+    if (gw0 < groups) {
+        const int ngw = (int)(groups - gw0 < 64 ? groups - gw0 : 64);
+        const int nwords = (ngw * N * BITS + 31) / 32;
+        uint32_t* idx = a.indices + gw0 * N * BITS / 32;
+        for (int i = lane; i < nwords; i += 64) nt_store(idx + i, ww[i]);
+    }
+}
+
+// Unpack of groups of eight on the same flat stream: one group per thread, its fields read
+// straight from the index words (a wave's fields are 6N consecutive words).
+template <int N, typename T>
+__global__ __launch_bounds__(kThreads) void k_unpack_flat8(UnpackArgs a) {
+    constexpr int M = 8, BITS = 3;
+    const int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (g0 >= a.rows * a.gpr) return;
+    uint32_t v[N], o[M];
+    load_group_raw<T, N>(reinterpret_cast<const typename T::storage*>(a.values) + g0 * N, true, v);
+    const int64_t lb = g0 * N * BITS;  // the group's first bit in the flat stream
+    const uint32_t* idx = a.indices + lb / 32;
+    uint64_t acc = idx[0];
+    if ((lb % 32) + N * BITS > 32) acc |= (uint64_t)idx[1] << 32;  // only when the fields straddle
+    acc >>= lb % 32;
+    uint32_t pos[N];
+#pragma unroll
+    for (int tt = 0; tt < N; ++tt) pos[tt] = (uint32_t)(acc >> (tt * BITS)) & 7u;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        uint32_t x = 0u;  // +0.0 where nothing is kept
+#pragma unroll
+        for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[tt] : x;  // later field wins
+        o[j] = x;
+    }
+    store_group_raw<T, M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, o);
+}
+
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
     // Each thread reads the one or two index words that hold its fields straight from memory
@@ -371,6 +469,12 @@ static hipError_t pack_nmt(PackArgs a, hipStream_t s) {
             return hipGetLastError();
         }
     }
+    if constexpr (M == 8) {
+        if ((a.gpr * N * 3) % 32 == 0) {  // every row's fields fill whole words: one flat stream
+            k_pack_flat8<N, T><<<grid_for(a.rows * a.gpr), kThreads, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     k_pack<N, M, T><<<tile_grid<N, M, T>(a.rows, a.gpr), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -386,6 +490,12 @@ static hipError_t unpack_nmt(UnpackArgs a, hipStream_t s) {
     if constexpr (M == 4 && N == 2) {
         if (byte_path<N, M>(a.gpr)) {
             k_unpack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (M == 8) {
+        if ((a.gpr * N * 3) % 32 == 0) {  // every row's fields fill whole words: one flat stream
+            k_unpack_flat8<N, T><<<grid_for(a.rows * a.gpr), kThreads, 0, s>>>(a);
             return hipGetLastError();
         }
     }

@@ -336,3 +336,28 @@ def test_usage_training_loop_then_deployment():
     dense = S.nm_unpack(values, indices, 256, n, m).float()
     ref = x.float() @ dense.t().contiguous()
     assert torch.allclose(y, ref, rtol=1e-4, atol=1e-3)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("wtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,gpr", [(7, 32), (13, 64), (129, 32), (2, 96)])
+def test_pack_groups_of_eight_flat_path_is_bit_exact(n, wtype, rows, gpr):
+    """Groups of eight whose rows' fields fill whole words (gpr * n * 3 a multiple of 32) take
+    the flat kernel: one partial block, several full blocks plus a partial one, and ragged
+    waves; values, index words and hard indices bit-exact against the oracle, and the round
+    trip through unpack exact."""
+    m = 8
+    if (gpr * n * 3) % 32:
+        pytest.skip("not on the flat path")
+    _say("pack flat8", n, wtype, rows, gpr)
+    w, L, _, wd, Ld, _ = _inputs(rows, gpr * m, n, m, wtype, 91)
+    values, indices, hard = S.nm_mask_harden_pack(wd, Ld, n, m, with_hard=True)
+    rv, ri, rh = oracle.pack(w, L, n, m)
+    assert np.array_equal(hard.cpu().numpy(), rh)
+    assert np.array_equal(_u32(indices), ri)
+    bits = values.view(torch.int16 if wtype == torch.bfloat16 else torch.int32).cpu().numpy()
+    assert np.array_equal(bits, rv.view(bits.dtype))
+    dense = S.nm_unpack(values, indices, gpr * m, n, m)
+    want = oracle.unpack(rv, ri, gpr * m, n, m)
+    got = dense.view(torch.int16 if wtype == torch.bfloat16 else torch.int32).cpu().numpy()
+    assert np.array_equal(got, want.view(got.dtype))
