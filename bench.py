@@ -456,6 +456,23 @@ def workload_single256(args):
     for p, fn in calls.items():
         fn(0)
         res[p] = {"avg_launch_us": round(_elapsed_ms(fn, reps=200) * 1e3, 2)}
+
+    # the four passes captured into one HIP graph (same arguments on every replay), which takes
+    # the host's per-call cost out of the step
+    def step(r):
+        for fn in calls.values():
+            fn(0)
+    res["step_eager_us"] = round(_elapsed_ms(step, reps=200) * 1e3, 2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(0)
+    res["step_graph_replay_us"] = round(_elapsed_ms(lambda r: g.replay(), reps=200) * 1e3, 2)
     return {"metric": "launch latency, one 256x256 fp32 weight", "unit": "us", "results": res}
 
 

@@ -1,0 +1,97 @@
+"""The entry points can be captured into a HIP graph (through torch's graph capture on the
+current stream): they allocate nothing, synchronise nothing and record no memset.  Each graph is
+replayed several times with eager work and synchronisations between the replays, and every
+replay's outputs are compared bit for bit with the eager call's (same arguments, so the same
+noise).  Every call goes through the C ABI."""
+import sys
+
+import pytest
+import torch
+
+import nm_synth
+import semi_structured_sparsity_amd as S
+from oracle_inputs import oracle_prior
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32) if t.is_floating_point() else t
+
+
+def _replay_and_compare(graph, outs, refs, reps=3):
+    for r in range(reps):
+        for o in outs:  # poison the outputs: a replay that writes nothing cannot pass
+            if o.is_floating_point():
+                o.fill_(float("nan"))
+            else:
+                o.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        scratch = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for o, ref in zip(outs, refs):
+            assert torch.equal(_bits(o), _bits(ref)), f"replay {r} differs from the eager call"
+
+
+@pytest.mark.parametrize("shape,wtype", [((256, 256), torch.float32), ((4096, 4096), torch.bfloat16)])
+def test_layer_step_replays_as_a_graph(shape, wtype):
+    n, m, kappa, tau, seed, off = 2, 4, 100.0, 4.0, 5, 7
+    rows, cols = shape
+    _say("graph step", shape, wtype)
+    w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, wtype, 0.02, 3, logits="prior", prior=oracle_prior,
+                                     device=DEV)
+    out, dl = torch.empty_like(w), torch.empty_like(L)
+    values = torch.empty((rows, cols // 2), dtype=wtype, device=DEV)
+    indices = torch.empty((rows, cols // 32), dtype=torch.int32, device=DEV)
+    dense = torch.empty_like(w)
+
+    def step():
+        S.nm_mask_forward(w, L, n, m, kappa, tau, seed, off, out=out)
+        S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, off, out=dl)
+        S.nm_mask_harden_pack(w, L, n, m, out=(values, indices, None))
+        S.nm_unpack(values, indices, cols, n, m, out=dense)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in (out, dl, values, indices, dense)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    _replay_and_compare(g, [out, dl, values, indices, dense], refs)
+
+
+@pytest.mark.parametrize("tokens", [1, 16, 256])
+def test_sparse_product_replays_as_a_graph(tokens):
+    """Decode- and prefill-sized products of a packed LLaMA-7B-shaped weight (4096x4096)."""
+    _say("graph spmm", tokens)
+    w, L, _ = nm_synth.matrix_inputs(4096, 4096, 2, 4, torch.bfloat16, 0.02, 4, device=DEV)
+    values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
+    x = nm_synth.normal((tokens, 4096), 1.0, 5, torch.bfloat16, device=DEV)
+    y = torch.empty((tokens, 4096), dtype=torch.bfloat16, device=DEV)
+    S.nm_sparse_matmul(values, indices, x, out=y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        S.nm_sparse_matmul(values, indices, x, out=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.nm_sparse_matmul(values, indices, x, out=y)
+    _replay_and_compare(g, [y], [ref])
