@@ -47,6 +47,9 @@
  * called from several host threads.  Calls are asynchronous and ordered on `stream` (a
  * hipStream_t passed as void*; NULL is the default stream).  The return value reports argument
  * validation and launch only; execution errors surface at the caller's next synchronisation.
+ * Calls can be captured into a HIP graph on `stream` (none allocates, synchronises or records a
+ * memset); the sample is a launch argument, so a captured forward or backward replays the noise
+ * of the step it was captured with.
  *
  * Errors: arguments are checked on the host before any HIP call; on an error nothing is
  * launched and no output is touched.  An empty matrix (rows == 0 or cols == 0) is valid and
