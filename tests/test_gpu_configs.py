@@ -321,3 +321,27 @@ def test_forward_backward_pack_beyond_2_31_elements():
         assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), oracle._np(rv).view(np.int16))
         rd = oracle.unpack(rv, ri, cols, n, m)
         assert np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(), rd.view(np.int16))
+
+
+def test_pack_groups_of_eight_beyond_2_31_elements():
+    """A 4096 x 524416 bf16 weight at 2:8 (2.15 G elements, 30 GB of logits) on the flat
+    groups-of-eight kernels: every 64-bit offset of the pack and unpack, checked on sampled rows
+    (the last one included) against the oracle, bit-exact."""
+    n, m = 2, 8
+    rows, cols = 4096, 524416  # cols/8 = 65552 groups per row: whole index words per row
+    assert rows * cols > 2**31 and (cols // m * n * 3) % 32 == 0
+    _say("flat8 beyond 2^31", rows, cols)
+    w = nm_synth.normal((rows, cols), 0.02, 95, torch.bfloat16, device=DEV)
+    L = nm_synth.gaussian_logits(rows, cols, n, m, 96, device=DEV)
+    values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
+    dense = S.nm_unpack(values, indices, cols, n, m)
+    torch.cuda.synchronize()
+    for r in (0, 2731, rows - 1):
+        rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
+        assert np.array_equal(hard[r:r + 1].cpu().numpy(), rh), f"hard row {r}"
+        assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri), f"indices row {r}"
+        assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), oracle._np(rv).view(np.int16)), f"values row {r}"
+        rd = oracle.unpack(rv, ri, cols, n, m)
+        assert np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(), rd.view(np.int16)), f"dense row {r}"
+    del w, L, values, indices, hard, dense
+    torch.cuda.empty_cache()
