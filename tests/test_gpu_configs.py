@@ -321,6 +321,13 @@ def test_forward_backward_pack_beyond_2_31_elements():
         assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), oracle._np(rv).view(np.int16))
         rd = oracle.unpack(rv, ri, cols, n, m)
         assert np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(), rd.view(np.int16))
+    # the one-pass forward + pack on the same inputs: equal, bit for bit, to the two passes
+    del dense
+    fw, fv, fi, fh = S.nm_mask_forward_pack(w, L, n, m, kappa, tau, 5, 1, with_hard=True)
+    assert torch.equal(_bits(fv), _bits(values)) and torch.equal(fi, indices) and torch.equal(fh, hard)
+    del values, indices, hard, fv, fi, fh
+    out = S.nm_mask_forward(w, L, n, m, kappa, tau, 5, 1)
+    assert torch.equal(_bits(fw), _bits(out))
 
 
 def test_pack_groups_of_eight_beyond_2_31_elements():
