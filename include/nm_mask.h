@@ -49,7 +49,8 @@
  * validation and launch only; execution errors surface at the caller's next synchronisation.
  * Calls can be captured into a HIP graph on `stream` (none allocates, synchronises or records a
  * memset); the sample is a launch argument, so a captured forward or backward replays the noise
- * of the step it was captured with.
+ * of the step it was captured with, unless the step offset is read from device memory
+ * (nm_mask_forward_offset_dev, nm_mask_backward_offset_dev).
  *
  * Errors: arguments are checked on the host before any HIP call; on an error nothing is
  * launched and no output is touched.  An empty matrix (rows == 0 or cols == 0) is valid and
@@ -138,6 +139,22 @@ nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample
 nm_status nm_mask_backward(const nm_shape *shape, const nm_sample *sample, const void *w,
                            const float *logits, const void *grad_w_masked, float *grad_logits,
                            void *stream);
+
+/* nm_mask_forward and nm_mask_backward with the step offset read from device memory when the
+ * kernels run, for a training step captured once into a HIP graph and replayed at every step:
+ * the caller updates *offset_dev (for instance with a stream-ordered copy or a one-element
+ * kernel) before each replay, and each replay samples that step's noise.  The results are those
+ * of nm_mask_forward / nm_mask_backward with sample->offset = *offset_dev (sample->offset is
+ * not used).
+ *   offset_dev  one uint64_t in device memory, 8-byte aligned (NM_EALIGN otherwise), read
+ *               on the stream; NULL is NM_EINVAL
+ *   the other arguments and errors  as nm_mask_forward / nm_mask_backward */
+nm_status nm_mask_forward_offset_dev(const nm_shape *shape, const nm_sample *sample,
+                                     const uint64_t *offset_dev, const void *w, const float *logits,
+                                     void *w_masked, void *stream);
+nm_status nm_mask_backward_offset_dev(const nm_shape *shape, const nm_sample *sample,
+                                      const uint64_t *offset_dev, const void *w, const float *logits,
+                                      const void *grad_w_masked, float *grad_logits, void *stream);
 
 /* Backward with a weight regulariser in the loss (MaskLLM project page, Table 3: weight
  * regularisation helps mask learning).  The page gives no formula; this entry point takes it as

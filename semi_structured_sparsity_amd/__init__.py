@@ -59,6 +59,8 @@ _SIGNATURES = {
     "nm_mask_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_mask_backward_wreg": (ctypes.c_int, [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P]),
     "nm_mask_forward_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "nm_mask_forward_offset_dev": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "nm_mask_backward_offset_dev": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "nm_mask_harden_pack": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
@@ -171,14 +173,29 @@ def _logit_shape(rows, cols, n, m):
 # ---------------------------------------------------------------------------------------------
 # the four entry points of the layer
 
+def _offset_dev(offset):
+    """A one-element int64 device tensor holding the step offset (read when the kernels run)."""
+    if offset.dtype != torch.int64 or offset.numel() != 1:
+        raise TypeError("a device offset must be a one-element int64 tensor")
+    return _dev(offset, "offset")
+
+
 def nm_mask_forward(w, logits, n, m, kappa, tau, seed, offset, out=None):
-    """Masked frozen weights w * m (MaskLLM project page, Fig. 3 caption)."""
+    """Masked frozen weights w * m (MaskLLM project page, Fig. 3 caption).  `offset` is the
+    step: an int, or a one-element int64 tensor on the device, read when the kernel runs
+    (nm_mask_forward_offset_dev: a captured graph then samples each replay's step)."""
     rows, cols = w.shape
     sh = _shape(rows, cols, n, m, _wtype(w.dtype))
     out = torch.empty_like(w) if out is None else out
+    lshape = _logit_shape(rows, cols, n, m)
+    if isinstance(offset, torch.Tensor):
+        st = lib().nm_mask_forward_offset_dev(
+            ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, 0)), _offset_dev(offset), _dev(w, "w"),
+            _dev(logits, "logits", torch.float32, lshape), _dev(out, "out", w.dtype, w.shape), _stream(w.device))
+        _check(st, "nm_mask_forward_offset_dev")
+        return out
     st = lib().nm_mask_forward(ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)),
-                               _dev(w, "w"), _dev(logits, "logits", torch.float32,
-                                                  _logit_shape(rows, cols, n, m)),
+                               _dev(w, "w"), _dev(logits, "logits", torch.float32, lshape),
                                _dev(out, "out", w.dtype, w.shape), _stream(w.device))
     _check(st, "nm_mask_forward")
     return out
@@ -219,11 +236,19 @@ def nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_samp
 
 
 def nm_mask_backward(w, logits, grad, n, m, kappa, tau, seed, offset, out=None):
-    """Gradient of the loss with respect to the logits (overwrites `out` if given)."""
+    """Gradient of the loss with respect to the logits (overwrites `out` if given).  `offset` as
+    in nm_mask_forward (an int, or a one-element int64 device tensor)."""
     rows, cols = w.shape
     sh = _shape(rows, cols, n, m, _wtype(w.dtype))
     lshape = _logit_shape(rows, cols, n, m)
     out = torch.empty(lshape, dtype=torch.float32, device=w.device) if out is None else out
+    if isinstance(offset, torch.Tensor):
+        st = lib().nm_mask_backward_offset_dev(
+            ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, 0)), _offset_dev(offset), _dev(w, "w"),
+            _dev(logits, "logits", torch.float32, lshape), _dev(grad, "grad", w.dtype, w.shape),
+            _dev(out, "out", torch.float32, lshape), _stream(w.device))
+        _check(st, "nm_mask_backward_offset_dev")
+        return out
     st = lib().nm_mask_backward(ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)),
                                 _dev(w, "w"), _dev(logits, "logits", torch.float32, lshape),
                                 _dev(grad, "grad", w.dtype, w.shape),
@@ -236,6 +261,8 @@ def nm_mask_backward_wreg(w, logits, grad, n, m, kappa, tau, seed, offset, lam, 
     """Logit gradient of the task loss (upstream `grad`, or None for none) plus the weight
     regulariser lam * sum (w * m)^2 (MaskLLM project page, Table 3; the squared norm of the
     masked weights is the reading taken, the page gives no formula)."""
+    if isinstance(offset, torch.Tensor):
+        raise TypeError("nm_mask_backward_wreg takes the step offset as an int")
     rows, cols = w.shape
     sh = _shape(rows, cols, n, m, _wtype(w.dtype))
     lshape = _logit_shape(rows, cols, n, m)

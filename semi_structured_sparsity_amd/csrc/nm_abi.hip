@@ -138,6 +138,41 @@ int64_t nm_monitor_workspace_bytes(const nm_shape* shape) {
     return 8 * nm::monitor_parts(shape->n, shape->m, groups);
 }
 
+nm_status nm_mask_forward_offset_dev(const nm_shape* shape, const nm_sample* sample,
+                                     const uint64_t* offset_dev, const void* w, const float* logits,
+                                     void* w_masked, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!offset_dev || !w || !logits || !w_masked) return NM_EINVAL;
+    if (((uintptr_t)offset_dev & 7u) != 0 || !aligned16(w) || !aligned16(logits) || !aligned16(w_masked))
+        return NM_EALIGN;
+    nm::FwdArgs a{w, logits, w_masked, groups, A, B, noise_key(sample), nullptr, nullptr, nullptr, offset_dev};
+    return launched(nm::launch_forward(shape->n, shape->m, shape->wtype, a, false, (hipStream_t)stream));
+}
+
+nm_status nm_mask_backward_offset_dev(const nm_shape* shape, const nm_sample* sample,
+                                      const uint64_t* offset_dev, const void* w, const float* logits,
+                                      const void* grad_w_masked, float* grad_logits, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!offset_dev || !w || !logits || !grad_w_masked || !grad_logits) return NM_EINVAL;
+    if (((uintptr_t)offset_dev & 7u) != 0 || !aligned16(w) || !aligned16(logits) ||
+        !aligned16(grad_w_masked) || !aligned16(grad_logits))
+        return NM_EALIGN;
+    nm::BwdArgs a{w, logits, grad_w_masked, grad_logits, groups, A, B, C, noise_key(sample), 0.0f, offset_dev};
+    return launched(nm::launch_backward(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
+}
+
 nm_status nm_mask_forward_monitor(const nm_shape* shape, const nm_sample* sample, const void* w,
                                   const float* logits, void* w_masked, const uint8_t* prev_sample,
                                   uint8_t* sample_idx, double* stats, void* workspace,

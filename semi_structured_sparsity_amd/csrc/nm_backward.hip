@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     if constexpr (REG != 2)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.grad) + g0 * M, full, nvalid * M, gw);
     float h[PK];
-    thread_noise<N, M>(a.nk, g0, h);
+    thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
 
     float dl[PK];
 #pragma unroll

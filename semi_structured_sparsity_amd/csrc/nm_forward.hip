@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     if constexpr (MODE != 1)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     float h[PK];
-    thread_noise<N, M>(a.nk, g0, h);
+    thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
 
     float out[P * M];
 #pragma unroll
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
 #pragma unroll
     for (int p = 0; p < P; ++p) prev[p] = (a.prev && p < nvalid) ? a.prev[g0 + p] : 0u;
     float h[PK];
-    thread_noise<N, M>(a.f.nk, g0, h);
+    thread_noise<N, M>(step_key(a.f.nk, a.f.offset_dev), g0, h);
     if constexpr (M != 4) __syncthreads();  // the candidate table is in LDS
 
     float out[P * M];

@@ -12,6 +12,15 @@ struct NoiseKey {
     uint32_t off0, off1;  // offset lo, hi
 };
 
+// The noise key of a launch: the offset is the launch argument, or, when offset_dev is given,
+// the 64-bit value it points to, read when the kernel runs (a graph replayed once per training
+// step then samples fresh noise at each step).  The pointer is uniform: one scalar load.
+__device__ __forceinline__ NoiseKey step_key(const NoiseKey& nk, const uint64_t* offset_dev) {
+    if (!offset_dev) return nk;
+    const uint64_t off = *offset_dev;
+    return NoiseKey{nk.k0, nk.k1, (uint32_t)off, (uint32_t)(off >> 32)};
+}
+
 struct FwdArgs {
     const void* w;
     const float* logits;
@@ -23,6 +32,7 @@ struct FwdArgs {
     void* values;
     uint32_t* indices;
     uint8_t* hard;       // may be null
+    const uint64_t* offset_dev;  // may be null: the offset then comes from nk
 };
 
 struct MonitorArgs {
@@ -43,6 +53,7 @@ struct BwdArgs {
     float A, B, C;       // C = kappa/tau
     NoiseKey nk;
     float lam2;          // 2 * lambda of the weight regulariser (launch_backward_wreg only)
+    const uint64_t* offset_dev;  // may be null: the offset then comes from nk
 };
 
 struct PackArgs {

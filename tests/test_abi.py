@@ -246,3 +246,19 @@ def test_forward_pack_pointer_rules():
     assert L.nm_mask_forward_pack(sh, smp, *args, ODD, None) == NM_EALIGN
     assert L.nm_mask_forward_pack(sh, _sample(1.0, 0.0), *args, None, None) == NM_EINVAL
     assert L.nm_mask_forward_pack(_shape(rows=0), smp, None, None, None, None, None, None, None) == NM_OK
+
+
+def test_device_offset_pointer_rules():
+    """The step offset pointer is required and 8-byte aligned; the other pointers follow
+    nm_mask_forward / nm_mask_backward; a bad sample is still refused."""
+    L = S.lib()
+    sh, smp = _shape(), _sample()
+    ODD8 = ctypes.c_void_p((1 << 20) + 4)
+    assert L.nm_mask_forward_offset_dev(sh, smp, None, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_forward_offset_dev(sh, smp, ODD8, FAKE, FAKE, FAKE, None) == NM_EALIGN
+    assert L.nm_mask_forward_offset_dev(sh, smp, ctypes.c_void_p((1 << 20) + 8), FAKE, FAKE, ODD, None) == NM_EALIGN
+    assert L.nm_mask_backward_offset_dev(sh, smp, None, FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_backward_offset_dev(sh, smp, ODD8, FAKE, FAKE, FAKE, FAKE, None) == NM_EALIGN
+    assert L.nm_mask_backward_offset_dev(sh, smp, FAKE, FAKE, FAKE, None, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_forward_offset_dev(sh, _sample(1.0, 0.0), FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
+    assert L.nm_mask_backward_offset_dev(_shape(rows=0), smp, None, None, None, None, None, None) == NM_OK

@@ -95,3 +95,45 @@ def test_sparse_product_replays_as_a_graph(tokens):
     with torch.cuda.graph(g):
         S.nm_sparse_matmul(values, indices, x, out=y)
     _replay_and_compare(g, [y], [ref])
+
+
+@pytest.mark.parametrize("wtype", [torch.bfloat16, torch.float32])
+def test_training_step_graph_with_the_offset_on_the_device(wtype):
+    """A forward + backward captured once, with the step offset read from a device tensor, and
+    replayed for steps 3, 4, 11 and 2**40 + 5: each replay equals the eager calls at that step
+    (fresh noise per replay), bit for bit."""
+    n, m, kappa, tau, seed = 2, 4, 100.0, 4.0, 21
+    rows, cols = 96, 512
+    _say("graph device offset", wtype)
+    w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, wtype, 0.5, 22, device=DEV)
+    step = torch.zeros(1, dtype=torch.int64, device=DEV)
+    out, dl = torch.empty_like(w), torch.empty_like(L)
+
+    def run():
+        S.nm_mask_forward(w, L, n, m, kappa, tau, seed, step, out=out)
+        S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, step, out=dl)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    prev = None
+    for k in (3, 4, 11, 2**40 + 5):
+        step.fill_(k)
+        out.fill_(float("nan"))
+        dl.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        ref_f = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, k)
+        ref_b = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, k)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref_f)), f"forward replay at step {k}"
+        assert torch.equal(_bits(dl), _bits(ref_b)), f"backward replay at step {k}"
+        if prev is not None:
+            assert not torch.equal(_bits(out), prev), "each step samples fresh noise"
+        prev = _bits(out).clone()
