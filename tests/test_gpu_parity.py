@@ -165,6 +165,30 @@ def test_forward_and_backward_are_deterministic_and_fresh_per_step():
     assert torch.equal(a, b) and not torch.equal(a, c)
 
 
+def test_resume_is_exact_on_the_gpu(tmp_path):
+    """Ten annealed steps straight equal five steps, a save and reload of the inputs, and the
+    last five (the noise is a function of (seed, offset) alone), for the forward, backward and
+    pack outputs, bit for bit."""
+    n, m, seed, steps = 2, 4, 17, 10
+    w, L, G = nm_synth.matrix_inputs(48, 512, n, m, torch.bfloat16, 0.02, 61, device=DEV)
+
+    def run(w, L, G, s):
+        f = s / (steps - 1)
+        kappa, tau = 100.0 + 400.0 * f, 4.0 + (0.05 - 4.0) * f
+        out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, s)
+        dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, s)
+        v, i = S.nm_mask_harden_pack(w, L, n, m)
+        return [t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32) for t in (out, dl, v, i)]
+
+    straight = [run(w, L, G, s) for s in range(steps)]
+    torch.save({"w": w.cpu(), "L": L.cpu(), "G": G.cpu()}, tmp_path / "ckpt.pt")
+    ck = torch.load(tmp_path / "ckpt.pt", weights_only=True)
+    w2, L2, G2 = ck["w"].to(DEV), ck["L"].to(DEV), ck["G"].to(DEV)
+    for s in range(steps // 2, steps):
+        for a_, b_ in zip(straight[s], run(w2, L2, G2, s)):
+            assert torch.equal(a_, b_), f"step {s} differs after the reload"
+
+
 # ---------------------------------------------------------------------------------------------
 # hard mask, pack, unpack: bit-exact
 
