@@ -385,3 +385,17 @@ def test_pack_groups_of_eight_flat_path_is_bit_exact(n, wtype, rows, gpr):
     want = oracle.unpack(rv, ri, gpr * m, n, m)
     got = dense.view(torch.int16 if wtype == torch.bfloat16 else torch.int32).cpu().numpy()
     assert np.array_equal(got, want.view(got.dtype))
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (2, 8), (4, 8)])
+def test_bf16_output_is_the_rne_rounding_of_the_fp32_product(n, m):
+    """The forward's bf16 output is, bit for bit, torch's round-to-nearest-even conversion of
+    the fp32 product of the weights with the kernel's own fp32 soft mask (nm_debug_soft_mask
+    with the same sample): the rounding step is the library routine's."""
+    kappa, tau, seed, off = 100.0, 1.0, 9, 4
+    _say("bf16 rne", n, m)
+    _, _, _, wd, Ld, _ = _inputs(37, 23 * m, n, m, torch.bfloat16, 71)
+    out = S.nm_mask_forward(wd, Ld, n, m, kappa, tau, seed, off)
+    soft = S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed, off)
+    want = (wd.float() * soft).to(torch.bfloat16)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
