@@ -399,3 +399,22 @@ def test_bf16_output_is_the_rne_rounding_of_the_fp32_product(n, m):
     soft = S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed, off)
     want = (wd.float() * soft).to(torch.bfloat16)
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (2, 8), (4, 8)])
+def test_hard_mask_is_the_large_kappa_limit_of_the_soft_mask(n, m):
+    """Where kappa times a group's top-two logit gap exceeds the spread of the Gumbel noise
+    (17.33 + 2.86) by 40, every other candidate's probability is below e^-39.8 (tau = 1), so the
+    soft mask sampled on the GPU is the hard mask extracted on the GPU to 1e-6."""
+    kappa, tau = 1.0e4, 1.0
+    _say("kappa limit", n, m)
+    _, _, _, wd, Ld, _ = _inputs(64, 32 * m, n, m, torch.float32, 72)
+    soft = S.nm_debug_soft_mask(Ld, n, m, kappa, tau, 3, 5).view(64, 32, m)
+    _, _, hard = S.nm_mask_harden_pack(wd, Ld, n, m, with_hard=True)
+    table = torch.tensor(S.candidate_table(n, m), dtype=torch.int32, device=DEV)
+    keep = ((table[hard.long()].unsqueeze(-1) >> torch.arange(m, device=DEV, dtype=torch.int32)) & 1).float()
+    top2 = torch.topk(Ld, 2, dim=-1).values
+    sure = kappa * (top2[..., 0] - top2[..., 1]) > 60.2
+    assert float(sure.float().mean()) > 0.85  # most groups are decided
+    err = (soft - keep).abs().amax(-1)
+    assert float(err[sure].max()) <= 1e-6
