@@ -126,3 +126,26 @@ def test_monitor_full_llama7b_down_projection():
     nd1 = _check_step(Lc, n, m, kappa, tau, seed, 1, s1, st1, prev)
     _say("  near-tie differences", nd0, nd1, "of", rows * cols // m)
     assert nd0 + nd1 <= 1e-4 * rows * cols // m
+
+
+@pytest.mark.parametrize("n,m,kappa", [(2, 4, 1.0), (2, 4, 3.0), (4, 8, 0.5)])
+def test_sampled_candidates_follow_softmax_of_kappa_logits(n, m, kappa):
+    """Gumbel-max property (a textbook result): over many groups that share one logit vector,
+    the GPU's sampled candidates occur with the probabilities softmax(kappa * l), tested by a
+    chi-square goodness of fit (the same samples fail against the uniform law)."""
+    import scipy.stats
+    K = S.num_candidates(n, m)
+    rows, gpr = 256, 512
+    g = torch.Generator().manual_seed(77 + K)
+    lvec = torch.randn(K, generator=g) * 0.8
+    L = lvec.expand(rows, gpr, K).contiguous().to(DEV)
+    w = torch.ones((rows, gpr * m), dtype=torch.bfloat16, device=DEV)
+    _say("gumbel-max", n, m, kappa)
+    _, sample, _ = S.nm_mask_forward_monitor(w, L, n, m, kappa, 1.0, 123, 0)
+    counts = torch.bincount(sample.view(-1).long(), minlength=K).cpu().double().numpy()
+    p = torch.softmax(kappa * lvec.double(), 0).numpy()
+    total = counts.sum()
+    chi2 = float((((counts - total * p) ** 2) / (total * p)).sum())
+    assert scipy.stats.chi2.sf(chi2, K - 1) > 1e-4, (chi2, counts, total * p)
+    uni = float((((counts - total / K) ** 2) / (total / K)).sum())
+    assert scipy.stats.chi2.sf(uni, K - 1) < 1e-6
