@@ -184,7 +184,8 @@ def kernel_source_hash():
     import hashlib
     import semi_structured_sparsity_amd.build as b
     h = hashlib.sha256()
-    for name in ("nm_forward.hip", "nm_backward.hip", "nm_pack.hip", "nm_layer.hpp", "nm_device.hpp"):
+    for name in ("nm_forward.hip", "nm_backward.hpp", "nm_backward.hip", "nm_backward_wreg.hip", "nm_pack.hip",
+                 "nm_layer.hpp", "nm_device.hpp"):
         h.update(open(os.path.join(b.CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 

@@ -12,8 +12,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("nm_forward.hip", "nm_backward.hip", "nm_pack.hip", "nm_spmm.hip", "nm_abi.hip")]
+           ("nm_forward.hip", "nm_backward.hip", "nm_backward_wreg.hip", "nm_pack.hip", "nm_spmm.hip",
+            "nm_abi.hip")]
 HEADERS = [os.path.join(CSRC, "nm_device.hpp"), os.path.join(CSRC, "nm_layer.hpp"),
+           os.path.join(CSRC, "nm_backward.hpp"),
            os.path.join(CSRC, "nm_kernels.hpp"), os.path.join(ROOT, "include", "nm_mask.h")]
 LIB = os.path.join(PKG, "libnm_mask.so")
 OBJ_DIR = os.path.join(PKG, "_build")

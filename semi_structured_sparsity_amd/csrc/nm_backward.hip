@@ -1,78 +1,7 @@
-// nm_backward.hip -- backward to the logits (plain and with the weight regulariser) and its launchers.
-#include "nm_layer.hpp"
+// nm_backward.hip -- launcher of the plain backward to the logits.
+#include "nm_backward.hpp"
 
 namespace nm {
-
-// ------------------------------------------------------------------------------------------
-// Backward to the logits (Fig. 3 caption: all steps differentiable).  Upstream G = dL/dw_masked:
-//   dL/dy_k = d_k = sum_{j kept by k} G_j w_j,  s = sum_k y_k d_k,
-//   dL/dl_k = (kappa/tau) * y_k * (d_k - s).
-// The noise is regenerated from the same (seed, offset) as the forward.
-//
-// REG adds the weight regulariser lambda * sum (w_j m_j)^2 to the loss (MaskLLM project page,
-// Table 3: weight regularisation helps mask learning; the squared norm of the masked weights is
-// the reading taken, the page gives no formula).  Its gradient on w_masked is 2 lambda w_j m_j,
-// so G_j becomes G_j + 2 lambda w_j m_j, with m_j the soft mask this pass already has.
-//   REG 0: task gradient only;  1: task gradient + regulariser;  2: regulariser only (no G read).
-
-template <int N, int M, typename T, int REG>
-__global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
-    using S = Sample<N, M>;
-    constexpr int K = S::K, P = S::P, PK = S::PK;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t g0 = t * P;
-    if (g0 >= a.groups) return;
-    const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
-    const bool full = nvalid == P;
-
-    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
-    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
-    float l[PK];
-    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
-    float w[P * M], gw[P * M];
-    load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
-    if constexpr (REG != 2)
-        load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.grad) + g0 * M, full, nvalid * M, gw);
-    float h[PK];
-    thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
-
-    float dl[PK];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        float e[K], sj[M];
-        group_exp<N, M>(l + p * K, h + p * K, a.A, a.B, e);
-        const float inv = group_soft<N, M>(e, sj);
-        float aj[M];
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            const float wj = w[p * M + j];
-            if constexpr (REG == 0) {
-                aj[j] = gw[p * M + j] * wj;
-            } else {
-                const float mj = sj[j] * inv;
-                const float up = REG == 1 ? fmaf(a.lam2 * wj, mj, gw[p * M + j]) : (a.lam2 * wj) * mj;
-                aj[j] = up * wj;
-            }
-        }
-        float d[K];
-        float es = 0.0f;
-        static_for<0, K>([&](auto kc) NM_INLINE {
-            constexpr int k = decltype(kc)::value;
-            float dk = 0.0f;
-            static_for<0, M>([&](auto jc) NM_INLINE {
-                constexpr int j = decltype(jc)::value;
-                if constexpr ((cand_keep<N, M, k>() >> j) & 1u) dk += aj[j];
-            });
-            d[k] = dk;
-            es = fmaf(e[k], dk, es);
-        });
-        const float s = es * inv;
-        const float ci = a.C * inv;
-#pragma unroll
-        for (int k = 0; k < K; ++k) dl[p * K + k] = (ci * e[k]) * (d[k] - s);
-    }
-    store_dlogits<N, M>(a.dlogits, g0, full, nvalid, staged, tile, dl);
-}
 
 // ------------------------------------------------------------------------------------------
 // Launchers.
@@ -83,18 +12,8 @@ static hipError_t bwd_nmt(const BwdArgs& a, hipStream_t s) {
     k_backward<N, M, T, 0><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
-template <int N, int M, typename T>
-static hipError_t bwd_wreg_nmt(const BwdArgs& a, hipStream_t s) {
-    const int64_t threads = (a.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
-    if (a.grad) k_backward<N, M, T, 1><<<grid_for(threads), kThreads, 0, s>>>(a);
-    else k_backward<N, M, T, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
-    return hipGetLastError();
-}
 hipError_t launch_backward(int n, int m, int wtype, const BwdArgs& a, hipStream_t s) {
     NM_DISPATCH(bwd_nmt, n, m, wtype, a, s);
-}
-hipError_t launch_backward_wreg(int n, int m, int wtype, const BwdArgs& a, hipStream_t s) {
-    NM_DISPATCH(bwd_wreg_nmt, n, m, wtype, a, s);
 }
 
 }  // namespace nm
