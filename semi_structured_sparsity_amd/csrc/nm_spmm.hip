@@ -351,6 +351,109 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24_skinny(SpmmArgs a) {
     }
 }
 
+// One or two tokens: the product is a matrix-vector product bound by reading the packed rows
+// once, and 16-row matrix-core fragments would make each wave gather 64-byte pieces of 16
+// rows.  Here each wave streams whole packed rows instead: lane L takes the 16-byte chunks
+// L, L + 64, ... of a row (chunk c holds the kept values 8c .. 8c + 7, that is the dense
+// groups 4c .. 4c + 3 and the index bits [16c, 16c + 16) of the row, the upper or lower half
+// of index word c/2).  X, J tokens of `in` bf16, is staged once per block in LDS; the dense
+// column of a kept value is picked out of the two X words of its group by a byte permute
+// whose selector places the chosen bf16 in the upper half of an fp32.  The next chunks are
+// loaded before the current ones are used (the first before the X barrier), and each row ends
+// with a fixed-order wave reduction, so the result is deterministic.
+template <int J>
+__global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_block) {
+    constexpr int U = 4;  // 16-byte chunks per lane in flight
+    extern __shared__ uint4 xs[];  // [J][in / 8] 16-byte pieces of X
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t nch = a.in / 16, xch = a.in / 8;
+    const int64_t rend = (int64_t)(blockIdx.x + 1) * rows_per_block;
+    const int64_t r1 = rend < a.out ? rend : a.out;
+    int64_t r = (int64_t)blockIdx.x * rows_per_block + wv, c0 = 0;
+
+    uint4 v[U];
+    uint32_t iw[U];
+    auto fetch = [&](int64_t rr, int64_t cc, uint4* vv, uint32_t* ii) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = cc + 64 * u + lane;
+            vv[u] = make_uint4(0u, 0u, 0u, 0u);
+            ii[u] = 0u;
+            if (rr < r1 && c < nch) {
+                vv[u] = *reinterpret_cast<const uint4*>(a.values + rr * a.vstride + c * 8);
+                ii[u] = a.indices[rr * a.istride + (c >> 1)];
+            }
+        }
+    };
+    fetch(r, c0, v, iw);
+    for (int64_t c = tid; c < J * xch; c += 512) {
+        const int64_t t = c / xch, k = c - t * xch;
+        xs[c] = *reinterpret_cast<const uint4*>(a.x + t * a.xstride + k * 8);
+    }
+    __syncthreads();
+
+    float acc[J];
+#pragma unroll
+    for (int t = 0; t < J; ++t) acc[t] = 0.0f;
+    while (r < r1) {  // uniform over the wave
+        int64_t rn = r, cn = c0 + 64 * U;
+        if (cn >= nch) {
+            rn = r + 8;
+            cn = 0;
+        }
+        uint4 vn[U];
+        uint32_t iwn[U];
+        fetch(rn, cn, vn, iwn);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + 64 * u + lane;
+            if (c < nch) {
+                const uint32_t bits = iw[u] >> (16 * (int)(c & 1));
+                const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};  // kept pair of group g
+#pragma unroll
+                for (int t = 0; t < J; ++t) {
+                    const uint4 xa = xs[t * xch + 2 * c], xb = xs[t * xch + 2 * c + 1];
+                    const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint32_t p = (bits >> (4 * g + 2 * h)) & 3u;
+                            // bytes 2p, 2p + 1 of {xd[2g + 1], xd[2g]} into bytes 2, 3; zeros below
+                            const uint32_t sel = 0x01000c0cu + p * 0x02020000u;
+                            const float xv = __uint_as_float(__builtin_amdgcn_perm(xd[2 * g + 1], xd[2 * g], sel));
+                            const float wv_ = __uint_as_float(h ? (vw[g] & 0xFFFF0000u) : (vw[g] << 16));
+                            acc[t] = fmaf(wv_, xv, acc[t]);
+                        }
+                    }
+                }
+            }
+        }
+        if (cn == 0) {  // the row is done
+#pragma unroll
+            for (int t = 0; t < J; ++t) {
+                float s = acc[t];
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+                if (lane == 0) {
+                    if (a.ytype == 0)
+                        static_cast<float*>(a.y)[t * a.ystride + r] = s;
+                    else
+                        static_cast<__bf16*>(a.y)[t * a.ystride + r] = (__bf16)s;
+                }
+                acc[t] = 0.0f;
+            }
+        }
+        r = rn;
+        c0 = cn;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v[u] = vn[u];
+            iw[u] = iwn[u];
+        }
+    }
+}
+
 template <int WAVES>
 static hipError_t launch_tile(const SpmmArgs& a, hipStream_t s) {
     using TL = SpTile<WAVES>;
@@ -368,7 +471,26 @@ static hipError_t launch_tile(const SpmmArgs& a, hipStream_t s) {
 // Up to this many tokens the skinny kernel runs; above it the tiles.
 constexpr int64_t SP_SKINNY_MAX_TOKENS = 64;
 
+// Up to this many bf16 of X (all tokens, 48 KB) the row-streaming kernel stages X in LDS.
+constexpr int64_t SP_SPMV_MAX_X = 24576;
+
 hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;  // MI355X
+    if (a.tokens <= 2 && a.tokens * a.in <= SP_SPMV_MAX_X) {
+        // about two blocks of eight waves per CU; every wave ends its row loop, then the block
+        const int64_t target = 2 * (int64_t)cus;
+        const int64_t rpb = (a.out + target - 1) / target;
+        const int64_t grid = (a.out + rpb - 1) / rpb;
+        const size_t smem = (size_t)(a.tokens * a.in * 2);
+        if (a.tokens == 1)
+            k_spmv24<1><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
+        else
+            k_spmv24<2><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
+        return hipGetLastError();
+    }
     if (a.tokens <= SP_SKINNY_MAX_TOKENS) {
         const unsigned gx = (unsigned)((a.out + 15) / 16);
         if (a.tokens <= 16)
@@ -384,10 +506,6 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
     // every CU a block is taken (256 x 256, 128 x 128 or 64 x 64).  With 256 x 256 tiles only,
     // mid-size batches would leave most CUs idle (16 blocks for 4096 W rows at 256 tokens).
     // Deeper pipelines (6 or 9 stages per block instead of 3) were measured no faster.
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;  // MI355X
     auto tiles = [&](int64_t t) { return ((a.out + t - 1) / t) * ((a.tokens + t - 1) / t); };
     if (tiles(256) >= cus) return launch_tile<8>(a, s);
     if (tiles(128) >= cus) return launch_tile<4>(a, s);

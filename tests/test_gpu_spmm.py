@@ -136,13 +136,17 @@ def test_sparse_matmul_each_tile_size_with_ragged_edges(out, inn, tokens, tile):
     assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=torch.float32), y)
 
 
-@pytest.mark.parametrize("out,inn,tokens", [(36, 64, 1), (100, 128, 7), (256, 4160, 32), (68, 192, 33),
-                                             (132, 256, 64), (64, 320, 65), (96, 1024, 128), (4, 64, 128)])
+@pytest.mark.parametrize("out,inn,tokens", [(36, 64, 1), (36, 64, 2), (6000, 128, 1), (5000, 4160, 2),
+                                             (520, 11008, 2), (8, 24640, 1), (40, 12352, 2), (100, 128, 7),
+                                             (256, 4160, 32), (68, 192, 33), (132, 256, 64), (64, 320, 65),
+                                             (96, 1024, 128), (4, 64, 128)])
 @pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
 def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
-    """Up to 64 tokens the product runs on blocks of 16 W rows whose waves split k (fewer k
-    blocks than waves included), above it on the 64 x 64 tiles; every output against the
-    oracle, nothing written past y."""
+    """One or two tokens whose X fits in 48 KB run on the row-streaming kernel (several rows per
+    wave, rows longer than one pass of the wave, X of 2 x 11008 bf16); 24640 columns at one token
+    and 12352 at two are just above that and, like 3 to 64 tokens, run on blocks of 16 W rows
+    whose waves split k (fewer k blocks than waves included); above 64 tokens the 64 x 64 tiles.
+    Every output against the oracle, nothing written past y."""
     _say("spmm few tokens", out, inn, tokens, ytype)
     _, values, indices = _packed_layer(out, inn, 60 + out + tokens, w_std=1.0)
     x = nm_synth.normal((tokens, inn), 1.0, 61, torch.bfloat16, device=DEV)
@@ -157,7 +161,7 @@ def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
     assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=ytype), y)
 
 
-@pytest.mark.parametrize("name_index,tokens", [(4, 1), (6, 16), (0, 128)])
+@pytest.mark.parametrize("name_index,tokens", [(4, 1), (6, 2), (6, 16), (0, 128)])
 def test_sparse_matmul_llama7b_decode_batches(name_index, tokens):
     """Decode-sized batches on full LLaMA-7B-shaped weights, three windows of 128 W rows."""
     name, out, inn = nm_synth.LLAMA2_7B_LAYER[name_index]
