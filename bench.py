@@ -632,7 +632,7 @@ def workload_spmm(args):
     # trace gives the kernels alone)
     weights = sum(mt["rows"] * mt["cols"] for mt in mats)
     batches = {}
-    for tk in (1, 2, 16, 64, 128, 256, 512, 1024, 2048):
+    for tk in (1, 2, 4, 16, 64, 128, 256, 512, 1024, 2048):
         for mt in mats:
             mt["xd"] = nm_synth.normal((tk, mt["cols"]), 1.0, 11 + tk, torch.bfloat16, device=dev)
             mt["yd"] = torch.empty((tk, mt["rows"]), dtype=torch.bfloat16, device=dev)

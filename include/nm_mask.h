@@ -227,8 +227,8 @@ nm_status nm_prior_init(const nm_shape *shape, float alpha, const void *w, float
  * Supported sizes: in a positive multiple of 64 and out a multiple of 4 (else NM_EUNSUPPORTED),
  * any tokens >= 0; out = 0 or tokens = 0 launches nothing.  Pointers 16-byte aligned.  Above
  * 64 tokens the product runs on square tiles of 256, 128 or 64 W rows and tokens, the largest
- * that still gives every compute unit a block (a partial last tile costs a whole one); from 3
- * to 64 tokens, on blocks of 16 W rows that split k and read the packed weights once; at 1 or 2
+ * that still gives every compute unit a block (a partial last tile costs a whole one); from 5
+ * to 64 tokens, on blocks of 16 W rows that split k and read the packed weights once; at 1 to 4
  * tokens whose X is at most 24576 bf16 in all (48 KB), without the matrix cores, each wave
  * streaming whole packed rows against X held in LDS (larger X takes the 16-row blocks).
  * Deterministic: every output is accumulated in a fixed order. */

@@ -351,20 +351,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24_skinny(SpmmArgs a) {
     }
 }
 
-// One or two tokens: the product is a matrix-vector product bound by reading the packed rows
+// One to four tokens: the product is a matrix-vector product bound by reading the packed rows
 // once, and 16-row matrix-core fragments would make each wave gather 64-byte pieces of 16
 // rows.  Here each wave streams whole packed rows instead: lane L takes the 16-byte chunks
 // L, L + 64, ... of a row (chunk c holds the kept values 8c .. 8c + 7, that is the dense
 // groups 4c .. 4c + 3 and the index bits [16c, 16c + 16) of the row, the upper or lower half
-// of index word c/2).  X, J tokens of `in` bf16, is staged once per block in LDS; the dense
-// column of a kept value is picked out of the two X words of its group by a byte permute
-// whose selector places the chosen bf16 in the upper half of an fp32.  The next chunks are
-// loaded before the current ones are used (the first before the X barrier), and each row ends
-// with a fixed-order wave reduction, so the result is deterministic.
+// of index word c/2).  X, its tokens (at most J) of `in` bf16, is staged once per block in
+// LDS; the dense column of a kept value is picked out of the two X words of its group by a
+// byte permute whose selector places the chosen bf16 in the upper half of an fp32.  The next
+// chunks are loaded before the current ones are used (the first before the X barrier), and
+// each row ends with a fixed-order wave reduction, so the result is deterministic.
 template <int J>
 __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_block) {
     constexpr int U = 4;  // 16-byte chunks per lane in flight
-    extern __shared__ uint4 xs[];  // [J][in / 8] 16-byte pieces of X
+    extern __shared__ uint4 xs[];  // [tokens][in / 8] 16-byte pieces of X
+    const int nt = (int)a.tokens;  // J when J <= 2, else 3 or 4
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t nch = a.in / 16, xch = a.in / 8;
     const int64_t rend = (int64_t)(blockIdx.x + 1) * rows_per_block;
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
         }
     };
     fetch(r, c0, v, iw);
-    for (int64_t c = tid; c < J * xch; c += 512) {
+    for (int64_t c = tid; c < nt * xch; c += 512) {
         const int64_t t = c / xch, k = c - t * xch;
         xs[c] = *reinterpret_cast<const uint4*>(a.x + t * a.xstride + k * 8);
     }
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
                 const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};  // kept pair of group g
 #pragma unroll
                 for (int t = 0; t < J; ++t) {
+                    if (J > 2 && t >= nt) break;  // uniform
                     const uint4 xa = xs[t * xch + 2 * c], xb = xs[t * xch + 2 * c + 1];
                     const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
                 float s = acc[t];
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-                if (lane == 0) {
+                if (lane == 0 && (J <= 2 || t < nt)) {
                     if (a.ytype == 0)
                         static_cast<float*>(a.y)[t * a.ystride + r] = s;
                     else
@@ -479,7 +481,7 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;  // MI355X
-    if (a.tokens <= 2 && a.tokens * a.in <= SP_SPMV_MAX_X) {
+    if (a.tokens <= 4 && a.tokens * a.in <= SP_SPMV_MAX_X) {
         // about two blocks of eight waves per CU; every wave ends its row loop, then the block
         const int64_t target = 2 * (int64_t)cus;
         const int64_t rpb = (a.out + target - 1) / target;
@@ -487,8 +489,10 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
         const size_t smem = (size_t)(a.tokens * a.in * 2);
         if (a.tokens == 1)
             k_spmv24<1><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
-        else
+        else if (a.tokens == 2)
             k_spmv24<2><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
+        else
+            k_spmv24<4><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
         return hipGetLastError();
     }
     if (a.tokens <= SP_SKINNY_MAX_TOKENS) {

@@ -137,16 +137,18 @@ def test_sparse_matmul_each_tile_size_with_ragged_edges(out, inn, tokens, tile):
 
 
 @pytest.mark.parametrize("out,inn,tokens", [(36, 64, 1), (36, 64, 2), (6000, 128, 1), (5000, 4160, 2),
-                                             (520, 11008, 2), (8, 24640, 1), (40, 12352, 2), (100, 128, 7),
+                                             (520, 11008, 2), (8, 24640, 1), (40, 12352, 2), (36, 64, 3),
+                                             (1000, 6144, 3), (520, 4096, 4), (40, 6208, 4), (100, 128, 7),
                                              (256, 4160, 32), (68, 192, 33), (132, 256, 64), (64, 320, 65),
                                              (96, 1024, 128), (4, 64, 128)])
 @pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
 def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
-    """One or two tokens whose X fits in 48 KB run on the row-streaming kernel (several rows per
-    wave, rows longer than one pass of the wave, X of 2 x 11008 bf16); 24640 columns at one token
-    and 12352 at two are just above that and, like 3 to 64 tokens, run on blocks of 16 W rows
-    whose waves split k (fewer k blocks than waves included); above 64 tokens the 64 x 64 tiles.
-    Every output against the oracle, nothing written past y."""
+    """One to four tokens whose X fits in 48 KB run on the row-streaming kernel (several rows per
+    wave, rows longer than one pass of the wave, X of 2 x 11008 bf16, three tokens on the
+    four-token kernel); 24640 columns at one token, 12352 at two and 6208 at four are just above
+    that and, like 5 to 64 tokens, run on blocks of 16 W rows whose waves split k (fewer k blocks
+    than waves included); above 64 tokens the 64 x 64 tiles.  Every output against the oracle,
+    nothing written past y."""
     _say("spmm few tokens", out, inn, tokens, ytype)
     _, values, indices = _packed_layer(out, inn, 60 + out + tokens, w_std=1.0)
     x = nm_synth.normal((tokens, inn), 1.0, 61, torch.bfloat16, device=DEV)
@@ -161,7 +163,7 @@ def test_sparse_matmul_few_tokens(out, inn, tokens, ytype):
     assert torch.equal(S.nm_sparse_matmul(values, indices, x, out_dtype=ytype), y)
 
 
-@pytest.mark.parametrize("name_index,tokens", [(4, 1), (6, 2), (6, 16), (0, 128)])
+@pytest.mark.parametrize("name_index,tokens", [(4, 1), (6, 2), (5, 4), (6, 16), (0, 128)])
 def test_sparse_matmul_llama7b_decode_batches(name_index, tokens):
     """Decode-sized batches on full LLaMA-7B-shaped weights, three windows of 128 W rows."""
     name, out, inn = nm_synth.LLAMA2_7B_LAYER[name_index]
