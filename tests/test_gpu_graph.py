@@ -74,7 +74,7 @@ def test_layer_step_replays_as_a_graph(shape, wtype):
     _replay_and_compare(g, [out, dl, values, indices, dense], refs)
 
 
-@pytest.mark.parametrize("tokens", [1, 16, 256])
+@pytest.mark.parametrize("tokens", [1, 3, 16, 256])
 def test_sparse_product_replays_as_a_graph(tokens):
     """Decode- and prefill-sized products of a packed LLaMA-7B-shaped weight (4096x4096)."""
     _say("graph spmm", tokens)
