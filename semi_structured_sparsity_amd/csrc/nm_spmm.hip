@@ -44,6 +44,7 @@ namespace nm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Tile family.  A block of WAVES waves owns a T x T tile of Y^T with T = 32 * WAVES (256, 128
@@ -357,9 +358,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24_skinny(SpmmArgs a) {
 // L, L + 64, ... of a row (chunk c holds the kept values 8c .. 8c + 7, that is the dense
 // groups 4c .. 4c + 3 and the index bits [16c, 16c + 16) of the row, the upper or lower half
 // of index word c/2).  X, its tokens (at most J) of `in` bf16, is staged once per block in
-// LDS; the dense column of a kept value is picked out of the two X words of its group by a
-// byte permute whose selector places the chosen bf16 in the upper half of an fp32.  The next
-// chunks are loaded before the current ones are used (the first before the X barrier), and
+// LDS; one byte permute per group and token picks the two kept columns out of the group's two
+// X words as a bf16 pair, and one two-term bf16 dot product (fp32 accumulate) takes it with
+// the kept pair as stored.  The next chunks are loaded before the current ones are used (the first before the X barrier), and
 // each row ends with a fixed-order wave reduction, so the result is deterministic.
 template <int J>
 __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_block) {
@@ -411,6 +412,15 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
             if (c < nch) {
                 const uint32_t bits = iw[u] >> (16 * (int)(c & 1));
                 const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};  // kept pair of group g
+                // group g keeps positions pa, pb: bytes 2pa, 2pa + 1, 2pb, 2pb + 1 of the group's
+                // eight X bytes {xd[2g + 1], xd[2g]} form the bf16 pair (x[pa], x[pb]), which
+                // lines up with the kept pair as stored
+                uint32_t sel[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t pa = (bits >> (4 * g)) & 3u, pb = (bits >> (4 * g + 2)) & 3u;
+                    sel[g] = 0x01000100u + pa * 0x0202u + ((pb * 0x0202u) << 16);
+                }
 #pragma unroll
                 for (int t = 0; t < J; ++t) {
                     if (J > 2 && t >= nt) break;  // uniform
@@ -418,15 +428,9 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
                     const uint32_t xd[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            const uint32_t p = (bits >> (4 * g + 2 * h)) & 3u;
-                            // bytes 2p, 2p + 1 of {xd[2g + 1], xd[2g]} into bytes 2, 3; zeros below
-                            const uint32_t sel = 0x01000c0cu + p * 0x02020000u;
-                            const float xv = __uint_as_float(__builtin_amdgcn_perm(xd[2 * g + 1], xd[2 * g], sel));
-                            const float wv_ = __uint_as_float(h ? (vw[g] & 0xFFFF0000u) : (vw[g] << 16));
-                            acc[t] = fmaf(wv_, xv, acc[t]);
-                        }
+                        const uint32_t xp = __builtin_amdgcn_perm(xd[2 * g + 1], xd[2 * g], sel[g]);
+                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, vw[g]),
+                                                                 __builtin_bit_cast(bf16x2_t, xp), acc[t], false);
                     }
                 }
             }
