@@ -175,6 +175,18 @@ __device__ __forceinline__ void nt_store(void* p, uint32_t v) {
     __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
 
+// Ordinary (write-back) stores of the compressed storage: the packed values, index words and
+// hard indices of the pack.  These outputs are the next kernel's inputs (unpack reads what pack
+// wrote), so they are written with the default cache policy rather than the streaming hint; the
+// byte and short stores of index bytes and hard indices in particular stay plain.  Measured on
+// MI355X, the pack is as fast this way; the unpack's 16-byte dense stores stay non-temporal
+// (ordinary stores made the LLaMA-7B-shaped unpack 30% slower).
+__device__ __forceinline__ void st_store(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st_store(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ __forceinline__ void st_store(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+__device__ __forceinline__ void st_store(void* p, uint16_t v) { *reinterpret_cast<uint16_t*>(p) = v; }
+__device__ __forceinline__ void st_store(void* p, uint8_t v) { *reinterpret_cast<uint8_t*>(p) = v; }
+
 // Streaming loads: every input element is read once per launch, so the sampling kernels load
 // their inputs non-temporally as well (measured: backward 6% and forward 5% faster on MI355X).
 // Only for accesses whose lanes cover whole cache lines together: when lanes are further apart

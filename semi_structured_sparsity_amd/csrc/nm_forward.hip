@@ -77,14 +77,15 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
                 byte |= (uint32_t)pos << (2 * (p * N + tt));
             }
         }
+        // the compressed storage with ordinary stores, as nm_mask_harden_pack writes it
         if constexpr (T::bytes == 2) {
-            nt_store(reinterpret_cast<uint16_t*>(a.values) + g0 * N,
+            st_store(reinterpret_cast<uint16_t*>(a.values) + g0 * N,
                      make_uint2(vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)));
         } else {
-            nt_store(reinterpret_cast<uint32_t*>(a.values) + g0 * N, make_uint4(vals[0], vals[1], vals[2], vals[3]));
+            st_store(reinterpret_cast<uint32_t*>(a.values) + g0 * N, make_uint4(vals[0], vals[1], vals[2], vals[3]));
         }
-        __builtin_nontemporal_store((uint8_t)byte, reinterpret_cast<uint8_t*>(a.indices) + t);  // byte t
-        if (a.hard) __builtin_nontemporal_store((uint16_t)hard, reinterpret_cast<uint16_t*>(a.hard + g0));
+        st_store(reinterpret_cast<uint8_t*>(a.indices) + t, (uint8_t)byte);  // byte t
+        if (a.hard) st_store(reinterpret_cast<uint16_t*>(a.hard + g0), (uint16_t)hard);
     }
 }
 

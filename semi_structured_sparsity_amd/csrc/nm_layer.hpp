@@ -282,10 +282,8 @@ __device__ __forceinline__ uint32_t load_bits(const typename T::storage* p, int6
 }
 template <typename T>
 __device__ __forceinline__ void store_bits(typename T::storage* p, int64_t i, uint32_t v) {
-    // non-temporal like the vector stores: where the compiler merges the two paths into one
-    // store, it keeps the non-temporal hint only if both paths carry it
-    if constexpr (T::bytes == 4) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p) + i);
-    else __builtin_nontemporal_store((uint16_t)v, reinterpret_cast<uint16_t*>(p) + i);
+    if constexpr (T::bytes == 4) st_store(reinterpret_cast<uint32_t*>(p) + i, v);
+    else st_store(reinterpret_cast<uint16_t*>(p) + i, (uint16_t)v);
 }
 
 // Raw element bits (bit copies: packed values keep NaN payloads and signed zeros).  CNT elements
@@ -320,7 +318,9 @@ __device__ __forceinline__ void load_raw(const typename T::storage* __restrict__
     }
 }
 
-template <typename T, int CNT>
+// NTS: the 16-byte vectors are stored non-temporally (the unpack's dense output); otherwise
+// every store is an ordinary one (the pack's compressed storage).
+template <typename T, int CNT, bool NTS = false>
 __device__ __forceinline__ void store_raw(typename T::storage* p, bool vec, int valid,
                                           const uint32_t* in) {
     static_assert(CNT * T::bytes % 16 == 0, "whole 16-byte vectors");
@@ -333,7 +333,8 @@ __device__ __forceinline__ void store_raw(typename T::storage* p, bool vec, int 
                 if constexpr (T::bytes == 4) d[q] = in[4 * i + q];
                 else d[q] = in[8 * i + 2 * q] | (in[8 * i + 2 * q + 1] << 16);
             }
-            nt_store(reinterpret_cast<uint4*>(p) + i, make_uint4(d[0], d[1], d[2], d[3]));
+            if constexpr (NTS) nt_store(reinterpret_cast<uint4*>(p) + i, make_uint4(d[0], d[1], d[2], d[3]));
+            else st_store(reinterpret_cast<uint4*>(p) + i, make_uint4(d[0], d[1], d[2], d[3]));
         }
         return;
     }
@@ -371,9 +372,12 @@ __device__ __forceinline__ void load_logit_unit(const float* __restrict__ p, boo
 
 // One group's raw weights (M elements) and the store of N kept values / M dense values, with
 // the widest single access the group's byte size allows when `vec` (rows 16-byte aligned, so a
-// group of 2^i bytes is 2^i-byte aligned); element accesses otherwise.
+// group of 2^i bytes is 2^i-byte aligned); element accesses otherwise, of the first `valid`
+// elements only (the rest read as 0): a thread whose last groups lie past the end of its row
+// reads nothing beyond its own groups.
 template <typename T, int CNT>
-__device__ __forceinline__ void load_group_raw(const typename T::storage* __restrict__ p, bool vec, uint32_t* out) {
+__device__ __forceinline__ void load_group_raw(const typename T::storage* __restrict__ p, bool vec, uint32_t* out,
+                                               int valid = CNT) {
     constexpr int BYTES = CNT * T::bytes;
     if constexpr (BYTES % 16 == 0) {
         if (vec) {
@@ -393,29 +397,29 @@ __device__ __forceinline__ void load_group_raw(const typename T::storage* __rest
     }
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-        if constexpr (T::bytes == 4) out[i] = reinterpret_cast<const uint32_t*>(p)[i];
-        else out[i] = (uint32_t)p[i];
+        if constexpr (T::bytes == 4) out[i] = i < valid ? reinterpret_cast<const uint32_t*>(p)[i] : 0u;
+        else out[i] = i < valid ? (uint32_t)p[i] : 0u;
     }
 }
 
-template <typename T, int CNT>
+template <typename T, int CNT, bool NTS = false>
 __device__ __forceinline__ void store_group_raw(typename T::storage* p, bool vec, const uint32_t* in) {
     constexpr int BYTES = CNT * T::bytes;
     if constexpr (BYTES % 16 == 0) {
         if (vec) {
-            store_raw<T, CNT>(p, true, CNT, in);
+            store_raw<T, CNT, NTS>(p, true, CNT, in);
             return;
         }
     } else if constexpr (BYTES == 8) {
         if (vec) {
-            if constexpr (T::bytes == 2) nt_store(p, make_uint2(in[0] | (in[1] << 16), in[2] | (in[3] << 16)));
-            else nt_store(p, make_uint2(in[0], in[1]));
+            if constexpr (T::bytes == 2) st_store(p, make_uint2(in[0] | (in[1] << 16), in[2] | (in[3] << 16)));
+            else st_store(p, make_uint2(in[0], in[1]));
             return;
         }
     } else if constexpr (BYTES == 4) {
         if (vec) {
-            if constexpr (T::bytes == 2) nt_store(p, in[0] | (in[1] << 16));
-            else nt_store(p, in[0]);
+            if constexpr (T::bytes == 2) st_store(p, in[0] | (in[1] << 16));
+            else st_store(p, in[0]);
             return;
         }
     }

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
         if (mine > 0) {
             if (vec) load_logit_unit<GT * K>(a.logits + g0 * K, true, GT * K, l);
             else load_logit_unit<GT * K>(a.logits + g0 * K, false, mine * K, l);
-            load_group_raw<T, GT * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, vec, raw);
+            load_group_raw<T, GT * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, vec, raw, mine * M);
         }
         for (int i = lane; i < WW; i += 64) ww[i] = 0u;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
             if (a.hard) {
 #pragma unroll
                 for (int i = 0; i < GT; ++i)
-                    if (i < mine) __builtin_nontemporal_store((uint8_t)hard[i], a.hard + g0 + i);
+                    if (i < mine) st_store(a.hard + g0 + i, (uint8_t)hard[i]);
             }
             atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
             if ((lb % 32) + TS::TBITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
         uint32_t* idx = a.indices + r * a.words_per_row + (q_begin + wq) * N * BITS / 32;
-        for (int i = lane; i < nwords; i += 64) nt_store(idx + i, ww[i]);
+        for (int i = lane; i < nwords; i += 64) st_store(idx + i, ww[i]);
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the words are read before the next row clears them
         __builtin_amdgcn_wave_barrier();
     }
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
             acc |= (uint64_t)p << (tt * BITS);
         }
         store_group_raw<T, N>(reinterpret_cast<typename T::storage*>(a.values) + g0 * N, true, v);
-        if (a.hard) __builtin_nontemporal_store((uint8_t)bk, a.hard + g0);
+        if (a.hard) st_store(a.hard + g0, (uint8_t)bk);
         const int lb = lane * N * BITS;  // the thread's first bit in the wave's words
         atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
         if ((lb % 32) + N * BITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
         const int ngw = (int)(groups - gw0 < 64 ? groups - gw0 : 64);
         const int nwords = (ngw * N * BITS + 31) / 32;
         uint32_t* idx = a.indices + gw0 * N * BITS / 32;
-        for (int i = lane; i < nwords; i += 64) nt_store(idx + i, ww[i]);
+        for (int i = lane; i < nwords; i += 64) st_store(idx + i, ww[i]);
     }
 }
 
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack_flat8(UnpackArgs a) {
         for (int tt = 0; tt < N; ++tt) x = pos[tt] == (uint32_t)j ? v[tt] : x;  // later field wins
         o[j] = x;
     }
-    store_group_raw<T, M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, o);
+    store_group_raw<T, M, true>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, o);
 }
 
 template <int N, int M, typename T>
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
         }
         auto* dp = reinterpret_cast<typename T::storage*>(a.dense) + g0 * M;
         if (vec) {
-            store_group_raw<T, GT * M>(dp, true, o);
+            store_group_raw<T, GT * M, true>(dp, true, o);
         } else {
             for (int e = 0; e < mine * M; ++e) store_bits<T>(dp, e, o[e]);
         }
@@ -328,12 +328,12 @@ __global__ __launch_bounds__(kThreads) void k_pack_bytes(PackArgs a) {
     if constexpr (U * N * T::bytes == 16) {
         store_raw<T, U * N>(vp, true, U * N, vals);
     } else {  // 8 bytes: four bf16 values
-        nt_store(vp, make_uint2(vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)));
+        st_store(vp, make_uint2(vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)));
     }
-    __builtin_nontemporal_store((uint8_t)byte, reinterpret_cast<uint8_t*>(a.indices) + t);  // byte t
+    st_store(reinterpret_cast<uint8_t*>(a.indices) + t, (uint8_t)byte);  // byte t
     if (a.hard) {
-        if constexpr (U == 2) __builtin_nontemporal_store((uint16_t)hard, reinterpret_cast<uint16_t*>(a.hard + g0));
-        else nt_store(a.hard + g0, hard);
+        if constexpr (U == 2) st_store(reinterpret_cast<uint16_t*>(a.hard + g0), (uint16_t)hard);
+        else st_store(a.hard + g0, hard);
     }
 }
 
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
                 dense[q * M + j] = o;
             }
         }
-        store_raw<T, U * M>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, U * M, dense);
+        store_raw<T, U * M, true>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * M, true, U * M, dense);
     }
 }
 
