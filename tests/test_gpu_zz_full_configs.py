@@ -21,8 +21,9 @@ import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
 from oracle_inputs import oracle_prior
-from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, soft_mask_check,
-                    tol_for_tau)
+import roundtrip_diag
+from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, oracle_bounds,
+                    soft_mask_check)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -41,69 +42,100 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-def _check_rows(w, L, G, n, m, kappa, tau, seed, offset, out_fwd, out_bwd):
-    """Oracle on sampled rows against full-size GPU outputs."""
+def _check_rows(w, L, G, n, m, kappa, tau, seed, offset, out_fwd, out_bwd, rows_to_check=None, chunk=256):
+    """The oracle on whole row windows against the full-size GPU outputs: every row by default,
+    in windows of `chunk` rows, or only `rows_to_check`.  The bound of each element is the stated
+    tolerance or, where larger, the one derived from the kernel's fp32 evaluation (parity.py).
+    Returns the largest error / bound of the forward and the backward."""
     rows = w.shape[0]
     bf16 = w.dtype == torch.bfloat16
+    cand = oracle.candidate_matrix(n, m)
+    windows = ([(r, r + 1) for r in rows_to_check] if rows_to_check is not None
+               else [(r, min(rows, r + chunk)) for r in range(0, rows, chunk)])
     worst_f = worst_b = 0.0
-    for r in _sample_rows(rows):
-        wr, Lr = w[r:r + 1].cpu(), L[r:r + 1].cpu()
-        ref = oracle.forward(wr, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
-        soft = oracle.soft_mask(Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
-        rel, bad = forward_check(out_fwd[r:r + 1].double().cpu().numpy(), ref,
-                                 wr.double().numpy(), soft, m, tol_for_tau(tau), bf16)
-        assert bad == 0, f"forward row {r}: {bad} elements out of tolerance"
+    for r0, r1 in windows:
+        wr, Lr = w[r0:r1].cpu(), L[r0:r1].cpu()
+        wd = wr.double().numpy()
+        ref = oracle.forward(wr, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r0)
+        y, dy, dm = oracle_bounds(oracle, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r0)
+        soft = (y @ cand).reshape(r1 - r0, -1)
+        rel, bad = forward_check(out_fwd[r0:r1].double().cpu().numpy(), ref, wd, soft, m, TOL_FP32, bf16, dm)
+        assert bad == 0, f"forward rows {r0}..{r1 - 1}: {bad} elements out of tolerance (worst {rel})"
         worst_f = max(worst_f, rel)
         if G is not None:
-            Gr = G[r:r + 1].cpu()
-            refb = oracle.backward(wr, Lr, Gr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
-            y = oracle.probs(Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r)
-            d = candidate_sums(wr.double().numpy(), Gr.double().numpy(), n, m,
-                               oracle.candidate_matrix(n, m))
-            rel, bad = backward_check(out_bwd[r:r + 1].double().cpu().numpy(), refb, y, d,
-                                      kappa / tau, tol_for_tau(tau))
-            assert bad == 0, f"backward row {r}: {bad} elements out of tolerance"
+            Gr = G[r0:r1].cpu()
+            refb = oracle.backward(wr, Lr, Gr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r0)
+            d = candidate_sums(wd, Gr.double().numpy(), n, m, cand)
+            rel, bad = backward_check(out_bwd[r0:r1].double().cpu().numpy(), refb, y, d, kappa / tau, TOL_FP32,
+                                      dy=dy, n=n, m=m)
+            assert bad == 0, f"backward rows {r0}..{r1 - 1}: {bad} elements out of tolerance (worst {rel})"
             worst_b = max(worst_b, rel)
     return worst_f, worst_b
 
 
-def _check_pack_full(w, L, n, m):
-    """Whole matrix, bit-exact against the oracle; returns the GPU outputs."""
-    values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
-    dense = S.nm_unpack(values, indices, w.shape[1], n, m)
+def _poisoned_like(t):
+    return roundtrip_diag.poisoned(tuple(t.shape), t.dtype, t.device)
+
+
+def _fwd_bwd(w, L, G, n, m, kappa, tau, seed, offset):
+    """Forward and backward into poisoned outputs (an unwritten element cannot pass)."""
+    out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, offset, out=_poisoned_like(w))
+    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, offset, out=_poisoned_like(L)) if G is not None else None
+    return out, dl
+
+
+_PREV_POINTERS = {}
+
+
+def _check_pack_full(w, L, n, m, tag=""):
+    """Whole matrix, bit-exact against the oracle; returns the GPU outputs.  Every output starts
+    poisoned, and a failed round trip classifies itself (roundtrip_diag)."""
+    global _PREV_POINTERS
+    rows, cols = w.shape
+    values, indices, hard = roundtrip_diag.pack_outputs(w, n, m, S.index_words_per_row(cols, n, m))
+    S.nm_mask_harden_pack(w, L, n, m, with_hard=True, out=(values, indices, hard))
+    dense = S.nm_unpack(values, indices, cols, n, m, out=roundtrip_diag.poisoned((rows, cols), w.dtype, w.device))
     rv, ri, rh = oracle.pack(w.cpu(), L.cpu(), n, m)
     assert np.array_equal(hard.cpu().numpy(), rh)
     assert np.array_equal(indices.cpu().numpy().view(np.uint32), ri)
     assert np.array_equal(_bits(values).cpu().numpy(), rv.view(_bits(values).cpu().numpy().dtype))
     # the copied-back dense weights against the oracle's unpack, and the selection on the GPU
-    rd = oracle.unpack(rv, ri, w.shape[1], n, m)
+    rd = oracle.unpack(rv, ri, cols, n, m)
     dense_ok = np.array_equal(_bits(dense).cpu().numpy(), rd.view(_bits(dense).cpu().numpy().dtype))
     keep = _keep_mask(hard, n, m)
     want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
     select_ok = torch.equal(_bits(dense), want)
     if not (dense_ok and select_ok):
-        _report_unpack(w, n, m, values, indices, dense, rd, want)
+        _report_unpack(tag, w, n, m, values, indices, hard, dense, rd, want)
+    ptrs = {k: t.data_ptr() for k, t in (("values", values), ("indices", indices), ("dense", dense))}
+    _PREV_POINTERS = ptrs
     assert dense_ok and select_ok
     return values, indices, hard, dense
 
 
-def _report_unpack(w, n, m, values, indices, dense, rd, want):
-    """Say where an unpack disagrees: the copied-back output against the oracle, the same output
-    against the selection computed on the GPU, a second copy of the output, and a repeated unpack
-    of the same packed inputs into a fresh buffer."""
+def _report_unpack(tag, w, n, m, values, indices, hard, dense, rd, want):
+    """Classify a failed unpack (roundtrip_diag) and repeat the pieces: a second copy of the
+    output, the packed inputs against the oracle once more, and an unpack of the same packed
+    inputs into a fresh poisoned buffer."""
     cols = w.shape[1]
     it = np.int16 if w.dtype == torch.bfloat16 else np.int32
     got = _bits(dense).cpu().numpy()
     ref = rd.view(it)
-    bad = np.argwhere(got != ref)
-    _say("unpack mismatch vs oracle:", bad.shape[0], "elements; first",
-         [(int(r), int(c), int(got[r, c]), int(ref[r, c])) for r, c in bad[:8]])
-    bad_gpu = (_bits(dense) != want).nonzero()
-    _say("  vs selection on the GPU:", bad_gpu.shape[0], "elements; first", bad_gpu[:8].tolist())
     again = _bits(dense).cpu().numpy()
-    _say("  second copy of the output equals the first:", bool(np.array_equal(again, got)))
-    d2 = S.nm_unpack(values, indices, cols, n, m)
-    _say("  repeated unpack equals the oracle:", bool(np.array_equal(_bits(d2).cpu().numpy(), ref)))
+    rechecks = {
+        "dense_vs_oracle_wrong": int((got != ref).sum()),
+        "dense_vs_selection_wrong": int((_bits(dense) != want).sum()),
+        "second_copy_equal": bool(np.array_equal(again, got)),
+    }
+    roundtrip_diag.report(tag, w, values, indices, hard, dense, want, m, rechecks, _PREV_POINTERS)
+    # then repeat the unpack: into a fresh poisoned buffer, and into the same buffer
+    d2 = S.nm_unpack(values, indices, cols, n, m, out=roundtrip_diag.poisoned(tuple(w.shape), w.dtype, w.device))
+    again2 = {"repeat_unpack_equals_oracle": bool(np.array_equal(_bits(d2).cpu().numpy(), ref)),
+              "repeat_unpack_equals_first": bool(torch.equal(_bits(d2), _bits(dense)))}
+    S.nm_unpack(values, indices, cols, n, m, out=dense)
+    torch.cuda.synchronize()
+    again2["same_buffer_unpack_equals_oracle"] = bool(np.array_equal(_bits(dense).cpu().numpy(), ref))
+    _say("ROUND TRIP RECHECKS", again2)
 
 
 def _keep_mask(hard, n, m):
@@ -155,7 +187,7 @@ def test_config1_single_256x256_fp32_weight_every_element():
     assert bad == 0
     words = S.nm_debug_noise(256, 256, n, m, seed, off).cpu().numpy().view(np.uint32).reshape(-1)
     assert np.array_equal(words, oracle.noise_words(seed, off, 0, words.size))
-    _check_pack_full(wd, Ld, n, m)
+    _check_pack_full(wd, Ld, n, m, tag="config1")
 
 
 @pytest.mark.parametrize("i", range(len(nm_synth.LLAMA2_7B_LAYER)))
@@ -166,13 +198,12 @@ def test_config2_llama7b_layer(i):
     _say("config2", name, rows, cols)
     w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
                                      prior=oracle_prior, device=DEV)
-    out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, 0)
-    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, 0)
+    out, dl = _fwd_bwd(w, L, G, n, m, kappa, tau, seed, 0)
     wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl)
-    _say("  sampled rows fwd/bwd err/bound", wf, wb)
+    _say("  every row: fwd/bwd err/bound", wf, wb)
     _soft_properties(L, n, m, kappa, tau, seed, 0)
     _grad_properties(w, G, dl, n, m, kappa, tau)
-    _check_pack_full(w, L, n, m)
+    _check_pack_full(w, L, n, m, tag=f"config2 {name}")
     # the prior's candidate is the hard mask wherever the prior logit margin (3) dominates
     prior = oracle_prior(w, n, m).to(DEV)
     _, _, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
@@ -201,42 +232,25 @@ def test_config3_annealed_sweep_sampled(layer, step):
         _say("config3", layer, step, name)
         w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, logits="prior",
                                          prior=oracle_prior, device=DEV)
-        out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, step)
-        dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, step)
-        _check_rows(w, L, G, n, m, kappa, tau, seed, step, out, dl)
+        out, dl = _fwd_bwd(w, L, G, n, m, kappa, tau, seed, step)
+        # every row of the last layer's matrices at the last step (tau = 0.05), sampled rows elsewhere
+        every = layer == 31 and step == 9
+        wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, step, out, dl,
+                             rows_to_check=None if every else _sample_rows(rows))
+        _say("  ", "every row" if every else "sampled rows", "fwd/bwd err/bound", wf, wb)
         _grad_properties(w, G, dl, n, m, kappa, tau)
         if step == 9:
-            _check_pack_full(w, L, n, m)
+            _check_pack_full(w, L, n, m, tag=f"config3 layer {layer} step {step} {name}")
         del w, L, G, out, dl
     torch.cuda.empty_cache()
 
 
-def _report_round_trip(layer, name, w, L, n, m, values, indices, hard, dense, keep):
-    """Say which output of a failed round trip is wrong: the pass repeated on the same inputs,
-    and the first mismatching rows against the oracle."""
-    rows, cols = w.shape
-    argmax = torch.argmax(L, dim=-1)
-    bad_hard = (hard.long() != argmax).nonzero()
-    want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
-    bad_dense = (_bits(dense) != want).nonzero()
-    _say("round trip failed:", "layer", layer, name, rows, cols,
-         "hard mismatches", bad_hard.shape[0], bad_hard[:4].tolist(),
-         "dense mismatches", bad_dense.shape[0], bad_dense[:4].tolist())
-    v2, i2, h2 = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
-    d2 = S.nm_unpack(values, indices, cols, n, m)
-    _say("  repeat: values equal", torch.equal(_bits(v2), _bits(values)), "indices equal", torch.equal(i2, indices),
-         "hard equal", torch.equal(h2, hard), "unpack of the first pack equal", torch.equal(_bits(d2), _bits(dense)))
-    for r in sorted({int(x) for x in bad_dense[:4, 0].tolist()} | {int(x) for x in bad_hard[:4, 0].tolist()}):
-        rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
-        _say("  row", r, "values ok", np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16)),
-             "indices ok", np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri),
-             "hard ok", np.array_equal(hard[r:r + 1].cpu().numpy(), rh),
-             "unpack ok", np.array_equal(_bits(dense[r:r + 1]).cpu().numpy(),
-                                         oracle.unpack(values[r:r + 1].cpu(), indices[r:r + 1].cpu().numpy().view(np.uint32),
-                                                       cols, n, m).view(np.int16)))
-
-
 def test_config4_nemotron15b_every_matrix_round_trip():
+    """Every matrix of the Nemotron-shaped model: the hard mask is the first argmax of the
+    logits, and unpack(pack) keeps exactly the selected weights with +0.0 elsewhere, from
+    poisoned outputs; the oracle checks the first and last rows of a square and a rectangular
+    matrix per layer."""
+    global _PREV_POINTERS
     n, m = 2, 4
     total = 0
     for layer in range(nm_synth.LAYERS):
@@ -244,15 +258,32 @@ def test_config4_nemotron15b_every_matrix_round_trip():
             seed = nm_synth.input_seed(4, layer, i)
             w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.015, seed,
                                              with_grad=False, device=DEV)
-            values, indices, hard = S.nm_mask_harden_pack(w, L, n, m, with_hard=True)
-            dense = S.nm_unpack(values, indices, cols, n, m)
-            # hard mask = first argmax of the logits
+            values, indices, hard = roundtrip_diag.pack_outputs(w, n, m, S.index_words_per_row(cols, n, m))
+            S.nm_mask_harden_pack(w, L, n, m, with_hard=True, out=(values, indices, hard))
+            dense = S.nm_unpack(values, indices, cols, n, m,
+                                out=roundtrip_diag.poisoned((rows, cols), w.dtype, w.device))
             hard_ok = torch.equal(hard.long(), torch.argmax(L, dim=-1))
             keep = _keep_mask(hard, n, m)
-            # round trip: exactly the selected weights survive, +0.0 elsewhere
-            trip_ok = torch.equal(_bits(dense), torch.where(keep, _bits(w), torch.zeros_like(_bits(w))))
+            want = torch.where(keep, _bits(w), torch.zeros_like(_bits(w)))
+            trip_ok = torch.equal(_bits(dense), want)
             if not (hard_ok and trip_ok):
-                _report_round_trip(layer, name, w, L, n, m, values, indices, hard, dense, keep)
+                d2 = S.nm_unpack(values, indices, cols, n, m,
+                                 out=roundtrip_diag.poisoned((rows, cols), w.dtype, w.device))
+                v2, i2, h2 = roundtrip_diag.pack_outputs(w, n, m, S.index_words_per_row(cols, n, m))
+                S.nm_mask_harden_pack(w, L, n, m, with_hard=True, out=(v2, i2, h2))
+                rechecks = {"layer": layer, "matrix": name,
+                            "hard_wrong": int((hard.long() != torch.argmax(L, dim=-1)).sum()),
+                            "repeat_pack_values_equal": bool(torch.equal(_bits(v2), _bits(values))),
+                            "repeat_pack_indices_equal": bool(torch.equal(i2, indices)),
+                            "repeat_pack_hard_equal": bool(torch.equal(h2, hard)),
+                            "repeat_unpack_equals_selection": bool(torch.equal(_bits(d2), want)),
+                            "repeat_unpack_equals_first": bool(torch.equal(_bits(d2), _bits(dense)))}
+                roundtrip_diag.report(f"config4 layer {layer} {name}", w, values, indices, hard, dense, want,
+                                      m, rechecks, _PREV_POINTERS)
+                S.nm_unpack(values, indices, cols, n, m, out=dense)  # again, into the same buffer
+                _say("ROUND TRIP RECHECKS", {"same_buffer_unpack_equals_selection": bool(torch.equal(_bits(dense), want))})
+            _PREV_POINTERS = {k: t.data_ptr() for k, t in (("values", values), ("indices", indices),
+                                                            ("dense", dense))}
             assert hard_ok and trip_ok
             assert int(keep.view(-1, m).sum(1).min()) == n == int(keep.view(-1, m).sum(1).max())
             if i in (0, 4):  # the oracle on sampled rows of a square and a rectangular matrix
@@ -261,7 +292,7 @@ def test_config4_nemotron15b_every_matrix_round_trip():
                     assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri)
                     assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16))
             total += rows * cols
-            del w, L, values, indices, hard, dense, keep
+            del w, L, values, indices, hard, dense, keep, want
         if layer % 8 == 7:
             _say("config4 through layer", layer)
     torch.cuda.empty_cache()
@@ -274,13 +305,12 @@ def test_config5_general_nm_4096x11008(n, m):
     seed = nm_synth.input_seed(5, 0, m * 10 + n)
     _say("config5", n, m)
     w, L, G = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.02, seed, device=DEV)
-    out = S.nm_mask_forward(w, L, n, m, kappa, tau, seed, 0)
-    dl = S.nm_mask_backward(w, L, G, n, m, kappa, tau, seed, 0)
-    wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl)
-    _say("  sampled rows fwd/bwd err/bound", wf, wb)
+    out, dl = _fwd_bwd(w, L, G, n, m, kappa, tau, seed, 0)
+    wf, wb = _check_rows(w, L, G, n, m, kappa, tau, seed, 0, out, dl, chunk=128 if m == 8 else 256)
+    _say("  every row: fwd/bwd err/bound", wf, wb)
     _soft_properties(L, n, m, kappa, tau, seed, 0)
     _grad_properties(w, G, dl, n, m, kappa, tau)
-    _check_pack_full(w, L, n, m)
+    _check_pack_full(w, L, n, m, tag=f"config5 {n}:{m}")
 
 
 # ---------------------------------------------------------------------------------------------
