@@ -12,18 +12,76 @@ outputs), with "relative" made precise for each quantity:
   magnitude of the terms that form it: |gpu_k - ref_k| <= tol * c y_k (|d_k| + sum_i y_i |d_i|)
   plus an underflow floor.
 
-tol = 1e-5 for tau >= 1/2.  Below that the fp32 noise itself limits agreement: the Gumbel
-exponent is an fp32 number of magnitude up to ~25, whose rounding (~2^-24 * 25) is amplified by
-1/tau; tol_for_tau scales the bound by 0.5/tau there.
+Where the kernel's fp32 evaluation cannot reach tol = 1e-5 -- at small tau, where the fp32
+Gumbel exponent's own rounding is amplified by 1/tau -- each element's bound is the larger of
+the stated one and the bound derived from that evaluation (`prob_bound` and the `dy` / `dm`
+arguments below): the error of each fp32 operation of the kernel, propagated through the
+softmax, the soft mask and the backward.
 """
 import numpy as np
 
 TOL_FP32 = 1e-5
 TOL_BF16 = 1e-2
+U24 = 2.0**-24     # unit roundoff of fp32
+LOG2E = 1.4426950408889634
 
 
-def tol_for_tau(tau):
-    return TOL_FP32 * max(1.0, 0.5 / float(tau))
+def prob_bound(L, kappa, tau, words, gumbel, y, n, m):
+    """Bound on |kernel y_k - y_k| for every candidate slot (float64, shape of L), where y are the
+    oracle's binary64 probabilities and the kernel evaluates, per group and in fp32,
+        h_k = log2(-log2 u_k),  hi_k = fma(A, l_k, -fl(B h_k)),  rem_k = fma(A, l_k, -hi_k) - fl(B h_k),
+        t_k = (hi_k - max_i hi_i) + rem_k,  e_k = 2^t_k,  y_k = e_k / sum e
+    with A = fl(kappa log2(e) / tau), B = fl(1 / tau), kappa and tau themselves rounded to fp32.
+
+    Error of each score difference t_k - t_k* against the candidate k* with the largest exact
+    score (base 2), per term:
+      A and B rounded: kappa, tau and the quotient each round once (3 u for A, 2 u for B,
+        u = 2^-24), times A |l_k - l_k*| and B |h_k - h_k*|;
+      the Gumbel exponent: |dh| <= 2^-21 + 2^-22 |h| (measured for every 23-bit uniform), times B,
+        for k and for k*;
+      fl(B h) rounds (2^-24 |B h|) and is not recovered by the residual; the residual's fma and
+        subtraction add as much again: 2^-23 B |h|, for k and for k*;
+      hi_k - mu and the addition of rem_k round relative to |t_k|: 2^-23 |t_k|.
+    With D_k that total, ln y_k = ln2 (t_k - log2 sum 2^t) changes by at most ln2 (D_k + sum y_i D_i).
+    The rest is relative to y_k: the exp2 (1 ulp), the sums over candidates and positions (at
+    most K + M terms), the reciprocal and the final product: (K + M + 8) u.  Below the normal
+    range of fp32 (e_k < 2^-126, with the largest e about 1) the kernel may lose the whole value:
+    an absolute 2^-125 covers that.  Soft-mask entries sum N of these per position
+    (`soft_bound`)."""
+    L = np.asarray(L, np.float64)
+    y = np.asarray(y, np.float64)
+    K = L.shape[-1]
+    g = np.asarray(gumbel(words), np.float64).reshape(L.shape)
+    h = -g * LOG2E - np.log2(LN2)
+    A, B = kappa * LOG2E / tau, 1.0 / tau
+    z2 = (kappa * L + g) / tau * LOG2E
+    ks = np.argmax(z2, -1)[..., None]
+    at = lambda a: np.take_along_axis(a, ks, -1)  # noqa: E731
+    t = z2 - at(z2)
+    ah = np.abs(h)
+    D = (3 * U24 * A * np.abs(L - at(L)) + 2 * U24 * B * np.abs(h - at(h))
+         + B * (2.0**-20 + 2.0**-22 * (ah + at(ah))) + 2.0**-23 * B * (ah + at(ah))
+         + 2.0**-23 * np.abs(t) + 2.0**-60)
+    dln = LN2 * (D + (y * D).sum(-1, keepdims=True))
+    return y * (np.expm1(dln) + (K + m + 8) * U24) + 2.0**-125
+
+
+def soft_bound(dy, n, m, cand_matrix):
+    """Bound on the soft mask m_j = sum over candidates keeping j of y_k: [rows, cols]."""
+    dy = np.asarray(dy, np.float64)
+    rows, gpr, K = dy.shape
+    return (dy @ np.asarray(cand_matrix, np.float64)).reshape(rows, gpr * m)
+
+
+def oracle_bounds(oracle, L, n, m, kappa, tau, seed, offset, rows=None, row_begin=0):
+    """(y, dy, dm) for a row window [row_begin, row_begin + L.shape[0]) of a rows-row matrix: the
+    oracle's probabilities, and the fp32 evaluation bounds of the probabilities and soft mask."""
+    L = np.asarray(oracle._np(L), np.float32)
+    wr, gpr, K = L.shape
+    y = oracle.probs(L, n, m, kappa, tau, seed, offset, rows=rows, row_begin=row_begin)
+    words = oracle.noise_words(seed, offset, row_begin * gpr * K, wr * gpr * K)
+    dy = prob_bound(L, kappa, tau, words, oracle.gumbel, y, n, m)
+    return y, dy, soft_bound(dy, n, m, oracle.candidate_matrix(n, m))
 
 
 def to_f64(t):
@@ -52,28 +110,54 @@ def _verdict(err, bound):
     return float(np.nan_to_num(ratio, nan=np.inf).max(initial=0.0)), int(bad.sum())
 
 
-def soft_mask_check(gpu, ref, m, tol):
+def soft_mask_check(gpu, ref, m, tol, dm=None):
+    """Per group: the stated bound tol * max |ref|, or elementwise the derived bound dm where it
+    is larger."""
     g = np.asarray(gpu, np.float64).reshape(-1, m)
     r = np.asarray(ref, np.float64).reshape(-1, m)
-    return _verdict(_diff(g, r).max(1), tol * np.abs(r).max(1))
+    bound = np.repeat(tol * np.abs(r).max(1, keepdims=True), m, 1)
+    if dm is not None:
+        bound = np.maximum(bound, np.asarray(dm, np.float64).reshape(-1, m))
+    return _verdict(_diff(g, r), bound)
 
 
-def forward_check(gpu, ref, w, soft_ref, m, tol, bf16):
-    """gpu: float64 array of the GPU output; ref: oracle float64; w: float64 weights.
-    Returns (largest error / allowed error, number of elements over it)."""
+def forward_check(gpu, ref, w, soft_ref, m, tol, bf16, dm=None):
+    """gpu: float64 array of the GPU output; ref: oracle float64; w: float64 weights; dm: the
+    derived soft-mask bound (optional).  Returns (largest error / allowed error, number of
+    elements over it)."""
     gpu = np.asarray(gpu, np.float64)
+    aw = np.abs(w)
     mmax = np.repeat(np.abs(soft_ref).reshape(-1, m).max(1), m).reshape(ref.shape)
-    out_round = (TOL_BF16 if bf16 else 2.0**-24) * np.abs(ref)
-    return _verdict(_diff(gpu, ref), tol * mmax * np.abs(w) + out_round)
+    bound = tol * mmax * aw
+    if dm is not None:  # the soft mask's error times |w|, and the product's rounding
+        bound = np.maximum(bound, aw * (np.asarray(dm, np.float64).reshape(ref.shape) + U24 * np.abs(soft_ref)))
+    out_round = (TOL_BF16 if bf16 else U24) * np.abs(ref)
+    return _verdict(_diff(gpu, ref), bound + out_round)
 
 
-def backward_check(gpu, ref, y, d, c, tol):
-    """gpu, ref, y, d: [..., K] float64 (y = probabilities, d = candidate sums of G*w)."""
+def backward_check(gpu, ref, y, d, c, tol, dy=None, n=None, m=None, dd=None):
+    """gpu, ref, y, d: [..., K] float64 (y = probabilities, d = candidate sums of G*w, or their
+    magnitudes).  With dy (prob_bound) the bound is, elementwise, the larger of the stated one
+    and the derived one: for grad_k = c y_k (d_k - s), s = sum_i y_i d_i,
+        c (dy_k (|d_k| + |s|) + y_k sum_i dy_i |d_i|)        the probabilities' error,
+        + c y_k (dd_k + sum_i y_i dd_i)                        an error of d itself (optional),
+        + e c y_k (|d_k| + sum_i y_i |d_i|)                    rounding of the sums over N kept
+    products, the K-term dot product with y, c = fl(kappa / tau) from fp32 kappa and tau, and
+    the last products: e = (N + K + 12) u."""
     gpu = np.asarray(gpu, np.float64)
     ad = np.abs(d)
-    terms = c * y * (ad + (y * ad).sum(-1, keepdims=True))
+    sy = (y * ad).sum(-1, keepdims=True)
+    terms = c * y * (ad + sy)
+    bound = tol * terms
+    if dy is not None:
+        K = ad.shape[-1]
+        derived = c * (dy * (ad + sy) + y * (dy * ad).sum(-1, keepdims=True)) + (n + K + 12) * U24 * terms
+        if dd is not None:
+            dd = np.asarray(dd, np.float64)
+            derived = derived + c * y * (dd + (y * dd).sum(-1, keepdims=True))
+        bound = np.maximum(bound, derived)
     floor = c * 1e-36 * ad.max(-1, keepdims=True)  # probabilities near the fp32 underflow
-    return _verdict(_diff(gpu, ref), tol * terms + floor)
+    return _verdict(_diff(gpu, ref), bound + floor)
 
 
 def candidate_sums(w, grad, n, m, cand_matrix):

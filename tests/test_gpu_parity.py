@@ -11,8 +11,8 @@ import torch
 import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
-from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, soft_mask_check,
-                    to_f64, tol_for_tau)
+from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, oracle_bounds,
+                    soft_mask_check, to_f64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -81,7 +81,9 @@ def test_gumbel_transform_over_all_2_23_uniforms():
 # ---------------------------------------------------------------------------------------------
 # soft mask, forward, backward
 
-SAMPLES = [(100.0, 4.0), (100.0, 1.0), (1.0, 1.0), (0.0, 2.0), (30.0, 0.5), (5.0, 0.1)]
+# (kappa, tau): the annealing schedule's ends (100, 4) and (500, 0.05), and points between
+SAMPLES = [(100.0, 4.0), (100.0, 1.0), (1.0, 1.0), (0.0, 2.0), (30.0, 0.5), (5.0, 0.1), (3.0, 0.05),
+           (500.0, 0.05)]
 
 
 @pytest.mark.parametrize("n,m", SUPPORTED)
@@ -92,7 +94,8 @@ def test_soft_mask_matches_oracle(n, m, kappa, tau):
     _, L, _, _, Ld, _ = _inputs(rows, gpr * m, n, m, torch.float32, 1)
     got = to_f64(S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed=11, offset=3))
     want = oracle.soft_mask(L, n, m, kappa, tau, 11, 3)
-    rel, bad = soft_mask_check(got, want, m, tol_for_tau(tau))
+    _, _, dm = oracle_bounds(oracle, L, n, m, kappa, tau, 11, 3)
+    rel, bad = soft_mask_check(got, want, m, TOL_FP32, dm)
     _say("  worst err/bound", rel)
     assert bad == 0
     # invariants hold on the GPU too: sum to n, within [0, 1]
@@ -139,9 +142,9 @@ def test_backward_over_sample_parameters(kappa, tau):
     w, L, G, wd, Ld, Gd = _inputs(rows, gpr * m, n, m, torch.bfloat16, 4)
     got = to_f64(S.nm_mask_backward(wd, Ld, Gd, n, m, kappa, tau, 1, 1))
     want = oracle.backward(w, L, G, n, m, kappa, tau, 1, 1)
-    y = oracle.probs(L, n, m, kappa, tau, 1, 1)
+    y, dy, _ = oracle_bounds(oracle, L, n, m, kappa, tau, 1, 1)
     d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
-    rel, bad = backward_check(got, want, y, d, kappa / tau, tol_for_tau(tau))
+    rel, bad = backward_check(got, want, y, d, kappa / tau, TOL_FP32, dy=dy, n=n, m=m)
     _say("  worst err/bound", rel)
     assert bad == 0
 
