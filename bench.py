@@ -6,11 +6,14 @@ tau = 4, logits from the magnitude prior): forward (soft mask times frozen weigh
 the logits, hard-mask extraction with compressed pack, and unpack, for all seven matrices.
 Inputs are synthetic, seeded, generated on the GPU and resident in HBM before timing starts.
 
-Prints one JSON line.  `value` is masked weights per second of whole steps; the per-pass
-breakdown, the roofline of the dominant kernel (HIP-event timing, algorithmic bytes) and the
-oracle's CPU baseline on a bounded sample are added alongside.
+Prints one JSON line.  `value` is the metric: masked weights per second of the forward and
+backward passes, timed with HIP events inside each of the K whole-path steps (ms_per_step is the
+whole step).  Alongside: the per-pass breakdown, the roofline of the dominant kernel (HIP-event
+timing, algorithmic bytes), the 32-layer annealed sweep (32 such layers x 10 steps of forward,
+backward and harden/pack, tau 4 -> 0.05, kappa 100 -> 500), and the oracle's CPU baseline on a
+bounded sample on every host core available.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-sweep]
 """
 import argparse
 import json
@@ -55,6 +58,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-reps", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="leave out the 32-layer annealed sweep")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="least CPU time of the baseline")
     p.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                    help="print the path kernels' average durations from rocprofv3 --stats output")
@@ -104,24 +108,46 @@ def run_pass(S, mt, which, step):
 PASSES = ("fwd", "bwd", "harden_pack", "unpack")
 
 
-def step_all(S, mats, step):
+def step_all(S, mats, step, marks=None):
     # pass-major, as in a training step (all forwards, then all backwards, ...): each pass moves
     # >= 2 GB across the seven matrices, so no pass finds a matrix's data left in the 256 MB
-    # last-level cache by the previous pass over the same matrix
+    # last-level cache by the previous pass over the same matrix.  `marks`: a pair of events
+    # recorded on the launch stream before the forward pass and after the backward pass.
     for p in PASSES:
+        if marks is not None and p == "fwd":
+            marks[0].record()
         for mt in mats:
             run_pass(S, mt, p, step)
+        if marks is not None and p == "bwd":
+            marks[1].record()
+
+
+def host_cores():
+    """(threads to use, what the host reports): all cores this process may run on -- the CPU
+    affinity set, capped by a cgroup CPU quota when one is set -- next to os.cpu_count()."""
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    threads = min(affinity, quota) if quota else affinity
+    return threads, {"os_cpu_count": os.cpu_count(), "affinity": affinity, "cgroup_cpu_quota": quota}
 
 
 def cpu_baseline(min_seconds=10.0, max_passes=8):
     """The oracle over the same layer (same shapes, generators and parameters, CPU copies):
     forward, backward, pack and unpack of all seven matrices, repeated over successive steps
-    until at least `min_seconds` of CPU time has been spent.  Returns weights/s of whole steps."""
+    until at least `min_seconds` of CPU time has been spent, on every core available to the
+    process.  Returns weights/s of whole steps, and the forward + backward alone."""
     import torch
 
     import nm_synth
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads, host = host_cores()
     mats = []
     for i, (name, rows, cols) in enumerate(nm_synth.LLAMA2_7B_LAYER):
         seed = nm_synth.input_seed(2, 0, i)
@@ -129,15 +155,17 @@ def cpu_baseline(min_seconds=10.0, max_passes=8):
         prior = torch.from_numpy(oracle.prior_init(w, N, M)[1].astype("int64"))
         mats.append((seed, cols, w, nm_synth.prior_logits(prior, K, 3 * seed + 1),
                      nm_synth.normal((rows, cols), 1.0, 3 * seed + 2, torch.bfloat16)))
-    total_w, elapsed, passes = 0, 0.0, 0
+    total_w, elapsed, fb_elapsed, passes = 0, 0.0, 0.0, 0
     while passes < max_passes and (passes == 0 or elapsed < min_seconds):
         for seed, cols, w, L, G in mats:
             t0 = time.perf_counter()
             oracle.forward(w, L, N, M, KAPPA, TAU, seed, passes, nthreads=threads)
             oracle.backward(w, L, G, N, M, KAPPA, TAU, seed, passes, nthreads=threads)
+            t1 = time.perf_counter()
             v, idx, _ = oracle.pack(w, L, N, M, nthreads=threads)
             oracle.unpack(v, idx, cols, N, M, nthreads=threads)
             elapsed += time.perf_counter() - t0
+            fb_elapsed += t1 - t0
             total_w += w.numel()
         passes += 1
     # the same four passes on one thread over the first matrix (q, 4096x4096)
@@ -148,10 +176,12 @@ def cpu_baseline(min_seconds=10.0, max_passes=8):
     v, idx, _ = oracle.pack(w, L, N, M, nthreads=1)
     oracle.unpack(v, idx, cols, N, M, nthreads=1)
     t1 = time.perf_counter() - t0
-    return {"value": total_w / elapsed, "unit": "weights/s", "cores": oracle.threads_used(threads),
-            "kind": "oracle",
-            "sample": f"{passes} step(s) of the whole layer ({total_w} weight-passes): "
-                      f"fwd+bwd+harden_pack+unpack in binary64 on {threads} threads, {elapsed:.1f} s",
+    return {"value": total_w / fb_elapsed, "unit": "weights/s", "cores": oracle.threads_used(threads),
+            "kind": "oracle", "host": host,
+            "sample": f"{passes} step(s) of the whole layer ({total_w} weight-passes) in binary64 on "
+                      f"{threads} threads: value = forward + backward ({fb_elapsed:.1f} s), "
+                      f"whole_step = fwd+bwd+harden_pack+unpack ({elapsed:.1f} s)",
+            "whole_step": {"value": total_w / elapsed, "unit": "weights/s"},
             "single_thread": {"value": w.numel() / t1, "unit": "weights/s",
                               "sample": f"fwd+bwd+harden_pack+unpack of the 4096x4096 q matrix on 1 thread, "
                                         f"{t1:.1f} s"}}
@@ -751,15 +781,18 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0.record()
     for s in range(args.steps):
-        step_all(S, mats, args.warmup + s)
+        step_all(S, mats, args.warmup + s, marks[s])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / args.steps
     step_ms_wall = wall * 1e3 / args.steps
     ms_per_step = max(step_ms, step_ms_wall)
+    # the metric: forward + backward of every matrix, timed inside each of the K whole-path steps
+    fb_ms_per_step = sum(a.elapsed_time(b) for a, b in marks) / args.steps
 
     # per-kernel timing: each pass over the seven matrices, HIP events on the launch stream
     passes = {}
@@ -797,8 +830,15 @@ def main():
     step_bytes = sum(bpw.values()) * weights
     result = {
         "metric": METRIC,
-        "value": weights / (ms_per_step * 1e-3),
+        "value": weights / (fb_ms_per_step * 1e-3),
+        "value_is": "forward + backward weights per second: HIP events on the launch stream around the "
+                    "forward and backward passes of the seven matrices inside each of the K timed steps",
         "unit": "weights/s",
+        "fwd_bwd_ms_per_step": round(fb_ms_per_step, 4),
+        "fwd_bwd_GBps": round((bpw["fwd"] + bpw["bwd"]) * weights / (fb_ms_per_step * 1e-3) / 1e9, 1),
+        "fwd_bwd_pct_hbm_peak": round(100 * (bpw["fwd"] + bpw["bwd"]) * weights / (fb_ms_per_step * 1e-3) / 1e9
+                                      / HBM_PEAK_GBPS, 1),
+        "step_weights_per_s": weights / (ms_per_step * 1e-3),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -813,7 +853,7 @@ def main():
                 "3*onehot(magnitude prior, from nm_prior_init) + N(0,0.1); generated on the GPU",
         "config": {"workload": "LLaMA-2-7B-shaped decoder layer, 7 matrices, 202,375,168 weights, "
                                "2:4, bf16 weights, fp32 logits, kappa=100, tau=4",
-                   "passes_per_step": "fwd+bwd+harden_pack+unpack",
+                   "passes_per_step": "fwd+bwd+harden_pack+unpack (value: fwd+bwd)",
                    "global_batch": 1, "parallelism": "single GPU"},
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
@@ -828,6 +868,13 @@ def main():
                      "algorithmic_bytes_per_launch": round(dom_bytes, 0),
                      "avg_launch_us": passes[dom]["avg_launch_us"]},
     }
+    if not args.no_sweep:
+        # the target's workload: 32 layers x 10 annealed steps of fwd + bwd + harden_pack
+        del mats
+        torch.cuda.empty_cache()
+        sw = workload_sweep32(args)
+        result["sweep32"] = {k: sw[k] for k in ("metric", "value", "unit", "ms_per_step", "GBps", "pct_hbm_peak",
+                                                 "forward_pack_in_one_call", "config")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

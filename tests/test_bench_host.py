@@ -62,3 +62,14 @@ def test_counter_summary_divides_by_the_copy_calibration(tmp_path):
 def test_stored_traffic_is_dropped_when_the_kernels_change(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "not-the-stored-hash")
     assert bench.stored_traffic("bwd") is None
+
+
+def test_cpu_baseline_uses_every_available_core():
+    """The oracle's CPU leg runs on all cores the process may use (affinity, capped by a cgroup
+    quota when set) and reports what the host says next to it."""
+    threads, host = bench.host_cores()
+    assert threads >= 1
+    assert host["os_cpu_count"] == os.cpu_count()
+    assert threads <= host["affinity"] <= (os.cpu_count() or host["affinity"])
+    if host["cgroup_cpu_quota"] is None:
+        assert threads == host["affinity"]
