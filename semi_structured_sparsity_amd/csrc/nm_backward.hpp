@@ -22,8 +22,8 @@ template <int N, int M, typename T, int REG>
 __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     using S = Sample<N, M>;
     constexpr int K = S::K, P = S::P, PK = S::PK;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t g0 = t * P;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
+    const int64_t g0 = tg.g0;
     if (g0 >= a.groups) return;
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
     __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
-    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+    load_logits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
     float w[P * M], gw[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     if constexpr (REG != 2)
@@ -58,23 +58,18 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
             }
         }
         float d[K];
-        float es = 0.0f;
-        static_for<0, K>([&](auto kc) NM_INLINE {
+        float es = -0.0f;
+        candidate_sums<N, M>(aj, [&](auto kc, float dk) NM_INLINE {
             constexpr int k = decltype(kc)::value;
-            float dk = 0.0f;
-            static_for<0, M>([&](auto jc) NM_INLINE {
-                constexpr int j = decltype(jc)::value;
-                if constexpr ((cand_keep<N, M, k>() >> j) & 1u) dk += aj[j];
-            });
             d[k] = dk;
-            es = fmaf(e[k], dk, es);
+            es = k == 0 ? e[k] * dk : fmaf(e[k], dk, es);
         });
         const float s = es * inv;
         const float ci = a.C * inv;
 #pragma unroll
         for (int k = 0; k < K; ++k) dl[p * K + k] = (ci * e[k]) * (d[k] - s);
     }
-    store_dlogits<N, M>(a.dlogits, g0, full, nvalid, staged, tile, dl);
+    store_dlogits<N, M>(a.dlogits, g0, tg.q, full, nvalid, staged, tile, dl);
 }
 
 }  // namespace nm

@@ -136,9 +136,16 @@ __device__ __forceinline__ Philox4 noise_block(const NoiseKey& nk, uint64_t b) {
 // A = kappa*log2(e)/tau and B = 1/tau.  u = (2j + 1) 2^-24 is exact in fp32, and v_log_f32 is
 // within about 1 ulp (relative) for normal inputs, also just below 1 where a is tiny, so
 // h is accurate to a few ulp everywhere.
+//
+// u is formed in two instructions: one v_alignbit_b32 places j under the exponent of 1.0
+// (the float 1 + j 2^-23, in [1, 2)), and subtracting 1 - 2^-24 leaves (2j + 1) 2^-24, which is
+// representable, so the subtraction is exact.
+__device__ __forceinline__ float gumbel_u(uint32_t x) {
+    const float one_j = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, x, 9));  // 0x3F800000 | (x >> 9)
+    return one_j - 0x1.fffffep-1f;
+}
 __device__ __forceinline__ float gumbel_log2(uint32_t x) {
-    const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);  // exact
-    return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+    return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(gumbel_u(x)));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -15,8 +15,8 @@ template <int N, int M, typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     using S = Sample<N, M>;
     constexpr int K = S::K, P = S::P, PK = S::PK;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t g0 = t * P;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
+    const int64_t g0 = tg.g0;
     if (g0 >= a.groups) return;
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     float l[PK];
-    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+    load_logits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
     float w[P * M];
     if constexpr (MODE != 1)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
         } else {
             st_store(reinterpret_cast<uint32_t*>(a.values) + g0 * N, make_uint4(vals[0], vals[1], vals[2], vals[3]));
         }
-        st_store(reinterpret_cast<uint8_t*>(a.indices) + t, (uint8_t)byte);  // byte t
+        st_store(reinterpret_cast<uint8_t*>(a.indices) + g0 / P, (uint8_t)byte);  // the byte of groups g0, g0 + 1
         if (a.hard) st_store(reinterpret_cast<uint16_t*>(a.hard + g0), (uint16_t)hard);
     }
 }
@@ -132,8 +132,8 @@ template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
     using S = Sample<N, M>;
     constexpr int K = S::K, P = S::P, PK = S::PK;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t g0 = t * P;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
+    const int64_t g0 = tg.g0;
     const int64_t left = a.f.groups - g0;
     const int nvalid = left <= 0 ? 0 : (left < P ? (int)left : P);
     const bool full = nvalid == P;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
     }
     const bool staged = block_full<N, M>(a.f.groups);  // uniform over the block
     float l[PK];
-    load_logits<N, M>(a.f.logits, g0, full, nvalid, staged, tile, l);
+    load_logits<N, M>(a.f.logits, g0, tg.q, full, nvalid, staged, tile, l);
     float w[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.f.w) + g0 * M, full, nvalid * M, w);
     uint32_t prev[P];  // issued with the other loads so that its latency overlaps the noise
@@ -295,8 +295,8 @@ template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_prior(PriorArgs a) {
     using S = Sample<N, M>;
     constexpr int K = S::K, P = S::P, PK = S::PK;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t g0 = t * P;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
+    const int64_t g0 = tg.g0;
     if (g0 >= a.groups) return;
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_prior(PriorArgs a) {
         for (int k = 0; k < K; ++k) l[p * K + k] = k == kstar ? a.alpha : 0.0f;
         if (a.idx && p < nvalid) a.idx[g0 + p] = (uint8_t)kstar;
     }
-    store_dlogits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+    store_dlogits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
 }
 
 // ------------------------------------------------------------------------------------------

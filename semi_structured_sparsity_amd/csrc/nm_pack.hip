@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
     const bool full = nvalid == 1;
     const bool staged = block_full<N, M>(groups);  // uniform over the block
     float l[K];
-    load_logits<N, M>(a.logits, g0, full, nvalid, staged, tile, l);
+    load_logits<N, M>(a.logits, g0, threadIdx.x, full, nvalid, staged, tile, l);  // consecutive groups per wave
     uint32_t raw[M];
     if (full) load_group_raw<T, M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true, raw);
     const int lane = threadIdx.x & 63;

@@ -101,6 +101,37 @@ def classify(w, dense, want, m):
     return out
 
 
+def group_dump(w, dense, want, values, indices, m, n, limit=4096):
+    """Per wrong group (up to `limit`): the observed and expected dense group, the group's kept
+    values and index fields as written by the pack, and where each observed value occurs among
+    the packed values of the same row (the value the unpack must have read, and from where)."""
+    if m != 4 or n != 2 or dense.dtype != torch.bfloat16:
+        return []
+    got = bits(dense).cpu().numpy().view(np.uint16)
+    ref = bits(want).cpu().numpy().view(np.uint16)
+    rows, cols = got.shape
+    gpr = cols // m
+    g_got = got.reshape(rows, gpr, m)
+    g_ref = ref.reshape(rows, gpr, m)
+    bad = np.argwhere((g_got != g_ref).any(-1))[:limit]
+    vals = bits(values).cpu().numpy().view(np.uint16).reshape(rows, gpr, n)
+    idx_bytes = indices.cpu().numpy().view(np.uint8).reshape(rows, -1)
+    out = []
+    for r, q in bad:
+        r, q = int(r), int(q)
+        byte = int(idx_bytes[r, q // 2])
+        fields = [(byte >> (2 * (2 * (q % 2) + t))) & 3 for t in range(n)]
+        row_vals = vals[r].reshape(-1)
+        where = []
+        for v in g_got[r, q]:
+            hits = np.flatnonzero(row_vals == v)[:3] if v != 0 else []
+            where.append([int(h) for h in hits])
+        out.append({"row": r, "group": q, "got": [int(x) for x in g_got[r, q]], "want": [int(x) for x in g_ref[r, q]],
+                    "values": [int(x) for x in vals[r, q]], "index_byte": byte, "fields": fields,
+                    "got_found_in_row_values_at": where})
+    return out
+
+
 def _runs(idx):
     """[start, length] of the maximal runs of consecutive indices."""
     if idx.size == 0:
@@ -111,18 +142,31 @@ def _runs(idx):
     return [[int(idx[a]), int(b - a)] for a, b in zip(starts, ends)]
 
 
-def report(tag, w, values, indices, hard, dense, want, m, rechecks, pointers_prev=None):
+def report(tag, w, values, indices, hard, dense, want, m, rechecks, pointers_prev=None, n=2):
     """Print (and write when NM_DIAG_DIR is set) the classification of a failed round trip."""
     doc = {"tag": tag, "time": time.time(), "shape": list(w.shape), "dtype": str(w.dtype),
            "pointers": {k: int(t.data_ptr()) for k, t in (("w", w), ("values", values), ("indices", indices),
                                                            ("dense", dense)) if t is not None},
            "pointers_prev": pointers_prev or {},
            "classification": classify(w, dense, want, m)}
+    try:
+        st = torch.cuda.memory_stats(dense.device)
+        doc["allocator"] = {k: st.get(k) for k in ("num_alloc_retries", "num_device_alloc", "num_device_free",
+                                                   "segment.all.current", "reserved_bytes.all.current",
+                                                   "num_sync_all_streams")}
+    except Exception as e:
+        doc["allocator_error"] = repr(e)
+    try:
+        doc["groups"] = group_dump(w, dense, want, values, indices, m, n)
+    except Exception as e:  # the dump must never hide the classification
+        doc["groups_error"] = repr(e)
     doc["reused_from_prev"] = sorted(k for k, p in doc["pointers"].items()
                                      if p in set((pointers_prev or {}).values()))
     doc.update(rechecks)
     line = json.dumps(doc)
-    print("ROUND TRIP DIAGNOSIS", line, flush=True)
+    short = {k: v for k, v in doc.items() if k != "groups"}
+    short["groups_first"] = doc.get("groups", [])[:6]
+    print("ROUND TRIP DIAGNOSIS", json.dumps(short), flush=True)
     d = os.environ.get("NM_DIAG_DIR")
     if d:
         os.makedirs(d, exist_ok=True)

@@ -127,7 +127,7 @@ def _report_unpack(tag, w, n, m, values, indices, hard, dense, rd, want):
         "dense_vs_selection_wrong": int((_bits(dense) != want).sum()),
         "second_copy_equal": bool(np.array_equal(again, got)),
     }
-    roundtrip_diag.report(tag, w, values, indices, hard, dense, want, m, rechecks, _PREV_POINTERS)
+    roundtrip_diag.report(tag, w, values, indices, hard, dense, want, m, rechecks, _PREV_POINTERS, n=n)
     # then repeat the unpack: into a fresh poisoned buffer, and into the same buffer
     d2 = S.nm_unpack(values, indices, cols, n, m, out=roundtrip_diag.poisoned(tuple(w.shape), w.dtype, w.device))
     again2 = {"repeat_unpack_equals_oracle": bool(np.array_equal(_bits(d2).cpu().numpy(), ref)),
@@ -279,7 +279,7 @@ def test_config4_nemotron15b_every_matrix_round_trip():
                             "repeat_unpack_equals_selection": bool(torch.equal(_bits(d2), want)),
                             "repeat_unpack_equals_first": bool(torch.equal(_bits(d2), _bits(dense)))}
                 roundtrip_diag.report(f"config4 layer {layer} {name}", w, values, indices, hard, dense, want,
-                                      m, rechecks, _PREV_POINTERS)
+                                      m, rechecks, _PREV_POINTERS, n=n)
                 S.nm_unpack(values, indices, cols, n, m, out=dense)  # again, into the same buffer
                 _say("ROUND TRIP RECHECKS", {"same_buffer_unpack_equals_selection": bool(torch.equal(_bits(dense), want))})
             _PREV_POINTERS = {k: t.data_ptr() for k, t in (("values", values), ("indices", indices),

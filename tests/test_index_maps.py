@@ -270,15 +270,29 @@ def model_unpack_general(b, rows, cols, n, m, wb):
 # ---------------------------------------------------------------------------------------------
 # forward / backward: P groups per thread on a flat grid
 
+def thread_slot(tid, n, m):
+    """The thread's place in its block (thread_group in nm_layer.hpp): for K = 70 the waves of a
+    block take groups of one parity, waves 0-1 the even ones and waves 2-3 the odd ones."""
+    K, P, PK, lalign, stage = sample_tiling(n, m)
+    if (P * K) % 4 == 0:
+        return tid
+    return 2 * ((tid & 63) + 64 * ((tid >> 6) & 1)) + (tid >> 7)
+
+
 def model_forward_backward(rows, cols, n, m, wb):
     gpr = cols // m
     groups = rows * gpr
     K, P, PK, lalign, stage = sample_tiling(n, m)
     t = np.arange(grid_for((groups + P - 1) // P) * THREADS, dtype=np.int64)
-    g0 = t * P
-    live = g0 < groups
-    t, g0 = t[live], g0[live]
     blk, tid = t // THREADS, t % THREADS
+    q = thread_slot(tid, n, m)
+    g0 = (blk * THREADS + q) * P
+    live = g0 < groups
+    blk, tid, g0 = blk[live], q[live], g0[live]
+    if (P * K) % 4 != 0:  # every wave's groups share a parity, so the noise phase is wave-uniform
+        wave = (blk * THREADS + t[live] % THREADS) // 64
+        par = g0 % 2
+        assert all(len(set(par[wave == wv])) == 1 for wv in np.unique(wave)[:512])
     nvalid = np.minimum(groups - g0, P)
     fwd = dict(w=Buf(rows * cols * wb), logits=Buf(groups * K * 4), out=Buf(rows * cols * wb))
     bwd = dict(w=Buf(rows * cols * wb), grad=Buf(rows * cols * wb), logits=Buf(groups * K * 4),
@@ -348,7 +362,8 @@ def test_ragged_pack_unpack_index_maps(n, m, wb):
 
 
 @pytest.mark.parametrize("rows,cols,n,m,wb", FULL[:2] + [(3, 20, 2, 4, 2), (5, 24, 3, 8, 4), (7, 88, 4, 8, 2),
-                                                          (1, 12, 1, 4, 4), (3, 36, 3, 4, 2)])
+                                                          (1, 12, 1, 4, 4), (3, 36, 3, 4, 2), (4096, 11008, 4, 8, 2),
+                                                          (37, 184, 4, 8, 2)])
 def test_forward_backward_index_maps(rows, cols, n, m, wb):
     fwd, bwd = model_forward_backward(rows, cols, n, m, wb)
     fwd["out"].assert_written_once("k_forward out")
