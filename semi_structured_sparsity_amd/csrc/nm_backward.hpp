@@ -30,14 +30,21 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
 
     __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
+    // The logits go through LDS before the noise is generated (generating the noise while they
+    // are in flight, as k_forward does for groups of eight, measured slower here: the backward
+    // already overlaps its weight and gradient loads with that work).
+    constexpr bool EARLY = false;
     float l[PK];
-    load_logits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
+    StagedSpan<N, M> span;
+    logits_issue<N, M>(a.logits, g0, full, nvalid, staged, span, l);
+    if constexpr (!EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     float w[P * M], gw[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     if constexpr (REG != 2)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.grad) + g0 * M, full, nvalid * M, gw);
     float h[PK];
     thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
+    if constexpr (EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
 
     float dl[PK];
 #pragma unroll

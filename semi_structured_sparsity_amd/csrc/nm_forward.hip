@@ -23,13 +23,19 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
 
     __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
     const bool staged = block_full<N, M>(a.groups);  // uniform over the block
+    // Groups of eight: the noise (hundreds of instructions per group) is generated while the
+    // logit loads are in flight, and the logits go through LDS afterwards.
+    constexpr bool EARLY = M == 8;
     float l[PK];
-    load_logits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
+    StagedSpan<N, M> span;
+    logits_issue<N, M>(a.logits, g0, full, nvalid, staged, span, l);
+    if constexpr (!EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     float w[P * M];
     if constexpr (MODE != 1)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     float h[PK];
     thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
+    if constexpr (EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
 
     float out[P * M];
 #pragma unroll

@@ -86,9 +86,6 @@ struct Sample {
     static constexpr bool STAGE = PK * 4 > LALIGN;
 };
 
-template <int VW> struct StageVec;
-template <> struct StageVec<16> { using type = float4; };
-template <> struct StageVec<8> { using type = float2; };
 
 // The group a thread of a sampling kernel owns.  A thread owns P consecutive groups, block by
 // block.  For K = 70 (one group per thread; 70 slots are 17.5 Philox blocks) an even group's
@@ -275,9 +272,18 @@ __device__ __forceinline__ void candidate_sums(const float (&aj)[M], F&& use) {
 template <int N, int M>
 struct StageTile {
     using S = Sample<N, M>;
-    using vec = typename StageVec<S::LALIGN>::type;
-    static constexpr int PER = S::PK * 4 / S::LALIGN;               // vectors per thread
-    static constexpr int VEC = S::STAGE ? kThreads * PER : 1;       // vectors per tile
+    using vec = float4;                                    // LDS element: the span moves in 16-byte vectors
+    static constexpr int G16 = kThreads * S::PK / 4;       // 16-byte vectors of a block's span
+    static constexpr int ROUNDS = (G16 + kThreads - 1) / kThreads;  // per thread (the last guarded)
+    static constexpr bool EVEN = G16 % kThreads == 0;
+    static constexpr int VEC = S::STAGE ? G16 : 1;         // vectors per tile
+    static_assert(kThreads * S::PK % 4 == 0, "a block's span is whole 16-byte vectors");
+};
+
+// The HBM side of a staged span, held in registers between the loads and the LDS exchange.
+template <int N, int M>
+struct StagedSpan {
+    uint4 v[StageTile<N, M>::ROUNDS];
 };
 
 template <int N, int M>
@@ -295,65 +301,98 @@ __device__ __forceinline__ V floats_to_vec(const float* in) {
     if constexpr (sizeof(V) == 16) return make_float4(in[0], in[1], in[2], in[3]);
     else return make_float2(in[0], in[1]);
 }
-template <typename V>
-__device__ __forceinline__ void nt_store_vec(V* p, const V& v) {
-    if constexpr (sizeof(V) == 16)
-        nt_store(p, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
-    else
-        nt_store(p, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
-}
 
-// q: the thread's place in the block's tile (thread_group); g0: its first group.
+// Logits in two steps, so that work independent of them (the noise) can run while the loads are
+// in flight.  logits_issue: a staged block's span is loaded into registers, 16-byte vectors with
+// consecutive lanes on consecutive vectors; a thread of an unstaged block loads its own logits
+// directly into l.  logits_exchange: the staged span goes through the LDS tile, and each thread
+// reads its PK floats at float offset q * PK (q: its place in the block, thread_group).
 template <int N, int M>
-__device__ __forceinline__ void load_logits(const float* logits, int64_t g0, int q, bool full, int nvalid, bool staged,
-                                            typename StageTile<N, M>::vec* tile, float (&l)[Sample<N, M>::PK]) {
+__device__ __forceinline__ void logits_issue(const float* logits, int64_t g0, bool full, int nvalid, bool staged,
+                                             StagedSpan<N, M>& st, float (&l)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
     using ST = StageTile<N, M>;
-    using V = typename ST::vec;
-    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
     if constexpr (S::STAGE) {
         if (staged) {
-            const V* src = reinterpret_cast<const V*>(logits + (int64_t)blockIdx.x * kThreads * PK);
+            const uint4* src = reinterpret_cast<const uint4*>(logits + (int64_t)blockIdx.x * kThreads * S::PK);
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if constexpr (sizeof(V) == 16) {
-                    const uint4 u = nt_load4(src + threadIdx.x + i * kThreads);
-                    tile[threadIdx.x + i * kThreads] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
-                } else {
-                    const uint2 u = nt_load2(src + threadIdx.x + i * kThreads);
-                    tile[threadIdx.x + i * kThreads] = make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
-                }
+            for (int r = 0; r < ST::ROUNDS; ++r) {
+                const int i = threadIdx.x + r * kThreads;
+                if (ST::EVEN || r + 1 < ST::ROUNDS || i < ST::G16) st.v[r] = nt_load4(src + i);
             }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < PER; ++i) vec_to_floats(tile[q * PER + i], l + W * i);
             return;
         }
     }
-    load_f32<PK, S::LALIGN>(logits + g0 * S::K, full, nvalid * S::K, l);
+    load_f32<S::PK, S::LALIGN>(logits + g0 * S::K, full, nvalid * S::K, l);
+}
+
+template <int N, int M>
+__device__ __forceinline__ void logits_exchange(int q, bool staged, float4* tile, const StagedSpan<N, M>& st,
+                                                float (&l)[Sample<N, M>::PK]) {
+    using S = Sample<N, M>;
+    using ST = StageTile<N, M>;
+    if constexpr (S::STAGE) {
+        if (staged) {
+#pragma unroll
+            for (int r = 0; r < ST::ROUNDS; ++r) {
+                const int i = threadIdx.x + r * kThreads;
+                if (ST::EVEN || r + 1 < ST::ROUNDS || i < ST::G16)
+                    tile[i] = make_float4(__uint_as_float(st.v[r].x), __uint_as_float(st.v[r].y),
+                                          __uint_as_float(st.v[r].z), __uint_as_float(st.v[r].w));
+            }
+            __syncthreads();
+            const float* mine = reinterpret_cast<const float*>(tile) + q * S::PK;
+            if constexpr (S::LALIGN == 16) {
+#pragma unroll
+                for (int i = 0; i < S::PK / 4; ++i) vec_to_floats(reinterpret_cast<const float4*>(mine)[i], l + 4 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < S::PK / 2; ++i) vec_to_floats(reinterpret_cast<const float2*>(mine)[i], l + 2 * i);
+            }
+        }
+    }
+}
+
+// Both steps at once.
+template <int N, int M>
+__device__ __forceinline__ void load_logits(const float* logits, int64_t g0, int q, bool full, int nvalid, bool staged,
+                                            float4* tile, float (&l)[Sample<N, M>::PK]) {
+    StagedSpan<N, M> st;
+    logits_issue<N, M>(logits, g0, full, nvalid, staged, st, l);
+    logits_exchange<N, M>(q, staged, tile, st, l);
 }
 
 template <int N, int M>
 __device__ __forceinline__ void store_dlogits(float* dlogits, int64_t g0, int q, bool full, int nvalid, bool staged,
-                                              typename StageTile<N, M>::vec* tile,
-                                              const float (&dl)[Sample<N, M>::PK]) {
+                                              float4* tile, const float (&dl)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
     using ST = StageTile<N, M>;
-    using V = typename ST::vec;
-    constexpr int PK = S::PK, PER = ST::PER, W = S::LALIGN / 4;
     if constexpr (S::STAGE) {
         if (staged) {
             __syncthreads();  // every thread has read its logits out of the tile
+            float* mine = reinterpret_cast<float*>(tile) + q * S::PK;
+            if constexpr (S::LALIGN == 16) {
 #pragma unroll
-            for (int i = 0; i < PER; ++i) tile[q * PER + i] = floats_to_vec<V>(dl + W * i);
+                for (int i = 0; i < S::PK / 4; ++i) reinterpret_cast<float4*>(mine)[i] = floats_to_vec<float4>(dl + 4 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < S::PK / 2; ++i) reinterpret_cast<float2*>(mine)[i] = floats_to_vec<float2>(dl + 2 * i);
+            }
             __syncthreads();
-            V* dst = reinterpret_cast<V*>(dlogits + (int64_t)blockIdx.x * kThreads * PK);
+            uint4* dst = reinterpret_cast<uint4*>(dlogits + (int64_t)blockIdx.x * kThreads * S::PK);
 #pragma unroll
-            for (int i = 0; i < PER; ++i) nt_store_vec(dst + threadIdx.x + i * kThreads, tile[threadIdx.x + i * kThreads]);
+            for (int r = 0; r < ST::ROUNDS; ++r) {
+                const int i = threadIdx.x + r * kThreads;
+                if (ST::EVEN || r + 1 < ST::ROUNDS || i < ST::G16) {
+                    const float4 v = tile[i];
+                    nt_store(dst + i, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                                 __float_as_uint(v.w)));
+                }
+            }
             return;
         }
     }
-    store_f32<PK, S::LALIGN>(dlogits + g0 * S::K, full, nvalid * S::K, dl);
+    store_f32<S::PK, S::LALIGN>(dlogits + g0 * S::K, full, nvalid * S::K, dl);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -522,6 +561,32 @@ __device__ __forceinline__ void store_group_raw(typename T::storage* p, bool vec
     }
 #pragma unroll
     for (int i = 0; i < CNT; ++i) store_bits<T>(p, i, in[i]);
+}
+
+// ------------------------------------------------------------------------------------------
+// Bit-field and 16-bit slot helpers in 32-bit operations only.  MI355X was measured to compute
+// v_lshlrev_b64 (and its right-shift forms) wrongly, now and then, when the shift amount is a
+// VGPR at the end of an 8-register allocation block: an unpack whose two such shifts placed the
+// second group's kept values produced wrong dense groups in about one in 10^5 threads (the
+// other group of the same thread, shifted by amounts in other registers, never).  The pack and
+// unpack kernels therefore never shift a 64-bit value by a register amount.
+
+// Low 32 bits of the 64-bit value (hi:lo) shifted right by s, 0 <= s < 32 (one v_alignbit).
+__device__ __forceinline__ uint32_t funnel_right(uint32_t hi, uint32_t lo, uint32_t s) {
+    return __builtin_amdgcn_alignbit(hi, lo, s);
+}
+// (lo << s) as a 64-bit value, 0 <= s < 32: the low word and the bits shifted out of it.
+__device__ __forceinline__ uint32_t shl_lo(uint32_t lo, uint32_t s) { return lo << s; }
+__device__ __forceinline__ uint32_t shl_carry(uint32_t lo, uint32_t s) { return (lo >> 1) >> (31u - s); }
+
+// Put the 16-bit value v at position p (0..3) of four 16-bit elements held as two 32-bit words
+// (w0: positions 0-1, w1: positions 2-3), replacing what is there.
+__device__ __forceinline__ void put16(uint32_t& w0, uint32_t& w1, uint32_t p, uint32_t v) {
+    const uint32_t sh = (p & 1u) << 4;
+    const uint32_t m = 0xFFFFu << sh, x = v << sh;
+    const uint32_t n0 = (w0 & ~m) | x, n1 = (w1 & ~m) | x;
+    w0 = p < 2u ? n0 : w0;
+    w1 = p < 2u ? w1 : n1;
 }
 
 // General pack/unpack: a block owns a tile of consecutive groups of one row (grid x = tile within

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
         __builtin_amdgcn_wave_barrier();
         if (mine > 0) {
             uint32_t v[GT * N], hard[GT];
-            uint64_t acc = 0;
+            uint32_t acc = 0;  // TBITS <= 32
 #pragma unroll
             for (int i = 0; i < GT; ++i) {
                 const float* li = l + i * K;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
 #pragma unroll
                     for (int j = 1; j < M; ++j) x = p == j ? raw[i * M + j] : x;
                     v[i * N + tt] = x;
-                    if (i < mine) acc |= (uint64_t)p << ((i * N + tt) * BITS);
+                    if (i < mine) acc |= (uint32_t)p << ((i * N + tt) * BITS);
                 }
             }
             auto* vp = reinterpret_cast<typename T::storage*>(a.values) + g0 * N;
@@ -86,8 +86,10 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackArgs a) {
                 for (int i = 0; i < GT; ++i)
                     if (i < mine) st_store(a.hard + g0 + i, (uint8_t)hard[i]);
             }
-            atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
-            if ((lb % 32) + TS::TBITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
+            // a thread's fields fit one word (TBITS <= 32); at bit lb % 32 they may straddle two
+            const uint32_t f = acc, s = (uint32_t)(lb % 32);
+            atomicOr(&ww[lb / 32], shl_lo(f, s));
+            if ((lb % 32) + TS::TBITS > 32) atomicOr(&ww[lb / 32 + 1], shl_carry(f, s));
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
             keep = up ? cand_keep<N, M, k>() : keep;
         });
         uint32_t v[N];
-        uint64_t acc = 0;
+        uint32_t acc = 0;  // N * BITS <= 21
 #pragma unroll
         for (int tt = 0; tt < N; ++tt) {
             const int p = __builtin_ctz(keep);  // kept positions in ascending order
@@ -150,13 +152,14 @@ __global__ __launch_bounds__(kThreads) void k_pack_flat8(PackArgs a) {
 #pragma unroll
             for (int j = 1; j < M; ++j) x = p == j ? raw[j] : x;
             v[tt] = x;
-            acc |= (uint64_t)p << (tt * BITS);
+            acc |= (uint32_t)p << (tt * BITS);
         }
         store_group_raw<T, N>(reinterpret_cast<typename T::storage*>(a.values) + g0 * N, true, v);
         if (a.hard) st_store(a.hard + g0, (uint8_t)bk);
         const int lb = lane * N * BITS;  // the thread's first bit in the wave's words
-        atomicOr(&ww[lb / 32], (uint32_t)(acc << (lb % 32)));
-        if ((lb % 32) + N * BITS > 32) atomicOr(&ww[lb / 32 + 1], (uint32_t)((acc << (lb % 32)) >> 32));
+        const uint32_t f = acc, s = (uint32_t)(lb % 32);
+        atomicOr(&ww[lb / 32], shl_lo(f, s));
+        if ((lb % 32) + N * BITS > 32) atomicOr(&ww[lb / 32 + 1], shl_carry(f, s));
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -180,9 +183,8 @@ __global__ __launch_bounds__(kThreads) void k_unpack_flat8(UnpackArgs a) {
     load_group_raw<T, N>(reinterpret_cast<const typename T::storage*>(a.values) + g0 * N, true, v);
     const int64_t lb = g0 * N * BITS;  // the group's first bit in the flat stream
     const uint32_t* idx = a.indices + lb / 32;
-    uint64_t acc = idx[0];
-    if ((lb % 32) + N * BITS > 32) acc |= (uint64_t)idx[1] << 32;  // only when the fields straddle
-    acc >>= lb % 32;
+    const uint32_t w1 = (lb % 32) + N * BITS > 32 ? idx[1] : 0u;  // read only when the fields straddle
+    const uint32_t acc = funnel_right(w1, idx[0], (uint32_t)(lb % 32));
     uint32_t pos[N];
 #pragma unroll
     for (int tt = 0; tt < N; ++tt) pos[tt] = (uint32_t)(acc >> (tt * BITS)) & 7u;
@@ -222,9 +224,8 @@ __global__ __launch_bounds__(kThreads) void k_unpack(UnpackArgs a) {
             for (int e = 0; e < GT * N; ++e) v[e] = e < mine * N ? load_bits<T>(vp, e) : 0u;
         }
         const uint32_t* idx = a.indices + r * a.words_per_row + lb / 32;
-        uint64_t acc = idx[0];
-        if ((lb % 32) + mine * N * BITS > 32) acc |= (uint64_t)idx[1] << 32;
-        acc >>= lb % 32;
+        const uint32_t w1 = (lb % 32) + mine * N * BITS > 32 ? idx[1] : 0u;
+        const uint32_t acc = funnel_right(w1, idx[0], (uint32_t)(lb % 32));
 #pragma unroll
         for (int i = 0; i < GT; ++i) {
             uint32_t pos[N];
@@ -354,19 +355,16 @@ __global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
         v[0] = d.x & 0xFFFFu; v[1] = d.x >> 16; v[2] = d.y & 0xFFFFu; v[3] = d.y >> 16;
     }
     if constexpr (T::bytes == 2) {
-        // a group's four bf16 outputs form one 64-bit word: each kept value is shifted to its
-        // position, clearing what an earlier field put there (later field wins)
+        // a group's four bf16 outputs are two 32-bit words: each kept value goes to its
+        // position, replacing what an earlier field put there (later field wins)
         uint32_t w[2 * U];
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-            uint64_t o = 0u;  // +0.0 where nothing is kept
+            uint32_t w0 = 0u, w1 = 0u;  // +0.0 where nothing is kept
 #pragma unroll
-            for (int tt = 0; tt < N; ++tt) {
-                const uint32_t sh = 16u * ((byte >> (2 * (q * N + tt))) & 3u);
-                o = (o & ~(0xFFFFull << sh)) | ((uint64_t)v[q * N + tt] << sh);
-            }
-            w[2 * q] = (uint32_t)o;
-            w[2 * q + 1] = (uint32_t)(o >> 32);
+            for (int tt = 0; tt < N; ++tt) put16(w0, w1, (byte >> (2 * (q * N + tt))) & 3u, v[q * N + tt]);
+            w[2 * q] = w0;
+            w[2 * q + 1] = w1;
         }
         auto* dp = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.dense) + g0 * M);
 #pragma unroll
@@ -404,9 +402,10 @@ __global__ __launch_bounds__(kThreads) void k_unpack_1of4(UnpackArgs a) {
     auto* dp = reinterpret_cast<uint4*>(reinterpret_cast<typename T::storage*>(a.dense) + g0 * 4);
     if constexpr (T::bytes == 2) {
         const uint32_t v = reinterpret_cast<const uint32_t*>(a.values)[t];  // the two kept values
-        const uint64_t o0 = (uint64_t)(v & 0xFFFFu) << (16u * (f & 3u));
-        const uint64_t o1 = (uint64_t)(v >> 16) << (16u * ((f >> 2) & 3u));
-        nt_store(dp, make_uint4((uint32_t)o0, (uint32_t)(o0 >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32)));
+        uint32_t a0 = 0u, a1 = 0u, b0 = 0u, b1 = 0u;
+        put16(a0, a1, f & 3u, v & 0xFFFFu);
+        put16(b0, b1, (f >> 2) & 3u, v >> 16);
+        nt_store(dp, make_uint4(a0, a1, b0, b1));
     } else {
         const uint32_t v = reinterpret_cast<const uint32_t*>(a.values)[t];
         const uint32_t p = f & 3u;
