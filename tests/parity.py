@@ -12,11 +12,12 @@ outputs), with "relative" made precise for each quantity:
   magnitude of the terms that form it: |gpu_k - ref_k| <= tol * c y_k (|d_k| + sum_i y_i |d_i|)
   plus an underflow floor.
 
-Where the kernel's fp32 evaluation cannot reach tol = 1e-5 -- at small tau, where the fp32
-Gumbel exponent's own rounding is amplified by 1/tau -- each element's bound is the larger of
-the stated one and the bound derived from that evaluation (`prob_bound` and the `dy` / `dm`
-arguments below): the error of each fp32 operation of the kernel, propagated through the
-softmax, the soft mask and the backward.
+Below tau = 1/2 the kernel's fp32 evaluation cannot reach tol = 1e-5: the fp32 Gumbel
+exponent's own rounding (2^-22 |h| relative) is amplified by 1/tau.  There each element's bound
+is the larger of the stated one and the bound derived from that evaluation (`prob_bound` and the
+`dy` / `dm` arguments below): the error of each fp32 operation of the kernel, propagated through
+the softmax, the soft mask and the backward.  From tau = 1/2 up the stated bound alone applies
+(`derived_below`).
 """
 import numpy as np
 
@@ -24,6 +25,16 @@ TOL_FP32 = 1e-5
 TOL_BF16 = 1e-2
 U24 = 2.0**-24     # unit roundoff of fp32
 LOG2E = 1.4426950408889634
+
+
+TAU_DERIVED = 0.5  # below this temperature the derived fp32 bound joins the stated one
+
+
+def derived_below(tau, *bounds):
+    """The derived bounds when tau < 1/2, else None for each (the stated tolerance alone)."""
+    keep = float(tau) < TAU_DERIVED
+    out = tuple(b if keep else None for b in bounds)
+    return out if len(out) > 1 else out[0]
 
 
 def prob_bound(L, kappa, tau, words, gumbel, y, n, m):

@@ -22,7 +22,7 @@ import oracle
 import semi_structured_sparsity_amd as S
 from oracle_inputs import oracle_prior
 import roundtrip_diag
-from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, oracle_bounds,
+from parity import (TOL_FP32, backward_check, candidate_sums, derived_below, forward_check, oracle_bounds,
                     soft_mask_check)
 
 pytestmark = pytest.mark.gpu
@@ -59,6 +59,7 @@ def _check_rows(w, L, G, n, m, kappa, tau, seed, offset, out_fwd, out_bwd, rows_
         ref = oracle.forward(wr, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r0)
         y, dy, dm = oracle_bounds(oracle, Lr, n, m, kappa, tau, seed, offset, rows=rows, row_begin=r0)
         soft = (y @ cand).reshape(r1 - r0, -1)
+        dy, dm = derived_below(tau, dy, dm)
         rel, bad = forward_check(out_fwd[r0:r1].double().cpu().numpy(), ref, wd, soft, m, TOL_FP32, bf16, dm)
         assert bad == 0, f"forward rows {r0}..{r1 - 1}: {bad} elements out of tolerance (worst {rel})"
         worst_f = max(worst_f, rel)
