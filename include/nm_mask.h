@@ -62,6 +62,8 @@
  *   NM_EUNSUPPORTED (n, m) or wtype outside the supported set
  *   NM_EALIGN       a data pointer that is not 16-byte aligned
  *   NM_EHIP         the HIP launch failed (hipGetLastError is consumed)
+ *   NM_ESCRATCH     the shape needs more scratch memory than nm_mask_forward_monitor_static's
+ *                   fixed array holds
  */
 #ifndef NM_MASK_H
 #define NM_MASK_H
@@ -77,7 +79,8 @@ typedef enum {
     NM_EINVAL = 1,
     NM_EALIGN = 2,
     NM_EUNSUPPORTED = 3,
-    NM_EHIP = 4
+    NM_EHIP = 4,
+    NM_ESCRATCH = 5
 } nm_status;
 
 enum { NM_F32 = 0, NM_BF16 = 1 };
@@ -127,6 +130,25 @@ nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample
                                   const float *logits, void *w_masked, const uint8_t *prev_sample,
                                   uint8_t *sample_idx, double *stats, void *workspace,
                                   int64_t workspace_bytes, void *stream);
+
+/* nm_mask_forward_monitor for callers that cannot allocate device memory (code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results, with the per-block partial sums kept in a fixed array of NM_MONITOR_SCRATCH_BYTES
+ * in device memory that the library owns (one per GPU, held until the process ends) instead
+ * of a caller workspace.  Nothing is allocated: the array's address is looked up once per
+ * device, on the first call with that device current.
+ *   arguments   as nm_mask_forward_monitor, without the workspace
+ *   NM_ESCRATCH the shape needs more than NM_MONITOR_SCRATCH_BYTES (nm_monitor_workspace_bytes
+ *               tells how much it needs), checked before any HIP call
+ *   NM_EHIP     the array's address could not be looked up, or the launch failed
+ * The array is shared by every call on the same GPU and keeps the last call's partial sums
+ * (each call overwrites the entries it uses before reading them): calls on one GPU whose
+ * executions overlap (on different streams, or from different host threads) race and must be
+ * ordered by the caller.  The stream's device must be the calling thread's current device. */
+#define NM_MONITOR_SCRATCH_BYTES (1 << 20)
+nm_status nm_mask_forward_monitor_static(const nm_shape *shape, const nm_sample *sample, const void *w,
+                                         const float *logits, void *w_masked, const uint8_t *prev_sample,
+                                         uint8_t *sample_idx, double *stats, void *stream);
 
 /* Backward to the logits (Fig. 3 caption: every step is differentiable).  With the upstream
  * gradient G = dL/dw_masked, d_k = sum over positions j kept by candidate k of G_j * w_j,

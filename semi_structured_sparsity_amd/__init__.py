@@ -18,6 +18,7 @@ Entry points, named as in the C ABI:
     nm_prior_init(w, n, m, alpha, with_idx=False)                     -> logits[, prior_idx]
     nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None)
                                                                       -> w_masked, sample, stats
+    nm_mask_forward_monitor_static(...)                               the same, with no workspace
 and `mask(...)`, the autograd function whose backward is nm_mask_backward, or
 nm_mask_backward_wreg when a weight-regulariser strength is given (the weights are frozen and get
 no gradient).
@@ -29,7 +30,8 @@ import torch
 
 from . import build as _build
 
-NM_OK, NM_EINVAL, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(5)
+NM_OK, NM_EINVAL, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP, NM_ESCRATCH = range(6)
+MONITOR_SCRATCH_BYTES = 1 << 20  # NM_MONITOR_SCRATCH_BYTES
 NM_F32, NM_BF16 = 0, 1
 
 _lib = None
@@ -65,6 +67,7 @@ _SIGNATURES = {
     "nm_unpack": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nm_prior_init": (ctypes.c_int, [_P, ctypes.c_float, _P, _P, _P, _P]),
     "nm_mask_forward_monitor": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int64, _P]),
+    "nm_mask_forward_monitor_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nm_monitor_workspace_bytes": (ctypes.c_int64, [_P]),
     "nm_sparse_matmul": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, _P]),
     "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
@@ -232,6 +235,29 @@ def nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_samp
         _dev(stats, "stats", torch.float64, (2,)), _dev(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(w.device))
     _check(st, "nm_mask_forward_monitor")
+    return w_masked, sample, stats
+
+
+def nm_mask_forward_monitor_static(w, logits, n, m, kappa, tau, seed, offset, prev_sample=None, out=None):
+    """nm_mask_forward_monitor without a workspace: the partial sums live in the library's fixed
+    device array (NM_MONITOR_SCRATCH_BYTES per GPU), for callers that cannot allocate.  With
+    `out` given, nothing is allocated here either.  Calls whose executions overlap on one GPU
+    race on that array."""
+    rows, cols = w.shape
+    sh = _shape(rows, cols, n, m, _wtype(w.dtype))
+    if out is None:
+        out = (torch.empty_like(w), torch.empty((rows, cols // m), dtype=torch.uint8, device=w.device),
+               torch.zeros(2, dtype=torch.float64, device=w.device))
+    w_masked, sample, stats = out
+    gshape = (rows, cols // m)
+    st = lib().nm_mask_forward_monitor_static(
+        ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)), _dev(w, "w"),
+        _dev(logits, "logits", torch.float32, _logit_shape(rows, cols, n, m)),
+        _dev(w_masked, "w_masked", w.dtype, w.shape),
+        None if prev_sample is None else _dev(prev_sample, "prev_sample", torch.uint8, gshape),
+        None if sample is None else _dev(sample, "sample", torch.uint8, gshape),
+        _dev(stats, "stats", torch.float64, (2,)), _stream(w.device))
+    _check(st, "nm_mask_forward_monitor_static")
     return w_masked, sample, stats
 
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/nm_mask.h"
 #include "nm_kernels.hpp"
 
@@ -66,6 +68,42 @@ nm_status launched(hipError_t e) { return e == hipSuccess ? NM_OK : NM_EHIP; }
 
 }  // namespace
 
+// ------------------------------------------------------------------------------------------
+// nm_mask_forward_monitor_static: the monitored forward with its per-block partial sums in a
+// fixed device array instead of a caller workspace.  In host code the array's name only stands
+// for the symbol: its device address (one per GPU, each GPU holds its own copy) is looked up
+// with hipGetSymbolAddress once per device, with that device current, and only that address is
+// handed to the kernels.
+
+static __device__ __align__(256) unsigned char scratch[NM_MONITOR_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until looked up
+
+nm_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return NM_EHIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return NM_EHIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t nm_num_candidates(int32_t n, int32_t m) { return supported_nm(n, m) ? binom_host(m, n) : -1; }
@@ -112,6 +150,7 @@ const char* nm_status_str(nm_status st) {
     case NM_EALIGN: return "pointer not 16-byte aligned";
     case NM_EUNSUPPORTED: return "unsupported n:m or element type";
     case NM_EHIP: return "HIP launch failed";
+    case NM_ESCRATCH: return "shape needs more scratch memory than the static array holds";
     default: return "unknown status";
     }
 }
@@ -129,6 +168,29 @@ nm_status nm_mask_forward(const nm_shape* shape, const nm_sample* sample, const 
     if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked)) return NM_EALIGN;
     nm::FwdArgs a{w, logits, w_masked, groups, A, B, noise_key(sample)};
     return launched(nm::launch_forward(shape->n, shape->m, shape->wtype, a, false, (hipStream_t)stream));
+}
+
+// The monitored forward with its partial sums in the static array (see `scratch` above).
+nm_status nm_mask_forward_monitor_static(const nm_shape* shape, const nm_sample* sample, const void* w,
+                                         const float* logits, void* w_masked, const uint8_t* prev_sample,
+                                         uint8_t* sample_idx, double* stats, void* stream) {
+    int64_t groups;
+    int32_t K;
+    float A, B, C;
+    nm_status st = check_shape(shape, &groups, &K);
+    if (st != NM_OK) return st;
+    if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
+    if (groups == 0) return NM_OK;
+    if (!w || !logits || !w_masked || !stats) return NM_EINVAL;
+    if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked) || !aligned16(stats)) return NM_EALIGN;
+    const int64_t need = 8 * nm::monitor_parts(shape->n, shape->m, groups);
+    if (need > NM_MONITOR_SCRATCH_BYTES) return NM_ESCRATCH;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != NM_OK) return st;
+    const float A0 = (float)((double)sample->kappa * 1.4426950408889634074);
+    nm::MonitorArgs a{nm::FwdArgs{w, logits, w_masked, groups, A, B, noise_key(sample)},
+                      prev_sample, sample_idx, static_cast<float2*>(ws), stats, A0};
+    return launched(nm::launch_forward_monitor(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
 int64_t nm_monitor_workspace_bytes(const nm_shape* shape) {

@@ -262,3 +262,19 @@ def test_device_offset_pointer_rules():
     assert L.nm_mask_backward_offset_dev(sh, smp, FAKE, FAKE, FAKE, None, FAKE, None) == NM_EINVAL
     assert L.nm_mask_forward_offset_dev(sh, _sample(1.0, 0.0), FAKE, FAKE, FAKE, FAKE, None) == NM_EINVAL
     assert L.nm_mask_backward_offset_dev(_shape(rows=0), smp, None, None, None, None, None, None) == NM_OK
+
+
+def test_static_monitor_refuses_shapes_past_its_scratch_size():
+    """nm_mask_forward_monitor_static checks its fixed array's size on the host, before any HIP
+    call: the fake aligned pointers below are never used."""
+    L = S.lib()
+    rows, cols = 70000, 4096  # 2:4, two groups per thread: 137,000 blocks of partial sums
+    sh = S._shape(rows, cols, 2, 4, S.NM_BF16)
+    assert L.nm_monitor_workspace_bytes(ctypes.byref(sh)) > S.MONITOR_SCRATCH_BYTES
+    st = L.nm_mask_forward_monitor_static(ctypes.byref(sh), ctypes.byref(S._sample(100.0, 4.0, 1, 1)), FAKE, FAKE,
+                                          FAKE, None, None, FAKE, None)
+    assert st == S.NM_ESCRATCH
+    assert L.nm_status_str(st).decode().startswith("shape needs more scratch")
+    small = S._shape(64, 256, 2, 4, S.NM_BF16)
+    assert L.nm_mask_forward_monitor_static(ctypes.byref(small), ctypes.byref(S._sample(100.0, 4.0, 1, 1)), FAKE,
+                                            FAKE, FAKE, None, None, ODD, None) == NM_EALIGN
