@@ -64,14 +64,16 @@ __global__ __launch_bounds__(kThreads) void k_backward(BwdArgs a) {
                 aj[j] = up * wj;
             }
         }
+        // s = sum_k y_k d_k: four interleaved fma chains, added at the end, so a K-term sum
+        // rounds about K/4 + 2 times on any path instead of K (K = 70 for 4:8)
         float d[K];
-        float es = -0.0f;
+        float es[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
         candidate_sums<N, M>(aj, [&](auto kc, float dk) NM_INLINE {
             constexpr int k = decltype(kc)::value;
             d[k] = dk;
-            es = k == 0 ? e[k] * dk : fmaf(e[k], dk, es);
+            es[k & 3] = k < 4 ? e[k] * dk : fmaf(e[k], dk, es[k & 3]);
         });
-        const float s = es * inv;
+        const float s = ((es[0] + es[1]) + (es[2] + es[3])) * inv;
         const float ci = a.C * inv;
 #pragma unroll
         for (int k = 0; k < K; ++k) dl[p * K + k] = (ci * e[k]) * (d[k] - s);

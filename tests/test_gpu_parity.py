@@ -11,7 +11,7 @@ import torch
 import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
-from parity import (TOL_FP32, backward_check, candidate_sums, derived_below, forward_check, oracle_bounds,
+from parity import (TOL_FP32, backward_check, candidate_sums, forward_check, oracle_bounds,
                     soft_mask_check, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -95,7 +95,7 @@ def test_soft_mask_matches_oracle(n, m, kappa, tau):
     got = to_f64(S.nm_debug_soft_mask(Ld, n, m, kappa, tau, seed=11, offset=3))
     want = oracle.soft_mask(L, n, m, kappa, tau, 11, 3)
     _, _, dm = oracle_bounds(oracle, L, n, m, kappa, tau, 11, 3)
-    rel, bad = soft_mask_check(got, want, m, TOL_FP32, derived_below(tau, dm))
+    rel, bad = soft_mask_check(got, want, m, TOL_FP32, dm)
     _say("  worst err/bound", rel)
     assert bad == 0
     # invariants hold on the GPU too: sum to n, within [0, 1]
@@ -144,7 +144,7 @@ def test_backward_over_sample_parameters(kappa, tau):
     want = oracle.backward(w, L, G, n, m, kappa, tau, 1, 1)
     y, dy, _ = oracle_bounds(oracle, L, n, m, kappa, tau, 1, 1)
     d = candidate_sums(w.double().numpy(), G.double().numpy(), n, m, oracle.candidate_matrix(n, m))
-    rel, bad = backward_check(got, want, y, d, kappa / tau, TOL_FP32, dy=derived_below(tau, dy), n=n, m=m)
+    rel, bad = backward_check(got, want, y, d, kappa / tau, TOL_FP32, dy=dy, n=n, m=m)
     _say("  worst err/bound", rel)
     assert bad == 0
 

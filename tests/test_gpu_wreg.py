@@ -12,7 +12,7 @@ import nm_synth
 import oracle
 import semi_structured_sparsity_amd as S
 from oracle_inputs import oracle_prior
-from parity import TOL_FP32, backward_check, candidate_sums_wreg_abs, derived_below, oracle_bounds, to_f64
+from parity import TOL_FP32, backward_check, candidate_sums_wreg_abs, oracle_bounds, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -37,7 +37,6 @@ def _check(got, w, L, G, n, m, kappa, tau, seed, off, lam, tol, rows=None, row_b
     wd = w.double().numpy()
     rws, cols = wd.shape
     dd = (2.0 * abs(lam) * wd * wd * dm).reshape(rws, cols // m, m) @ cand.T
-    dy, dd = derived_below(tau, dy, dd)
     return backward_check(got, want, y, d, kappa / tau, tol, dy=dy, n=n, m=m, dd=dd)
 
 

@@ -61,15 +61,16 @@ def _emulate_backward(L, words, w, G, kappa, tau, n, m, rng):
     a = (w.astype(f32) * G.astype(f32)).astype(f32).reshape(rows, gpr, m)
     cand = oracle.candidate_matrix(n, m).astype(bool)
     d = np.zeros(L.shape, f32)
-    es = np.zeros(L.shape[:-1], f32)
+    es = [np.zeros(L.shape[:-1], f32) for _ in range(4)]  # four interleaved fma chains
     for k in range(K):
         dk = np.zeros(L.shape[:-1], f32)
         for j in range(m):
             if cand[k, j]:
                 dk = (dk + a[..., j]).astype(f32)
         d[..., k] = dk
-        es = _fma32(e[..., k], dk, es)
-    s = (es * inv[..., 0]).astype(f32)[..., None]
+        es[k % 4] = _fma32(e[..., k], dk, es[k % 4])
+    tot = ((es[0] + es[1]).astype(f32) + (es[2] + es[3]).astype(f32)).astype(f32)
+    s = (tot * inv[..., 0]).astype(f32)[..., None]
     C = f32(float(f32(kappa)) / float(f32(tau)))
     ci = (C * inv).astype(f32)
     return ((ci * e).astype(f32) * (d - s).astype(f32)).astype(f32)
