@@ -271,8 +271,9 @@ int64_t nm_packed_index_words(const nm_shape *shape);
 /* Workspace bytes nm_mask_forward_monitor needs for this shape (8 per block of its grid), or -1
  * for an invalid shape. */
 int64_t nm_monitor_workspace_bytes(const nm_shape *shape);
-/* Static description of a status code. */
-const char *nm_status_str(nm_status status);
+/* Static description of a status code; any other value gives "unknown status".  The argument
+ * is a plain int32_t so that a value outside the enumeration is well defined on both sides. */
+const char *nm_status_str(int32_t status);
 
 /* ---- diagnostic exports: the same device functions the kernels use ------------------- */
 /* Raw noise words [rows*cols/m, K] (uint32) of a sample; kappa and tau are not used. */

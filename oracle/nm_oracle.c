@@ -273,6 +273,7 @@ static int init_ctx(group_ctx *c, const ref_shape *s, double kappa, double tau, 
     c->m = s->m;
     c->K = ref_num_candidates(s->n, s->m);
     if (c->K < 0 || ref_candidate_bits(s->n, s->m, c->cand) != 0) return 0;
+    if (!(isfinite(kappa) && isfinite(tau) && tau > 0.0)) return 0; /* z = (kappa l + g) / tau */
     c->kappa = kappa;
     c->tau = tau;
     c->seed = seed;

@@ -49,7 +49,7 @@ typedef struct {
     int32_t wtype;      /* REF_F32 or REF_BF16 */
 } ref_shape;
 
-/* Return codes: 0 ok, -1 bad argument. */
+/* Return codes: 0 ok, -1 bad argument (among them a non-finite kappa or tau, or tau <= 0). */
 
 /* --- candidates ------------------------------------------------------------------------- */
 /* C(m, n), or -1 if not 1 <= n <= m <= 8. */

@@ -143,7 +143,7 @@ int64_t nm_packed_index_words(const nm_shape* s) {
     return wpr < 0 ? -1 : wpr * s->rows;
 }
 
-const char* nm_status_str(nm_status st) {
+const char* nm_status_str(int32_t st) {
     switch (st) {
     case NM_OK: return "ok";
     case NM_EINVAL: return "invalid argument";

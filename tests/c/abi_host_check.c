@@ -2,6 +2,7 @@
  * host helpers and argument validation answer without a GPU (no device work is requested:
  * every call below either is a host helper or is rejected before any HIP call).  Prints one
  * line per check and exits non-zero on the first failure. */
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -56,7 +57,53 @@ int main(void) {
     nm_shape empty = {0, 4096, 2, 4, NM_BF16};
     CHECK(nm_unpack(&empty, NULL, NULL, NULL, NULL) == NM_OK); /* nothing to do, nothing launched */
 
+    /* extreme arguments: every size check must answer without overflowing int64 (signed
+     * overflow and out-of-range float conversions are what UBSan builds of this file catch) */
+    const int64_t big = INT64_MAX - INT64_MAX % 8;
+    const nm_shape huge[] = {{big, 8, 2, 4, NM_BF16},   {1, big, 4, 8, NM_F32},        {big, big, 2, 8, NM_BF16},
+                             {1 << 20, 1LL << 40, 2, 4, NM_F32}, {INT64_MIN, 4, 2, 4, NM_BF16}, {3, -8, 1, 4, NM_F32}};
+    for (size_t i = 0; i < sizeof huge / sizeof huge[0]; ++i) {
+        CHECK(nm_packed_value_elems(&huge[i]) == -1);
+        CHECK(nm_index_words_per_row(&huge[i]) == -1);
+        CHECK(nm_packed_index_words(&huge[i]) == -1);
+        CHECK(nm_monitor_workspace_bytes(&huge[i]) == -1);
+        CHECK(nm_mask_forward(&huge[i], &smp, fake, fake, fake, NULL) == NM_EINVAL);
+        CHECK(nm_mask_backward(&huge[i], &smp, fake, fake, fake, fake, NULL) == NM_EINVAL);
+        CHECK(nm_mask_harden_pack(&huge[i], fake, fake, fake, fake, NULL, NULL) == NM_EINVAL);
+        CHECK(nm_mask_forward_monitor_static(&huge[i], &smp, fake, fake, fake, NULL, NULL, fake, NULL) == NM_EINVAL);
+    }
+    /* the largest shapes the checks accept: sizes come out exact */
+    const nm_shape widest = {1, (1LL << 31) * 256 * 4 - 1024, 2, 4, NM_BF16}; /* 2^39 - 256 groups */
+    CHECK(nm_packed_value_elems(&widest) == widest.cols / 2);
+    CHECK(nm_index_words_per_row(&widest) == widest.cols / 32);
+    CHECK(nm_monitor_workspace_bytes(&widest) > 0);
+    CHECK(nm_mask_forward_monitor_static(&widest, &smp, fake, fake, fake, NULL, NULL, fake, NULL) == NM_ESCRATCH);
+    CHECK(nm_mask_forward_monitor(&widest, &smp, fake, fake, fake, NULL, NULL, fake, fake, 64, NULL) == NM_EINVAL);
+    /* product: token counts and shapes whose grid or offsets would overflow are refused */
+    nm_shape w24 = {4096, 4096, 2, 4, NM_BF16};
+    CHECK(nm_sparse_matmul(&w24, fake, fake, fake, INT64_MAX, fake, NM_F32, NULL) == NM_EINVAL);
+    CHECK(nm_sparse_matmul(&w24, fake, fake, fake, -1, fake, NM_F32, NULL) == NM_EINVAL);
+    CHECK(nm_sparse_matmul(&w24, fake, fake, fake, 1LL << 40, fake, NM_BF16, NULL) == NM_EINVAL);
+    nm_shape w24_tall = {(1LL << 31) * 256 * 4 / 64, 64, 2, 4, NM_BF16};
+    CHECK(nm_sparse_matmul(&w24_tall, fake, fake, fake, 1LL << 45, fake, NM_F32, NULL) == NM_EINVAL);
+    nm_shape w24_odd = {4094, 4096, 2, 4, NM_BF16};
+    CHECK(nm_sparse_matmul(&w24_odd, fake, fake, fake, 8, fake, NM_F32, NULL) == NM_EUNSUPPORTED);
+    /* samples whose kappa*log2(e)/tau or 1/tau leave fp32's range, or are not numbers */
+    const nm_sample bad_samples[] = {{3.0e38f, 1.0e-3f, 0, 0}, {1.0f, 1.0e-45f, 0, 0}, {1.0f, -1.0f, 0, 0},
+                                     {-1.0f, 1.0f, 0, 0},      {INFINITY, 1.0f, 0, 0},   {NAN, 1.0f, 0, 0},
+                                     {1.0f, NAN, 0, 0}};
+    for (size_t i = 0; i < sizeof bad_samples / sizeof bad_samples[0]; ++i) {
+        CHECK(nm_mask_forward(&sh, &bad_samples[i], fake, fake, fake, NULL) == NM_EINVAL);
+        CHECK(nm_mask_backward(&sh, &bad_samples[i], fake, fake, fake, fake, NULL) == NM_EINVAL);
+    }
+    CHECK(nm_mask_backward_wreg(&sh, &smp, 3.0e38f, fake, fake, fake, fake, NULL) == NM_EINVAL); /* 2*lambda */
+    CHECK(nm_debug_copy(fake, fake, INT64_MAX - 15, NULL) == NM_EINVAL);
+    CHECK(nm_debug_gumbel_log2(fake, fake, INT64_MAX, NULL) == NM_EINVAL);
+    CHECK(nm_candidate_table(2, 4, NULL) == NM_EINVAL);
+    CHECK(nm_candidate_table(0, 4, bits) == NM_EUNSUPPORTED && nm_candidate_table(9, 8, bits) == NM_EUNSUPPORTED);
+
     CHECK(strlen(nm_status_str(NM_EALIGN)) > 0);
+    CHECK(strlen(nm_status_str(12345)) > 0 && strlen(nm_status_str(-7)) > 0);
     CHECK(strcmp(nm_status_str(NM_OK), nm_status_str(NM_EINVAL)) != 0);
 
     printf(failures ? "abi host check: %d failure(s)\n" : "abi host check: ok\n", failures);
