@@ -48,6 +48,13 @@ def normal(shape, std, seed, dtype=torch.float32, device="cpu"):
     return t.to(dtype)
 
 
+def small_integers(shape, bound, seed, dtype=torch.bfloat16, device="cpu"):
+    """Integers drawn uniformly from [-bound, bound], in `dtype` (exact in bf16 for bound <= 256):
+    inputs whose products and partial sums are exact in fp32."""
+    t = torch.randint(-bound, bound + 1, shape, generator=_gen(seed, device), device=device)
+    return t.to(dtype)
+
+
 def num_candidates(n, m):
     return len(list(itertools.combinations(range(m), n)))
 

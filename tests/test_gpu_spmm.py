@@ -177,6 +177,45 @@ def test_sparse_matmul_llama7b_decode_batches(name_index, tokens):
         assert bad == 0
 
 
+# Exact arithmetic: weights and activations are integers in [-8, 8], so every product (|.| <= 64)
+# and every fp32 partial sum (at most 5,504 kept terms here, |.| < 2^19) is exact in any order.
+# The product must then equal the oracle's binary64 result bit for bit (and its bf16 rounding,
+# round-to-nearest-even, for bf16 outputs): one dropped, repeated or misplaced kept value
+# anywhere changes an output.  The shapes take every path: the row-streaming kernel at 1-4
+# tokens (several rows per wave, rows longer than one pass, a partial last pass), the 16-row
+# kernel at 5-64 tokens and just above the streaming kernel's X limit, and the 64, 128 and 256
+# tiles with ragged edges.
+EXACT_SHAPES = [
+    (36, 64, 1), (6000, 128, 1), (520, 11008, 2), (36, 64, 3), (1000, 6144, 3), (520, 4096, 4),  # streaming
+    (8, 24640, 1), (40, 12352, 2), (40, 6208, 4), (100, 128, 7), (256, 4160, 16), (68, 192, 17),  # 16-row
+    (256, 4160, 32), (68, 192, 33), (132, 256, 64),
+    (260, 64, 100), (2052, 128, 1100), (1092, 256, 700),  # 64 x 64 tiles
+    (4100, 192, 2049), (4000, 320, 1000),  # 128 x 128
+    (6148, 128, 2600),  # 256 x 256
+]
+
+
+@pytest.mark.parametrize("out,inn,tokens", EXACT_SHAPES)
+@pytest.mark.parametrize("ytype", [torch.float32, torch.bfloat16])
+def test_sparse_matmul_exact_on_small_integers(out, inn, tokens, ytype):
+    _say("spmm exact", out, inn, tokens, ytype)
+    w = nm_synth.small_integers((out, inn), 8, 80 + out + tokens, device=DEV)
+    L = nm_synth.gaussian_logits(out, inn, 2, 4, 81 + out, device=DEV)
+    values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
+    x = nm_synth.small_integers((tokens, inn), 8, 82 + inn + tokens, device=DEV)
+    buf = torch.full((tokens * out + 4096,), float("nan"), dtype=ytype, device=DEV)
+    y = buf[:tokens * out].view(tokens, out)
+    S.nm_sparse_matmul(values, indices, x, out_dtype=ytype, out=y)
+    ref = oracle.sparse_matmul(values.cpu(), indices.cpu().numpy().view(np.uint32), x.cpu(), 2, 4)
+    assert np.all(np.abs(ref) < 2**24) and np.array_equal(ref, np.round(ref))  # exact integers
+    want = torch.from_numpy(ref).to(torch.float32).to(ytype)
+    got = y.cpu()
+    bits = (lambda t: t.view(torch.int16)) if ytype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    wrong = int((bits(got) != bits(want)).sum())
+    assert wrong == 0, f"{wrong} outputs differ from the exact product"
+    assert bool(buf[tokens * out:].isnan().all())
+
+
 def test_sparse_matmul_rejects_unsupported_shapes():
     _, values, indices = _packed_layer(256, 64, 45)
     x = torch.zeros((128, 64), dtype=torch.bfloat16, device=DEV)
