@@ -509,8 +509,8 @@ def workload_single256(args):
 
 def workload_monitor(args):
     """Forward of one LLaMA-7B-shaped layer (2:4, kappa 100, tau 4, prior logits) with the fused
-    convergence monitors, next to the plain forward: per call the monitored kernel plus its
-    one-block reduction; algorithmic bytes add the sample written and the previous sample read
+    convergence monitors, next to the plain forward: per call the one monitored kernel (its
+    matrix-wide sums taken inside the launch); algorithmic bytes add the sample written and the previous sample read
     (1 byte per group each)."""
     import torch
 
@@ -523,7 +523,7 @@ def workload_monitor(args):
         mt["prev"] = torch.zeros(g, dtype=torch.uint8, device=dev)
         mt["sample"] = torch.empty(g, dtype=torch.uint8, device=dev)
         mt["stats"] = torch.zeros(2, dtype=torch.float64, device=dev)
-        mt["ws"] = torch.empty(S.monitor_workspace_bytes(mt["rows"], mt["cols"], N, M), dtype=torch.uint8,
+        mt["ws"] = torch.zeros(S.monitor_workspace_bytes(mt["rows"], mt["cols"], N, M), dtype=torch.uint8,
                                device=dev)
     weights = nm_synth.layer_weights(nm_synth.LLAMA2_7B_LAYER)
 

@@ -112,7 +112,8 @@ nm_status nm_mask_forward(const nm_shape *shape, const nm_sample *sample, const 
  * per group g:
  *   sampled candidate  s_g = the first k with the largest (kappa*l_k + g_k)/tau for this step's
  *                      noise (the Gumbel-max hard sample; the decision is taken in fp32, so on
- *                      near-ties within the fp32 rounding of the scores either candidate may win)
+ *                      near-ties within the fp32 rounding of the scores either candidate may win;
+ *                      with non-finite logits it is unspecified)
  *   max probability    p_g = max_k softmax(kappa * l)_k (the distribution itself, no noise)
  *   L1 distance        d_g = number of positions where the masks of s_g and prev_sample[g]
  *                      differ; a prev_sample entry >= K stands for the empty mask
@@ -123,9 +124,17 @@ nm_status nm_mask_forward(const nm_shape *shape, const nm_sample *sample, const 
  *   stats        2 doubles, written: stats[0] = sum of p_g, stats[1] = sum of d_g (0 without
  *                prev_sample); divide by the group count rows*cols/m for the means.  Left
  *                untouched for an empty matrix (nothing is launched).
- *   workspace    device memory of at least nm_monitor_workspace_bytes(shape) bytes, overwritten
- *                with per-block partial sums; workspace_bytes is its size (NM_EINVAL if short).
- * The sums are added in a fixed order: repeated calls give identical stats. */
+ *   workspace    device memory of at least nm_monitor_workspace_bytes(shape) bytes, 16-byte
+ *                aligned, holding arrival counters and partial sums; it must be zero-filled
+ *                before its first use, and every call leaves it zero-filled again, so one
+ *                workspace serves any number of calls (of any shapes it is large enough for)
+ *                and any number of replays of a captured graph; workspace_bytes is its size
+ *                (NM_EINVAL if short).  Calls whose executions overlap must not share one.
+ * One kernel launch, with no fence and no waiting between blocks: the sums are integers (the
+ * p_max sum in units of 2^-F, F = 56 minus the bit length of the group count, after an fp32
+ * sum per block of 256 threads), added up a 64-ary tree over the blocks by atomic adds, so
+ * repeated calls give identical stats whatever the order in which blocks finish.  With
+ * non-finite logits stats[0] is unspecified. */
 nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample, const void *w,
                                   const float *logits, void *w_masked, const uint8_t *prev_sample,
                                   uint8_t *sample_idx, double *stats, void *workspace,
@@ -133,19 +142,21 @@ nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample
 
 /* nm_mask_forward_monitor for callers that cannot allocate device memory (code being captured
  * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
- * results, with the per-block partial sums kept in a fixed array of NM_MONITOR_SCRATCH_BYTES
- * in device memory that the library owns (one per GPU, held until the process ends) instead
- * of a caller workspace.  Nothing is allocated: the array's address is looked up once per
- * device, on the first call with that device current.
+ * results, with the counters and partial sums of the in-launch sums kept in a fixed array of
+ * NM_MONITOR_SCRATCH_BYTES in device memory that the library owns (one per GPU, held until the
+ * process ends) instead of a caller workspace.  Nothing is allocated: the array's address is
+ * looked up once per device, on the first call with that device current.  64 KiB holds the
+ * sums of up to 262,144 blocks of 256 threads: 134 million groups at 2:4 (two per thread),
+ * 67 million at the other patterns.
  *   arguments   as nm_mask_forward_monitor, without the workspace
  *   NM_ESCRATCH the shape needs more than NM_MONITOR_SCRATCH_BYTES (nm_monitor_workspace_bytes
  *               tells how much it needs), checked before any HIP call
  *   NM_EHIP     the array's address could not be looked up, or the launch failed
- * The array is shared by every call on the same GPU and keeps the last call's partial sums
- * (each call overwrites the entries it uses before reading them): calls on one GPU whose
- * executions overlap (on different streams, or from different host threads) race and must be
- * ordered by the caller.  The stream's device must be the calling thread's current device. */
-#define NM_MONITOR_SCRATCH_BYTES (1 << 20)
+ * The array starts zero-filled (a static device array) and every call leaves it so; it is
+ * shared by every call on the same GPU: calls on one GPU whose executions overlap (on
+ * different streams, or from different host threads) race and must be ordered by the caller.
+ * The stream's device must be the calling thread's current device. */
+#define NM_MONITOR_SCRATCH_BYTES (1 << 16)
 nm_status nm_mask_forward_monitor_static(const nm_shape *shape, const nm_sample *sample, const void *w,
                                          const float *logits, void *w_masked, const uint8_t *prev_sample,
                                          uint8_t *sample_idx, double *stats, void *stream);

@@ -31,7 +31,7 @@ import torch
 from . import build as _build
 
 NM_OK, NM_EINVAL, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP, NM_ESCRATCH = range(6)
-MONITOR_SCRATCH_BYTES = 1 << 20  # NM_MONITOR_SCRATCH_BYTES
+MONITOR_SCRATCH_BYTES = 1 << 16  # NM_MONITOR_SCRATCH_BYTES
 NM_F32, NM_BF16 = 0, 1
 
 _lib = None
@@ -213,7 +213,8 @@ def nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_samp
     """The forward plus the convergence monitors (MaskLLM project page, Fig. 5 caption).
     Returns (w_masked, sample uint8 [rows, cols/m], stats float64 [2] on the device) with
     stats = (sum of the largest probability of softmax(kappa*l), sum of the L1 distance between
-    this step's sampled mask and prev_sample's) over all groups."""
+    this step's sampled mask and prev_sample's) over all groups.  A `workspace` passed in must
+    have been zero-filled before its first use (every call leaves it zero-filled again)."""
     rows, cols = w.shape
     sh = _shape(rows, cols, n, m, _wtype(w.dtype))
     need = lib().nm_monitor_workspace_bytes(ctypes.byref(sh))
@@ -224,7 +225,7 @@ def nm_mask_forward_monitor(w, logits, n, m, kappa, tau, seed, offset, prev_samp
                torch.zeros(2, dtype=torch.float64, device=w.device))
     w_masked, sample, stats = out
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=w.device)  # zero before first use
     gshape = (rows, cols // m)
     st = lib().nm_mask_forward_monitor(
         ctypes.byref(sh), ctypes.byref(_sample(kappa, tau, seed, offset)), _dev(w, "w"),

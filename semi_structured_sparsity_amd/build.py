@@ -25,6 +25,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 # -Wall is left out of the default flags: it doubles the device compile time of the fully
 # unrolled kernels (4.5 instead of 2 minutes for the backward's translation unit).
+# Per-source flags: the monitored forward's tree atomics are issued by one lane, so the
+# compiler's wave-level atomic combining (which would wait for each of a block's two adds
+# alone) is turned off for that file.
+SOURCE_FLAGS = {"nm_forward.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _run(cmd):
@@ -43,7 +47,8 @@ def build(out=LIB, verbose=False):
     objs = [os.path.join(OBJ_DIR, os.path.basename(src) + ".o") for src in SOURCES]
     jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, ["hipcc", *FLAGS, "-c", "-o", o, src]) for src, o in zip(SOURCES, objs)]
+        futs = [ex.submit(_run, ["hipcc", *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", "-o", o, src])
+                for src, o in zip(SOURCES, objs)]
         noise = [l for f in futs for l in f.result()]
     tmp = out + ".tmp"
     noise += _run(["hipcc", *FLAGS, "-shared", "-o", tmp, *objs])

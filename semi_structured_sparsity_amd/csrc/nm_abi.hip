@@ -64,6 +64,21 @@ nm::NoiseKey noise_key(const nm_sample* smp) {
                         (uint32_t)(smp->offset >> 32)};
 }
 
+nm::MonitorArgs monitor_args(const nm_shape* shape, const nm_sample* sample, const void* w, const float* logits,
+                             void* w_masked, const uint8_t* prev_sample, uint8_t* sample_idx, double* stats,
+                             void* workspace, int64_t groups, float A, float B) {
+    const nm::MonitorLayout L = nm::monitor_layout(shape->n, shape->m, groups);
+    const float A0 = (float)((double)sample->kappa * 1.4426950408889634074);
+    return nm::MonitorArgs{nm::FwdArgs{w, logits, w_masked, groups, A, B, noise_key(sample)},
+                           prev_sample,
+                           sample_idx,
+                           static_cast<unsigned long long*>(workspace),
+                           ldexp(1.0, L.frac_bits),
+                           ldexp(1.0, -L.frac_bits),
+                           stats,
+                           A0};
+}
+
 nm_status launched(hipError_t e) { return e == hipSuccess ? NM_OK : NM_EHIP; }
 
 }  // namespace
@@ -183,13 +198,11 @@ nm_status nm_mask_forward_monitor_static(const nm_shape* shape, const nm_sample*
     if (groups == 0) return NM_OK;
     if (!w || !logits || !w_masked || !stats) return NM_EINVAL;
     if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked) || !aligned16(stats)) return NM_EALIGN;
-    const int64_t need = 8 * nm::monitor_parts(shape->n, shape->m, groups);
-    if (need > NM_MONITOR_SCRATCH_BYTES) return NM_ESCRATCH;
+    if (nm::monitor_layout(shape->n, shape->m, groups).bytes > NM_MONITOR_SCRATCH_BYTES) return NM_ESCRATCH;
     void* ws = nullptr;
     if ((st = scratch_on_current_device(&ws)) != NM_OK) return st;
-    const float A0 = (float)((double)sample->kappa * 1.4426950408889634074);
-    nm::MonitorArgs a{nm::FwdArgs{w, logits, w_masked, groups, A, B, noise_key(sample)},
-                      prev_sample, sample_idx, static_cast<float2*>(ws), stats, A0};
+    const nm::MonitorArgs a = monitor_args(shape, sample, w, logits, w_masked, prev_sample, sample_idx, stats, ws,
+                                           groups, A, B);
     return launched(nm::launch_forward_monitor(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
@@ -197,7 +210,7 @@ int64_t nm_monitor_workspace_bytes(const nm_shape* shape) {
     int64_t groups;
     int32_t K;
     if (check_shape(shape, &groups, &K) != NM_OK) return -1;
-    return 8 * nm::monitor_parts(shape->n, shape->m, groups);
+    return nm::monitor_layout(shape->n, shape->m, groups).bytes;
 }
 
 nm_status nm_mask_forward_offset_dev(const nm_shape* shape, const nm_sample* sample,
@@ -247,13 +260,12 @@ nm_status nm_mask_forward_monitor(const nm_shape* shape, const nm_sample* sample
     if ((st = check_sample(sample, &A, &B, &C)) != NM_OK) return st;
     if (groups == 0) return NM_OK;
     if (!w || !logits || !w_masked || !stats || !workspace) return NM_EINVAL;
-    if (workspace_bytes < 8 * nm::monitor_parts(shape->n, shape->m, groups)) return NM_EINVAL;
+    if (workspace_bytes < nm::monitor_layout(shape->n, shape->m, groups).bytes) return NM_EINVAL;
     if (!aligned16(w) || !aligned16(logits) || !aligned16(w_masked) || !aligned16(stats) ||
         !aligned16(workspace))
         return NM_EALIGN;
-    const float A0 = (float)((double)sample->kappa * 1.4426950408889634074);
-    nm::MonitorArgs a{nm::FwdArgs{w, logits, w_masked, groups, A, B, noise_key(sample)},
-                      prev_sample, sample_idx, static_cast<float2*>(workspace), stats, A0};
+    const nm::MonitorArgs a = monitor_args(shape, sample, w, logits, w_masked, prev_sample, sample_idx, stats,
+                                           workspace, groups, A, B);
     return launched(nm::launch_forward_monitor(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 

@@ -105,12 +105,69 @@ __global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
 //           softmax(kappa * l), which carries no noise;
 //   l1:     popcount(mask(sample) xor mask(prev)), a prev index >= K standing for the empty mask.
 // No thread returns early: every lane of the block takes part in the block sums of p_max and
-// l1, which go to part[blockIdx.x]; k_monitor_reduce adds the block sums in double.
+// l1 (fp32, in LDS, then across the first wave; the l1 sums are exact integers).  The sums over
+// the whole matrix are taken in the same launch, with integer arithmetic so that they do not
+// depend on the order in which blocks finish: a block's p_max sum becomes an integer count of
+// 2^-F (F chosen by the host so that the matrix total stays below 2^56), its l1 sum is an
+// integer already.  The blocks are the leaves of a 64-ary tree whose nodes are two 64-bit words
+// in the workspace, each holding (arrivals << 57) + sum; node i of a level of c nodes has parent
+// i % ceil(c / 64), so that blocks that run at the same time add to different words (children
+// of one parent, adding in a burst, measured several times slower).  A block adds
+// (1 << 57) + its sum to its parent's word with one atomic fetch-and-add; the add that brings
+// the arrivals to the parent's child count returns every other child's contribution, so that
+// block holds the parent's complete sum, sets the word back to zero and carries the sum one
+// level up; the block that completes the root writes the stat.  Every exchange is a
+// read-modify-write of a single word, whose updates all happen in one order, so no fence is
+// needed (a device-scope fence per block, which writes back and invalidates L2, measured
+// twenty times slower), and no block waits for another.  The p_max and l1 words are carried
+// independently (their roots may be completed by different blocks).
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
+}
+
+constexpr unsigned long long kTreeOne = 1ull << 57, kTreeSum = kTreeOne - 1ull;
+
+// Lane 0 of a block with the block's sums bp (p_max) and bl (l1): both as integers, carried up
+// the tree (the adds of the two words in flight together); a completed root is a stat.
+__device__ __forceinline__ void block_sums(const MonitorArgs& a, float bp, float bl) {
+    // every p_max is at most 1, so the matrix total stays below 2^56 units: a block sum that is
+    // not (a NaN) adds nothing
+    const double x = (double)bp * a.pscale;
+    unsigned long long pv = (x >= 0.0 && x < 0x1p56) ? (unsigned long long)__builtin_rint(x) : 0ull;
+    unsigned long long lv = (unsigned long long)bl;  // popcounts: an exact integer <= 4096
+    bool cp = true, cl = true;
+    uint32_t node = blockIdx.x, below = gridDim.x;
+    unsigned long long* level = a.tree;
+    while (below > 1 && (cp || cl)) {
+        const uint32_t nodes = (below + 63) / 64, parent = node % nodes;
+        const uint32_t expect = (below - parent + nodes - 1) / nodes;  // children of `parent`
+        unsigned long long* wp = level + 2 * parent;
+        unsigned long long op = 0, ol = 0;
+        if (cp) op = __hip_atomic_fetch_add(wp, kTreeOne | pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cl) ol = __hip_atomic_fetch_add(wp + 1, kTreeOne | lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cp) {
+            cp = (op >> 57) + 1 == expect;
+            if (cp) {
+                pv += op & kTreeSum;
+                __hip_atomic_store(wp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (cl) {
+            cl = (ol >> 57) + 1 == expect;
+            if (cl) {
+                lv += ol & kTreeSum;
+                __hip_atomic_store(wp + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        level += 2 * nodes;
+        node = parent;
+        below = nodes;
+    }
+    if (cp) a.stats[0] = (double)pv * a.pinv;
+    if (cl) a.stats[1] = (double)lv;
 }
 
 // Candidate bit patterns of groups of four packed as nibbles of one constant (K <= 6).
@@ -131,6 +188,24 @@ __device__ __forceinline__ uint32_t cand_bits_rt(uint32_t k, const uint8_t* lds_
         return k < (uint32_t)K ? b : 0u;
     } else {
         return k < (uint32_t)K ? (uint32_t)lds_table[k] : 0u;
+    }
+}
+
+// A thread's outputs of the monitored forward: its masked weights and sampled candidates.
+template <int N, int M, typename T>
+__device__ __forceinline__ void monitor_store(const MonitorArgs& a, int64_t g0, bool full, int nvalid,
+                                              const float (&out)[Sample<N, M>::P * M],
+                                              const uint32_t (&ksv)[Sample<N, M>::P]) {
+    constexpr int P = Sample<N, M>::P;
+    store_from_float<T, P * M>(reinterpret_cast<typename T::storage*>(a.f.out) + g0 * M, full, nvalid * M, out);
+    if (a.sample) {
+        if (P == 2 && full && ((uintptr_t)a.sample & 1u) == 0) {
+            st_store(reinterpret_cast<uint16_t*>(a.sample + g0), (uint16_t)(ksv[0] | (ksv[P - 1] << 8)));
+        } else {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                if (p < nvalid) a.sample[g0 + p] = (uint8_t)ksv[p];
+        }
     }
 }
 
@@ -158,56 +233,76 @@ __global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
         }
     }
     const bool staged = block_full<N, M>(a.f.groups);  // uniform over the block
+    // as k_forward: groups of eight generate their noise while the logit loads are in flight
+    constexpr bool EARLY = M == 8;
     float l[PK];
-    load_logits<N, M>(a.f.logits, g0, tg.q, full, nvalid, staged, tile, l);
+    StagedSpan<N, M> span;
+    logits_issue<N, M>(a.f.logits, g0, full, nvalid, staged, span, l);
+    if constexpr (!EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     float w[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.f.w) + g0 * M, full, nvalid * M, w);
-    uint32_t prev[P];  // issued with the other loads so that its latency overlaps the noise
+    // the previous samples, issued with the other loads so that their latency overlaps the
+    // noise; a thread's P bytes in one load when they are aligned (P = 2: g0 is even)
+    const bool pair = P == 2 && full && ((uintptr_t)a.prev & 1u) == 0;
+    uint32_t prev[P];
+    if (pair && a.prev) {
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(a.prev + g0);
+        prev[0] = v & 0xFFu;
+        prev[P - 1] = v >> 8;
+    } else {
 #pragma unroll
-    for (int p = 0; p < P; ++p) prev[p] = (a.prev && p < nvalid) ? a.prev[g0 + p] : 0u;
+        for (int p = 0; p < P; ++p) prev[p] = (a.prev && p < nvalid) ? a.prev[g0 + p] : 0u;
+    }
     float h[PK];
     thread_noise<N, M>(step_key(a.f.nk, a.f.offset_dev), g0, h);
+    if constexpr (EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     if constexpr (M != 4) __syncthreads();  // the candidate table is in LDS
 
     float out[P * M];
+    uint32_t ksv[P];
     float psum = 0.0f, lsum = 0.0f;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        float sc[K], e[K], sj[M];
-        group_scores<N, M>(l + p * K, h + p * K, a.f.A, a.f.B, sc);
-#pragma unroll
-        for (int k = 0; k < K; ++k) e[k] = exp2_fast(sc[k]);
-        const float inv = group_soft<N, M>(e, sj);
-#pragma unroll
-        for (int j = 0; j < M; ++j) out[p * M + j] = w[p * M + j] * (sj[j] * inv);
-
-        // sampled candidate: first maximum of the scores
-        float best = sc[0];
+        // in the order that frees registers soonest: the scores, their first maximum (the
+        // sampled candidate), the largest probability (the last use of the logits), then the
+        // exponentials of the scores (in their place) and the soft mask
+        float e[K], sj[M];
+        group_scores<N, M>(l + p * K, h + p * K, a.f.A, a.f.B, e);
+        float best = e[0];
         uint32_t ks = 0;
 #pragma unroll
         for (int k = 1; k < K; ++k) {
-            const bool up = sc[k] > best;
-            best = up ? sc[k] : best;
+            const bool up = e[k] > best;
+            best = up ? e[k] : best;
             ks = up ? (uint32_t)k : ks;
         }
-        // largest probability of softmax(kappa * l)
+        // largest probability of softmax(kappa * l): 1 / sum_k 2^(A0 (l_k - l_max)), whose
+        // largest term is exactly 1 (a fused A0 l_k - A0 l_max would not be)
         float lmax = l[p * K];
 #pragma unroll
         for (int k = 1; k < K; ++k) lmax = fmaxf(lmax, l[p * K + k]);
         float z = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) z += exp2_fast(a.A0 * (l[p * K + k] - lmax));
+#pragma unroll
+        for (int k = 0; k < K; ++k) e[k] = exp2_fast(e[k]);
+        const float inv = group_soft<N, M>(e, sj);
+#pragma unroll
+        for (int j = 0; j < M; ++j) out[p * M + j] = w[p * M + j] * (sj[j] * inv);
         const bool live = p < nvalid;
         psum += live ? __builtin_amdgcn_rcpf(z) : 0.0f;
         if (a.prev) {
             const uint32_t d = cand_bits_rt<N, M>(ks, table) ^ cand_bits_rt<N, M>(prev[p], table);
             lsum += live ? (float)__builtin_popcount(d) : 0.0f;
         }
-        if (a.sample && live) a.sample[g0 + p] = (uint8_t)ks;
+        ksv[p] = ks;
     }
-    store_from_float<T, P * M>(reinterpret_cast<typename T::storage*>(a.f.out) + g0 * M, full, nvalid * M, out);
 
-    // block sums: every thread leaves its pair in LDS, the first wave adds them up
+    // Every thread issues its stores, then leaves its sums in LDS; the first wave adds them up
+    // and lane 0 takes the block's sums up the tree.  (Measured: letting the first wave climb
+    // before its own stores, or combining the waves through LDS atomics without a barrier, or
+    // wave sums in DPP steps, was no faster.)
+    monitor_store<N, M, T>(a, g0, full, nvalid, out, ksv);
     red[threadIdx.x] = make_float2(psum, lsum);
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -220,45 +315,7 @@ __global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
         }
         b.x = wave_sum(b.x);
         b.y = wave_sum(b.y);
-        if (threadIdx.x == 0) a.part[blockIdx.x] = b;
-    }
-}
-
-// One block of 1024 threads adds the per-block sums in a fixed order (deterministic).  Each
-// thread issues U loads before it adds, so the block keeps many loads in flight.
-__global__ __launch_bounds__(1024) void k_monitor_reduce(const float2* __restrict__ part, int64_t nparts,
-                                                        double* __restrict__ stats) {
-    constexpr int U = 8;
-    double s0 = 0.0, s1 = 0.0;
-    for (int64_t base = 0; base < nparts; base += 1024 * U) {
-        float2 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + u * 1024 + threadIdx.x;
-            v[u] = i < nparts ? part[i] : make_float2(0.0f, 0.0f);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            s0 += v[u].x;
-            s1 += v[u].y;
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        s0 += __shfl_xor(s0, o);
-        s1 += __shfl_xor(s1, o);
-    }
-    __shared__ double red[2][16];
-    if ((threadIdx.x & 63) == 0) {
-        red[0][threadIdx.x >> 6] = s0;
-        red[1][threadIdx.x >> 6] = s1;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double a = 0.0, b = 0.0;
-        for (int i = 0; i < 16; ++i) { a += red[0][i]; b += red[1][i]; }
-        stats[0] = a;
-        stats[1] = b;
+        if (threadIdx.x == 0) block_sums(a, b.x, b.y);
     }
 }
 
@@ -341,19 +398,23 @@ hipError_t launch_forward_pack(int wtype, const FwdArgs& a, hipStream_t s) {
     else k_forward<2, 4, F32, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
-int64_t monitor_parts(int n, int m, int64_t groups) {
+MonitorLayout monitor_layout(int n, int m, int64_t groups) {
     const int P = groups_per_thread(n, m);
-    return ((groups + P - 1) / P + kThreads - 1) / kThreads;
+    MonitorLayout L;
+    L.blocks = ((groups + P - 1) / P + kThreads - 1) / kThreads;
+    L.words = 0;
+    for (int64_t below = L.blocks; below > 1; below = (below + 63) / 64) L.words += 2 * ((below + 63) / 64);
+    L.bytes = 8 * (L.words > 2 ? L.words : 2);
+    int bits = 0;  // bit length of the group count: the p_max total is below 2^bits
+    while (bits < 62 && (groups >> bits) != 0) ++bits;
+    L.frac_bits = 56 - bits;
+    return L;
 }
 
 template <int N, int M, typename T>
 static hipError_t monitor_nmt(const MonitorArgs& a, hipStream_t s) {
     const int64_t threads = (a.f.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
-    const unsigned blocks = grid_for(threads);
-    k_forward_monitor<N, M, T><<<blocks, kThreads, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    k_monitor_reduce<<<1, 1024, 0, s>>>(a.part, (int64_t)blocks, a.stats);
+    k_forward_monitor<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a, hipStream_t s) {

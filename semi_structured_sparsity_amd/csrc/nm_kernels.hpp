@@ -35,11 +35,23 @@ struct FwdArgs {
     const uint64_t* offset_dev;  // may be null: the offset then comes from nk
 };
 
+// Workspace of the monitored forward: a 64-ary tree over the blocks of the launch, two 64-bit
+// words (p_max sum, L1 sum) per node of every level above the blocks.  The words are zero
+// between calls: each call's last arrival at a node sets that node back to zero.
+struct MonitorLayout {
+    int64_t blocks;   // blocks of the launch (the tree's leaves)
+    int64_t words;    // words of all levels
+    int64_t bytes;    // workspace size (at least 16)
+    int frac_bits;    // F: the p_max sums are kept as integers in units of 2^-F
+};
+MonitorLayout monitor_layout(int n, int m, int64_t groups);
+
 struct MonitorArgs {
     FwdArgs f;           // the forward's arguments (f.out = w_masked)
     const uint8_t* prev; // previous step's sampled candidates, may be null
     uint8_t* sample;     // this step's sampled candidates, may be null
-    float2* part;        // per-block sums (monitor_parts entries)
+    unsigned long long* tree;  // the tree's words, level by level
+    double pscale, pinv;       // 2^F and 2^-F
     double* stats;       // [2]: sum of p_max, sum of l1
     float A0;            // kappa*log2(e)
 };
@@ -117,7 +129,6 @@ hipError_t launch_backward_wreg(int n, int m, int wtype, const BwdArgs& a, hipSt
 hipError_t launch_pack(int n, int m, int wtype, const PackArgs& a, hipStream_t s);
 hipError_t launch_unpack(int n, int m, int wtype, const UnpackArgs& a, hipStream_t s);
 hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a, hipStream_t s);
-int64_t monitor_parts(int n, int m, int64_t groups);
 hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s);
 hipError_t launch_debug_noise(const NoiseArgs& a, hipStream_t s);
 hipError_t launch_debug_copy(const void* src, void* dst, int64_t vecs, hipStream_t s);

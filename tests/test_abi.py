@@ -126,7 +126,7 @@ def test_null_and_misaligned_pointers_are_rejected_on_the_host():
     # prev_sample and sample are optional and need no alignment
     assert L.nm_mask_forward_monitor(sh, sm, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0, None) == NM_EINVAL
     need = L.nm_monitor_workspace_bytes(sh)
-    assert need == 8   # 16 groups of 2:4: one block of 256 threads
+    assert need == 16  # 16 groups of 2:4: one block, no tree above it (the minimum size)
     assert L.nm_mask_forward_monitor(sh, sm, FAKE, FAKE, FAKE, ODD, ODD, FAKE, FAKE, need - 1, None) == NM_EINVAL
     for alpha in (float("nan"), float("inf"), -float("inf")):
         assert L.nm_prior_init(sh, alpha, FAKE, FAKE, None, None) == NM_EINVAL
@@ -169,13 +169,18 @@ def test_candidate_table_and_sizes_agree_with_the_oracle(n, m):
 
 
 @pytest.mark.parametrize("n,m", SUPPORTED)
-def test_monitor_workspace_is_one_float_pair_per_block(n, m):
+def test_monitor_workspace_layout(n, m):
+    """Two 8-byte words per node of a 64-ary tree over the launch's blocks of 256 threads, at
+    least 16 bytes."""
     K = oracle.num_candidates(n, m)
     P = 1 if (K % 4 == 0 or K == 70) else (2 if K % 2 == 0 else 4)
-    for rows, cols in [(1, m), (37, 23 * m), (4096, 4096)]:
+    for rows, cols in [(1, m), (37, 23 * m), (4096, 4096), (4100, 16384), (70000, 12288)]:
         groups = rows * cols // m
-        blocks = -(-(-(-groups // P)) // 256)
-        assert S.monitor_workspace_bytes(rows, cols, n, m) == 8 * blocks
+        below, words = -(-(-(-groups // P)) // 256), 0
+        while below > 1:
+            below = -(-below // 64)
+            words += 2 * below
+        assert S.monitor_workspace_bytes(rows, cols, n, m) == 8 * max(words, 2)
 
 
 def test_sparse_matmul_is_validated_on_the_host():
@@ -268,13 +273,17 @@ def test_static_monitor_refuses_shapes_past_its_scratch_size():
     """nm_mask_forward_monitor_static checks its fixed array's size on the host, before any HIP
     call: the fake aligned pointers below are never used."""
     L = S.lib()
-    rows, cols = 70000, 4096  # 2:4, two groups per thread: 137,000 blocks of partial sums
+    rows, cols = 70000, 12288  # 2:4, two groups per thread: 420,000 blocks, a tree of 106 KB
     sh = S._shape(rows, cols, 2, 4, S.NM_BF16)
     assert L.nm_monitor_workspace_bytes(ctypes.byref(sh)) > S.MONITOR_SCRATCH_BYTES
     st = L.nm_mask_forward_monitor_static(ctypes.byref(sh), ctypes.byref(S._sample(100.0, 4.0, 1, 1)), FAKE, FAKE,
                                           FAKE, None, None, FAKE, None)
     assert st == S.NM_ESCRATCH
     assert L.nm_status_str(st).decode().startswith("shape needs more scratch")
+    # the largest layer matrices of the model families fit
+    for rows, cols, n, m in [(24576, 6144, 2, 4), (24576, 6144, 1, 4), (11008, 4096, 4, 8)]:
+        need = L.nm_monitor_workspace_bytes(ctypes.byref(S._shape(rows, cols, n, m, S.NM_BF16)))
+        assert need <= S.MONITOR_SCRATCH_BYTES
     small = S._shape(64, 256, 2, 4, S.NM_BF16)
     assert L.nm_mask_forward_monitor_static(ctypes.byref(small), ctypes.byref(S._sample(100.0, 4.0, 1, 1)), FAKE,
                                             FAKE, FAKE, None, None, ODD, None) == NM_EALIGN

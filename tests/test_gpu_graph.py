@@ -137,3 +137,36 @@ def test_training_step_graph_with_the_offset_on_the_device(wtype):
         if prev is not None:
             assert not torch.equal(_bits(out), prev), "each step samples fresh noise"
         prev = _bits(out).clone()
+
+
+@pytest.mark.parametrize("n,m,shape", [(2, 4, (4096, 4096)), (4, 8, (520, 1024)), (1, 4, (4100, 16384))])
+def test_monitored_forward_replays_as_a_graph(n, m, shape):
+    """The monitored forward in one graph node: the stats are summed inside the launch through
+    counters in the workspace, which every launch leaves at zero, so each replay sums afresh.
+    (4100 x 16384 at 1:4 is 65,600 blocks: a tree of three levels above them.)"""
+    rows, cols = shape
+    _say("graph monitor", n, m, shape)
+    w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.5, 9, with_grad=False, device=DEV)
+    g_shape = (rows, cols // m)
+    prev = torch.randint(0, S.num_candidates(n, m) + 1, g_shape, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(S.monitor_workspace_bytes(rows, cols, n, m), dtype=torch.uint8, device=DEV)
+    out = (torch.empty_like(w), torch.empty(g_shape, dtype=torch.uint8, device=DEV),
+           torch.zeros(2, dtype=torch.float64, device=DEV))
+
+    def step():
+        S.nm_mask_forward_monitor(w, L, n, m, 30.0, 0.5, 5, 8, prev_sample=prev, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in out]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert all(torch.equal(_bits(o), _bits(r)) for o, r in zip(out, refs))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    _replay_and_compare(g, list(out), refs)

@@ -103,10 +103,52 @@ def test_monitor_is_deterministic_and_outputs_are_optional():
     b = S.nm_mask_forward_monitor(wd, Ld, n, m, 4.0, 1.0, 1, 2, prev_sample=prev)
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
     # without the sample output the stats are the same
-    ws = torch.empty(S.monitor_workspace_bytes(300, 512, n, m), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(S.monitor_workspace_bytes(300, 512, n, m), dtype=torch.uint8, device=DEV)
     out = (torch.empty_like(wd), None, torch.zeros(2, dtype=torch.float64, device=DEV))
     c = S.nm_mask_forward_monitor(wd, Ld, n, m, 4.0, 1.0, 1, 2, prev_sample=prev, out=out, workspace=ws)
     assert torch.equal(c[2], a[2]) and torch.equal(c[0].view(torch.int16), a[0].view(torch.int16))
+
+
+def test_one_workspace_serves_calls_of_several_shapes():
+    """The in-launch sums leave the workspace zero-filled: one workspace, zero-filled once and
+    sized for the largest shape, serves calls of several shapes and N:M patterns in turn (three
+    rounds), and each call's samples, stats and masked weights equal those of a call with a
+    fresh workspace, bit for bit; afterwards the workspace is all zeros again."""
+    cases = [(2, 4, 1000, 4096), (4, 8, 300, 4096), (1, 4, 37, 92), (2, 8, 129, 33 * 8), (2, 4, 1, 4)]
+    need = max(S.monitor_workspace_bytes(r, c, n, m) for n, m, r, c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    runs = []
+    for i, (n, m, rows, cols) in enumerate(cases):
+        w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.5, 35 + i, with_grad=False, device=DEV)
+        prev = torch.randint(0, S.num_candidates(n, m) + 1, (rows, cols // m), dtype=torch.uint8, device=DEV)
+        runs.append((n, m, w, L, prev, S.nm_mask_forward_monitor(w, L, n, m, 30.0, 0.5, 3, 4 + i, prev_sample=prev)))
+    for rnd in range(3):
+        for i, (n, m, w, L, prev, ref) in enumerate(runs):
+            _say("monitor shared workspace", rnd, n, m, tuple(w.shape))
+            out = (torch.empty_like(w), torch.empty_like(ref[1]),
+                   torch.full((2,), float("nan"), dtype=torch.float64, device=DEV))
+            got = S.nm_mask_forward_monitor(w, L, n, m, 30.0, 0.5, 3, 4 + i, prev_sample=prev, out=out, workspace=ws)
+            assert torch.equal(got[2], ref[2]), (rnd, i, got[2].tolist(), ref[2].tolist())
+            assert torch.equal(got[1], ref[1]) and torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16))
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_monitor_sums_over_more_than_65536_blocks():
+    """1:4 at 4100 x 16384 is 16,793,600 groups, one per thread: 65,600 blocks, a tree of three
+    levels above them.  Two consecutive steps against the oracle over the whole matrix."""
+    n, m, kappa, tau, seed = 1, 4, 30.0, 0.5, 61
+    rows, cols = 4100, 16384
+    _say("monitor 65600 blocks")
+    w, L, _ = nm_synth.matrix_inputs(rows, cols, n, m, torch.bfloat16, 0.5, 38, with_grad=False, device=DEV)
+    Lc = L.cpu()
+    _, s0, st0 = S.nm_mask_forward_monitor(w, L, n, m, kappa, tau, seed, 0)
+    nd0 = _check_step(Lc, n, m, kappa, tau, seed, 0, s0, st0)
+    prev = s0.cpu().numpy()
+    _, s1, st1 = S.nm_mask_forward_monitor(w, L, n, m, kappa, tau, seed, 1, prev_sample=s0)
+    nd1 = _check_step(Lc, n, m, kappa, tau, seed, 1, s1, st1, prev)
+    _say("  near-tie differences", nd0, nd1)
+    assert nd0 + nd1 <= 1e-4 * rows * cols // m
 
 
 def test_monitor_full_llama7b_down_projection():

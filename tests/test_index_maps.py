@@ -388,3 +388,81 @@ def test_model_catches_a_read_past_the_end():
     w.add(g0 * m * wb, GT * m * wb)  # the old read: GT*M elements whatever `mine` is
     with pytest.raises(AssertionError):
         w.assert_in_bounds("old k_pack w")
+
+
+# ---------------------------------------------------------------------------------------------
+# The monitored forward's in-launch sums (k_forward_monitor and monitor_sums in nm_forward.hip;
+# workspace layout monitor_layout): blocks finish in any order; each adds (1 << 57) + its sum to
+# its parent's word of a 64-ary tree (node i of a level of c nodes under parent i % ceil(c/64))
+# with one fetch-and-add, and the add that completes a node
+# carries the node's sum one level up and sets the word back to zero.  The model replays the
+# protocol with arbitrary finishing orders (each fetch-and-add is one step, as the hardware
+# orders the updates of one word), and checks that each sum reaches the root exactly once, that
+# no word overflows into its arrival count, that every index stays inside the tree, and that
+# every word is left at zero.
+
+ONE = 1 << 57
+
+
+def monitor_layout(n, m, groups):
+    """(blocks of the launch, nodes per tree level, words, bytes, F)."""
+    P = sample_tiling(n, m)[1]
+    blocks = grid_for(-(-groups // P))
+    levels, below = [], blocks
+    while below > 1:
+        below = -(-below // 64)
+        levels.append(below)
+    words = 2 * sum(levels)
+    frac = 56 - int(groups).bit_length()
+    return blocks, levels, words, 8 * max(words, 2), frac
+
+
+def run_monitor_protocol(blocks, levels, tree, order, contrib):
+    """contrib[b] = (p, l) integer sums of block b; returns the (p, l) totals written."""
+    written = [[], []]
+    for b in order:
+        vals, carry = list(contrib[b]), [True, True]
+        node, below, base = b, blocks, 0
+        for nodes in levels:
+            parent = node % nodes
+            expect = -(-(below - parent) // nodes)
+            assert 1 <= expect <= 64
+            for q in range(2):
+                if not carry[q]:
+                    continue
+                i = base + 2 * parent + q
+                assert 0 <= i < len(tree)
+                old = tree[i]
+                tree[i] = old + (ONE | vals[q])
+                assert tree[i] < 1 << 64 and (tree[i] & (ONE - 1)) < ONE
+                carry[q] = (old >> 57) + 1 == expect
+                if carry[q]:
+                    vals[q] += old & (ONE - 1)
+                    tree[i] = 0
+            base += 2 * nodes
+            node, below = parent, nodes
+        for q in range(2):
+            if carry[q]:
+                written[q].append(vals[q])
+    return written
+
+
+@pytest.mark.parametrize("n,m,rows,cols", [(2, 4, 16, 16), (2, 4, 1000, 4096), (1, 4, 4100, 16384),
+                                           (4, 8, 11008, 4096), (2, 4, 24576, 6144), (3, 8, 37, 23 * 8)])
+def test_monitor_sums_protocol(n, m, rows, cols):
+    groups = rows * cols // m
+    blocks, levels, words, size, frac = monitor_layout(n, m, groups)
+    assert groups * 2 ** frac < 2 ** 56 and frac >= 16
+    rng = np.random.default_rng(blocks)
+    per_block = THREADS * sample_tiling(n, m)[1]
+    # the largest sums a block can hold: every p_max 1 (rounded up by 1/2), every l1 2n
+    contrib = [(g * 2 ** frac + 1, g * 2 * n) for g in
+               (min(per_block, groups - b * per_block) for b in range(blocks))]
+    assert sum(c[0] for c in contrib) < 2 ** 57
+    want = (sum(c[0] for c in contrib), sum(c[1] for c in contrib))
+    tree = [0] * words
+    for trial in range(3):  # three calls in a row on one workspace: each leaves it zero
+        order = rng.permutation(blocks) if trial != 2 else np.arange(blocks)[::-1]
+        written = run_monitor_protocol(blocks, levels, tree, order, contrib)
+        assert written == [[want[0]], [want[1]]]
+        assert not any(tree)
