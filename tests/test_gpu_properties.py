@@ -124,3 +124,34 @@ def test_monitored_forward_matches_the_oracle(n, m, p):
     st_ = stats.cpu().numpy()
     assert abs(st_[0] - float(maxp.sum())) <= TOL_FP32 * float(maxp.sum())
     assert st_[1] == l1_of(got, prev, oracle.candidate_bits(n, m))
+
+
+SPMM = st.fixed_dictionaries({
+    "out": st.integers(1, 160).map(lambda v: 4 * v),
+    "inn": st.integers(1, 48).map(lambda v: 64 * v),
+    "tokens": st.one_of(st.integers(1, 4), st.integers(5, 64), st.integers(65, 600)),
+    "bf16_out": st.booleans(),
+    "data": st.integers(0, 2**31 - 1),
+})
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(p=SPMM)
+def test_sparse_product_is_exact_on_small_integers(p):
+    """The product with the packed 2:4 weights over drawn shapes (every kernel path: 1-4, 5-64
+    and more tokens, ragged rows and tokens): with integer weights and activations in [-8, 8]
+    every product and fp32 partial sum is exact, so the result must equal the oracle's bit for
+    bit (its round-to-nearest-even bf16 value for bf16 outputs)."""
+    out, inn, tokens = p["out"], p["inn"], p["tokens"]
+    ytype = torch.bfloat16 if p["bf16_out"] else torch.float32
+    _say("props spmm", out, inn, tokens, ytype, p["data"])
+    w = nm_synth.small_integers((out, inn), 8, p["data"], device=DEV)
+    L = nm_synth.gaussian_logits(out, inn, 2, 4, p["data"] + 1, device=DEV)
+    values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
+    x = nm_synth.small_integers((tokens, inn), 8, p["data"] + 2, device=DEV)
+    y = S.nm_sparse_matmul(values, indices, x, out_dtype=ytype)
+    ref = oracle.sparse_matmul(values.cpu(), indices.cpu().numpy().view(np.uint32), x.cpu(), 2, 4)
+    want = torch.from_numpy(ref).to(torch.float32).to(ytype)
+    tb = torch.int16 if p["bf16_out"] else torch.int32
+    assert torch.equal(y.cpu().view(tb), want.view(tb))
