@@ -132,8 +132,7 @@ nm_status nm_mask_forward(const nm_shape *shape, const nm_sample *sample, const 
  *                (NM_EINVAL if short).  Calls whose executions overlap must not share one.
  * One kernel launch, with no fence and no waiting between blocks: the sums are integers (the
  * p_max sum in units of 2^-F, F = 56 minus the bit length of the group count, after an fp32
- * sum per block: 512 threads for groups of four, 256 for groups of eight), added up a 64-ary
- * tree over the blocks by atomic adds, so
+ * sum per block of 256 threads), added up a 64-ary tree over the blocks by atomic adds, so
  * repeated calls give identical stats whatever the order in which blocks finish.  With
  * non-finite logits stats[0] is unspecified. */
 nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample, const void *w,
@@ -147,8 +146,8 @@ nm_status nm_mask_forward_monitor(const nm_shape *shape, const nm_sample *sample
  * NM_MONITOR_SCRATCH_BYTES in device memory that the library owns (one per GPU, held until the
  * process ends) instead of a caller workspace.  Nothing is allocated: the array's address is
  * looked up once per device, on the first call with that device current.  64 KiB holds the
- * sums of up to 258,048 blocks: 264 million groups at 2:4 (512 threads of two groups per
- * block), 132 million at 1:4 and 3:4, 66 million for groups of eight (256 threads of one).
+ * sums of up to 262,144 blocks of 256 threads: 134 million groups at 2:4 (two per thread),
+ * 67 million at the other patterns.
  *   arguments   as nm_mask_forward_monitor, without the workspace
  *   NM_ESCRATCH the shape needs more than NM_MONITOR_SCRATCH_BYTES (nm_monitor_workspace_bytes
  *               tells how much it needs), checked before any HIP call

@@ -12,30 +12,30 @@ namespace nm {
 // page, section 3.1), with the hard mask the first argmax of the logits, as nm_mask_harden_pack.
 
 template <int N, int M, typename T, int MODE>
-__global__ __launch_bounds__(fwd_threads(M)) void k_forward(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_forward(FwdArgs a) {
     using S = Sample<N, M>;
-    constexpr int K = S::K, P = S::P, PK = S::PK, BT = fwd_threads(M);
-    const ThreadGroup<N, M> tg = thread_group<N, M, BT>();
+    constexpr int K = S::K, P = S::P, PK = S::PK;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
     const int64_t g0 = tg.g0;
     if (g0 >= a.groups) return;
     const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
     const bool full = nvalid == P;
 
-    __shared__ typename StageTile<N, M, BT>::vec tile[StageTile<N, M, BT>::VEC];
-    const bool staged = block_full<N, M, BT>(a.groups);  // uniform over the block
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
+    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
     // Groups of eight: the noise (hundreds of instructions per group) is generated while the
     // logit loads are in flight, and the logits go through LDS afterwards.
     constexpr bool EARLY = M == 8;
     float l[PK];
-    StagedSpan<N, M, BT> span;
-    logits_issue<N, M, BT>(a.logits, g0, full, nvalid, staged, span, l);
-    if constexpr (!EARLY) logits_exchange<N, M, BT>(tg.q, staged, tile, span, l);
+    StagedSpan<N, M> span;
+    logits_issue<N, M>(a.logits, g0, full, nvalid, staged, span, l);
+    if constexpr (!EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     float w[P * M];
     if constexpr (MODE != 1)
         load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
     float h[PK];
     thread_noise<N, M>(step_key(a.nk, a.offset_dev), g0, h);
-    if constexpr (EARLY) logits_exchange<N, M, BT>(tg.q, staged, tile, span, l);
+    if constexpr (EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
 
     float out[P * M];
 #pragma unroll
@@ -210,17 +210,17 @@ __device__ __forceinline__ void monitor_store(const MonitorArgs& a, int64_t g0, 
 }
 
 template <int N, int M, typename T>
-__global__ __launch_bounds__(fwd_threads(M)) void k_forward_monitor(MonitorArgs a) {
+__global__ __launch_bounds__(kThreads) void k_forward_monitor(MonitorArgs a) {
     using S = Sample<N, M>;
-    constexpr int K = S::K, P = S::P, PK = S::PK, BT = fwd_threads(M);
-    const ThreadGroup<N, M> tg = thread_group<N, M, BT>();
+    constexpr int K = S::K, P = S::P, PK = S::PK;
+    const ThreadGroup<N, M> tg = thread_group<N, M>();
     const int64_t g0 = tg.g0;
     const int64_t left = a.f.groups - g0;
     const int nvalid = left <= 0 ? 0 : (left < P ? (int)left : P);
     const bool full = nvalid == P;
 
-    __shared__ typename StageTile<N, M, BT>::vec tile[StageTile<N, M, BT>::VEC];
-    __shared__ float2 red[BT];
+    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
+    __shared__ float2 red[kThreads];
     __shared__ uint8_t table[M == 4 ? 1 : K];
     if constexpr (M != 4) {
         if (threadIdx.x < K) {
@@ -232,13 +232,13 @@ __global__ __launch_bounds__(fwd_threads(M)) void k_forward_monitor(MonitorArgs 
             table[threadIdx.x] = (uint8_t)b;
         }
     }
-    const bool staged = block_full<N, M, BT>(a.f.groups);  // uniform over the block
+    const bool staged = block_full<N, M>(a.f.groups);  // uniform over the block
     // as k_forward: groups of eight generate their noise while the logit loads are in flight
     constexpr bool EARLY = M == 8;
     float l[PK];
-    StagedSpan<N, M, BT> span;
-    logits_issue<N, M, BT>(a.f.logits, g0, full, nvalid, staged, span, l);
-    if constexpr (!EARLY) logits_exchange<N, M, BT>(tg.q, staged, tile, span, l);
+    StagedSpan<N, M> span;
+    logits_issue<N, M>(a.f.logits, g0, full, nvalid, staged, span, l);
+    if constexpr (!EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     float w[P * M];
     load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.f.w) + g0 * M, full, nvalid * M, w);
     // the previous samples, issued with the other loads so that their latency overlaps the
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(fwd_threads(M)) void k_forward_monitor(MonitorArgs 
     }
     float h[PK];
     thread_noise<N, M>(step_key(a.f.nk, a.f.offset_dev), g0, h);
-    if constexpr (EARLY) logits_exchange<N, M, BT>(tg.q, staged, tile, span, l);
+    if constexpr (EARLY) logits_exchange<N, M>(tg.q, staged, tile, span, l);
     if constexpr (M != 4) __syncthreads();  // the candidate table is in LDS
 
     float out[P * M];
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(fwd_threads(M)) void k_forward_monitor(MonitorArgs 
     if (threadIdx.x < 64) {
         float2 b = red[threadIdx.x];
 #pragma unroll
-        for (int i = 1; i < BT / 64; ++i) {
+        for (int i = 1; i < kThreads / 64; ++i) {
             const float2 v = red[threadIdx.x + 64 * i];
             b.x += v.x;
             b.y += v.y;
@@ -385,9 +385,8 @@ __global__ __launch_bounds__(kThreads) void k_prior(PriorArgs a) {
 template <int N, int M, typename T>
 static hipError_t fwd_nmt(const FwdArgs& a, bool soft, hipStream_t s) {
     const int64_t threads = (a.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
-    constexpr int BT = fwd_threads(M);
-    if (soft) k_forward<N, M, T, 1><<<grid_for(threads, BT), BT, 0, s>>>(a);
-    else k_forward<N, M, T, 0><<<grid_for(threads, BT), BT, 0, s>>>(a);
+    if (soft) k_forward<N, M, T, 1><<<grid_for(threads), kThreads, 0, s>>>(a);
+    else k_forward<N, M, T, 0><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft, hipStream_t s) {
@@ -395,16 +394,14 @@ hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft, 
 }
 hipError_t launch_forward_pack(int wtype, const FwdArgs& a, hipStream_t s) {
     const int64_t threads = (a.groups + Sample<2, 4>::P - 1) / Sample<2, 4>::P;
-    constexpr int BT = fwd_threads(4);
-    if (wtype == 1) k_forward<2, 4, BF16, 2><<<grid_for(threads, BT), BT, 0, s>>>(a);
-    else k_forward<2, 4, F32, 2><<<grid_for(threads, BT), BT, 0, s>>>(a);
+    if (wtype == 1) k_forward<2, 4, BF16, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
+    else k_forward<2, 4, F32, 2><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 MonitorLayout monitor_layout(int n, int m, int64_t groups) {
     const int P = groups_per_thread(n, m);
     MonitorLayout L;
-    const int64_t bt = fwd_threads(m);  // the monitored forward's grid
-    L.blocks = ((groups + P - 1) / P + bt - 1) / bt;
+    L.blocks = ((groups + P - 1) / P + kThreads - 1) / kThreads;
     L.words = 0;
     for (int64_t below = L.blocks; below > 1; below = (below + 63) / 64) L.words += 2 * ((below + 63) / 64);
     L.bytes = 8 * (L.words > 2 ? L.words : 2);
@@ -417,8 +414,7 @@ MonitorLayout monitor_layout(int n, int m, int64_t groups) {
 template <int N, int M, typename T>
 static hipError_t monitor_nmt(const MonitorArgs& a, hipStream_t s) {
     const int64_t threads = (a.f.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
-    constexpr int BT = fwd_threads(M);
-    k_forward_monitor<N, M, T><<<grid_for(threads, BT), BT, 0, s>>>(a);
+    k_forward_monitor<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a, hipStream_t s) {

@@ -14,15 +14,6 @@ namespace nm {
 
 constexpr int kThreads = 256;
 
-// Threads per block of the forward of groups of four (plain, fused with the pack, and monitored)
-// and of the 2:4 / 1:4 byte pack and 2:4 byte unpack: 512.  With twice the threads behind each
-// barrier a block moves twice the contiguous span of logits, weights and outputs in step.
-// Measured on the LLaMA-7B-shaped layer (2:4, bf16): the forward 4% faster than with 256
-// threads, the byte pack and unpack 1-2%; the backward (three barriers per block), the flat copy
-// and the groups-of-eight kernels were slower at 512, and every kernel was slower at 1024.
-constexpr int kThreadsWide = 512;
-constexpr int fwd_threads(int m) { return m == 4 ? kThreadsWide : kThreads; }
-
 // ------------------------------------------------------------------------------------------
 // Loads of logits / stores of logit gradients: CNT floats, 16- or 8-byte vectors.
 
@@ -91,7 +82,7 @@ struct Sample {
     static constexpr int LALIGN = (PK * 4) % 16 == 0 ? 16 : 8; // byte alignment of a thread's logits
     // Stage a block's logits (and logit gradients) through LDS when a thread's share is more than
     // one vector: then neighbouring lanes are more than a vector apart and direct accesses leave
-    // partly used cache lines in every instruction.  Tile: block threads * PK floats (<= 70 KB).
+    // partly used cache lines in every instruction.  Tile: kThreads * PK floats (<= 70 KB).
     static constexpr bool STAGE = PK * 4 > LALIGN;
 };
 
@@ -107,16 +98,16 @@ struct ThreadGroup {
     int64_t g0;  // first group
     int q;       // index of the thread's P-group tile within the block (for LDS staging)
 };
-template <int N, int M, int BT = kThreads>
+template <int N, int M>
 __device__ __forceinline__ ThreadGroup<N, M> thread_group() {
     using S = Sample<N, M>;
     const int tid = threadIdx.x;
     int q = tid;
     if constexpr (S::PH != 0) {
-        static_assert(S::P == 1 && BT == 256, "four waves, one group per thread");
+        static_assert(S::P == 1 && kThreads == 256, "four waves, one group per thread");
         q = 2 * ((tid & 63) + 64 * ((tid >> 6) & 1)) + (tid >> 7);
     }
-    return ThreadGroup<N, M>{((int64_t)blockIdx.x * BT + q) * S::P, q};
+    return ThreadGroup<N, M>{((int64_t)blockIdx.x * kThreads + q) * S::P, q};
 }
 
 // h[i] for slots i = 0 .. PK-1 when slot 0 is word SH of Philox block b0: each block is turned
@@ -278,26 +269,26 @@ __device__ __forceinline__ void candidate_sums(const float (&aj)[M], F&& use) {
 // one contiguous span with every lane on consecutive 16-byte vectors, and exchanged through an
 // LDS tile.  Partial blocks (the last one) use direct accesses.
 
-template <int N, int M, int BT = kThreads>
+template <int N, int M>
 struct StageTile {
     using S = Sample<N, M>;
     using vec = float4;                                    // LDS element: the span moves in 16-byte vectors
-    static constexpr int G16 = BT * S::PK / 4;             // 16-byte vectors of a block's span
-    static constexpr int ROUNDS = (G16 + BT - 1) / BT;     // per thread (the last guarded)
-    static constexpr bool EVEN = G16 % BT == 0;
+    static constexpr int G16 = kThreads * S::PK / 4;       // 16-byte vectors of a block's span
+    static constexpr int ROUNDS = (G16 + kThreads - 1) / kThreads;  // per thread (the last guarded)
+    static constexpr bool EVEN = G16 % kThreads == 0;
     static constexpr int VEC = S::STAGE ? G16 : 1;         // vectors per tile
-    static_assert(BT * S::PK % 4 == 0, "a block's span is whole 16-byte vectors");
+    static_assert(kThreads * S::PK % 4 == 0, "a block's span is whole 16-byte vectors");
 };
 
 // The HBM side of a staged span, held in registers between the loads and the LDS exchange.
-template <int N, int M, int BT = kThreads>
+template <int N, int M>
 struct StagedSpan {
-    uint4 v[StageTile<N, M, BT>::ROUNDS];
+    uint4 v[StageTile<N, M>::ROUNDS];
 };
 
-template <int N, int M, int BT = kThreads>
+template <int N, int M>
 __device__ __forceinline__ bool block_full(int64_t groups) {
-    return ((int64_t)blockIdx.x + 1) * BT * Sample<N, M>::P <= groups;
+    return ((int64_t)blockIdx.x + 1) * kThreads * Sample<N, M>::P <= groups;
 }
 
 template <typename V>
@@ -316,17 +307,17 @@ __device__ __forceinline__ V floats_to_vec(const float* in) {
 // consecutive lanes on consecutive vectors; a thread of an unstaged block loads its own logits
 // directly into l.  logits_exchange: the staged span goes through the LDS tile, and each thread
 // reads its PK floats at float offset q * PK (q: its place in the block, thread_group).
-template <int N, int M, int BT = kThreads>
+template <int N, int M>
 __device__ __forceinline__ void logits_issue(const float* logits, int64_t g0, bool full, int nvalid, bool staged,
-                                             StagedSpan<N, M, BT>& st, float (&l)[Sample<N, M>::PK]) {
+                                             StagedSpan<N, M>& st, float (&l)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
-    using ST = StageTile<N, M, BT>;
+    using ST = StageTile<N, M>;
     if constexpr (S::STAGE) {
         if (staged) {
-            const uint4* src = reinterpret_cast<const uint4*>(logits + (int64_t)blockIdx.x * BT * S::PK);
+            const uint4* src = reinterpret_cast<const uint4*>(logits + (int64_t)blockIdx.x * kThreads * S::PK);
 #pragma unroll
             for (int r = 0; r < ST::ROUNDS; ++r) {
-                const int i = threadIdx.x + r * BT;
+                const int i = threadIdx.x + r * kThreads;
                 if (ST::EVEN || r + 1 < ST::ROUNDS || i < ST::G16) st.v[r] = nt_load4(src + i);
             }
             return;
@@ -335,16 +326,16 @@ __device__ __forceinline__ void logits_issue(const float* logits, int64_t g0, bo
     load_f32<S::PK, S::LALIGN>(logits + g0 * S::K, full, nvalid * S::K, l);
 }
 
-template <int N, int M, int BT = kThreads>
-__device__ __forceinline__ void logits_exchange(int q, bool staged, float4* tile, const StagedSpan<N, M, BT>& st,
+template <int N, int M>
+__device__ __forceinline__ void logits_exchange(int q, bool staged, float4* tile, const StagedSpan<N, M>& st,
                                                 float (&l)[Sample<N, M>::PK]) {
     using S = Sample<N, M>;
-    using ST = StageTile<N, M, BT>;
+    using ST = StageTile<N, M>;
     if constexpr (S::STAGE) {
         if (staged) {
 #pragma unroll
             for (int r = 0; r < ST::ROUNDS; ++r) {
-                const int i = threadIdx.x + r * BT;
+                const int i = threadIdx.x + r * kThreads;
                 if (ST::EVEN || r + 1 < ST::ROUNDS || i < ST::G16)
                     tile[i] = make_float4(__uint_as_float(st.v[r].x), __uint_as_float(st.v[r].y),
                                           __uint_as_float(st.v[r].z), __uint_as_float(st.v[r].w));
@@ -611,7 +602,7 @@ __device__ __forceinline__ void put16(uint32_t& w0, uint32_t& w1, uint32_t p, ui
 // ------------------------------------------------------------------------------------------
 // Launch helpers.  Grids are flat, one tile per thread; the host has checked that every count fits.
 
-static inline unsigned grid_for(int64_t threads, int bt = kThreads) { return (unsigned)((threads + bt - 1) / bt); }
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + kThreads - 1) / kThreads); }
 
 // (n, m, wtype) -> template instance.  The caller has validated the triple.
 #define NM_DISPATCH(FN, n, m, wt, ...)                                            \

@@ -262,10 +262,10 @@ struct ByteTiling {
     static_assert(N == 1 || N == 2, "one index byte holds whole groups");
 };
 
-// The logits of a full block's THREADS threads form one contiguous span of THREADS * CNT
-// floats: it is read with consecutive lanes on consecutive 16-byte vectors (non-temporally: each
-// is read once) and handed to the threads through an LDS tile.
-template <int CNT, int THREADS>
+// The logits of a full block's threads form one contiguous span of kThreads * CNT floats: it is
+// read with consecutive lanes on consecutive 16-byte vectors (non-temporally: each is read
+// once) and handed to the threads through an LDS tile.
+template <int CNT>
 __device__ __forceinline__ void load_block_logits(const float* __restrict__ block_base, float4* tile,
                                                   float (&l)[CNT]) {
     static_assert(CNT % 4 == 0, "whole float4 vectors per thread");
@@ -273,8 +273,8 @@ __device__ __forceinline__ void load_block_logits(const float* __restrict__ bloc
     const float4* src = reinterpret_cast<const float4*>(block_base);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const uint4 u = nt_load4(src + threadIdx.x + i * THREADS);
-        tile[threadIdx.x + i * THREADS] =
+        const uint4 u = nt_load4(src + threadIdx.x + i * kThreads);
+        tile[threadIdx.x + i * kThreads] =
             make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
     __syncthreads();
@@ -283,17 +283,17 @@ __device__ __forceinline__ void load_block_logits(const float* __restrict__ bloc
 }
 
 template <int N, typename T>
-__global__ __launch_bounds__(kThreadsWide) void k_pack_bytes(PackArgs a) {
+__global__ __launch_bounds__(kThreads) void k_pack_bytes(PackArgs a) {
     using BT = ByteTiling<N, T>;
-    constexpr int M = 4, K = BT::K, U = BT::U, TH = kThreadsWide;
-    __shared__ float4 tile[TH * U * K / 4];
+    constexpr int M = 4, K = BT::K, U = BT::U;
+    __shared__ float4 tile[kThreads * U * K / 4];
     const int64_t groups = a.rows * a.gpr;
-    const int64_t t = (int64_t)blockIdx.x * TH + threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g0 = t * U;
-    const bool staged = ((int64_t)blockIdx.x + 1) * TH * U <= groups;  // uniform: a full block
+    const bool staged = ((int64_t)blockIdx.x + 1) * kThreads * U <= groups;  // uniform: a full block
     if (g0 >= groups) return;  // only in the last block, which is not staged
     float l[U * K];
-    if (staged) load_block_logits<U * K, TH>(a.logits + (int64_t)blockIdx.x * TH * U * K, tile, l);
+    if (staged) load_block_logits<U * K>(a.logits + (int64_t)blockIdx.x * kThreads * U * K, tile, l);
     else load_logit_unit<U * K>(a.logits + g0 * K, true, U * K, l);
     uint32_t raw[U * M];
     load_raw<T, U * M, U * M * T::bytes == 16>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, true,
@@ -339,10 +339,10 @@ __global__ __launch_bounds__(kThreadsWide) void k_pack_bytes(PackArgs a) {
 }
 
 template <int N, typename T>
-__global__ __launch_bounds__(kThreadsWide) void k_unpack_bytes(UnpackArgs a) {
+__global__ __launch_bounds__(kThreads) void k_unpack_bytes(UnpackArgs a) {
     using BT = ByteTiling<N, T>;
     constexpr int M = 4, U = BT::U;
-    const int64_t t = (int64_t)blockIdx.x * kThreadsWide + threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t g0 = t * U;
     if (g0 >= a.rows * a.gpr) return;
     const uint32_t byte = reinterpret_cast<const uint8_t*>(a.indices)[t];
@@ -464,7 +464,7 @@ template <int N, int M, typename T>
 static hipError_t pack_nmt(PackArgs a, hipStream_t s) {
     if constexpr (M == 4 && (N == 1 || N == 2)) {
         if (byte_path<N, M>(a.gpr)) {
-            k_pack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U, kThreadsWide), kThreadsWide, 0, s>>>(a);
+            k_pack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
             return hipGetLastError();
         }
     }
@@ -488,7 +488,7 @@ static hipError_t unpack_nmt(UnpackArgs a, hipStream_t s) {
     }
     if constexpr (M == 4 && N == 2) {
         if (byte_path<N, M>(a.gpr)) {
-            k_unpack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U, kThreadsWide), kThreadsWide, 0, s>>>(a);
+            k_unpack_bytes<N, T><<<grid_for(a.rows * a.gpr / ByteTiling<N, T>::U), kThreads, 0, s>>>(a);
             return hipGetLastError();
         }
     }

@@ -170,14 +170,13 @@ def test_candidate_table_and_sizes_agree_with_the_oracle(n, m):
 
 @pytest.mark.parametrize("n,m", SUPPORTED)
 def test_monitor_workspace_layout(n, m):
-    """Two 8-byte words per node of a 64-ary tree over the launch's blocks (512 threads for
-    groups of four, 256 for groups of eight), at least 16 bytes."""
+    """Two 8-byte words per node of a 64-ary tree over the launch's blocks of 256 threads, at
+    least 16 bytes."""
     K = oracle.num_candidates(n, m)
     P = 1 if (K % 4 == 0 or K == 70) else (2 if K % 2 == 0 else 4)
-    bt = 512 if m == 4 else 256
-    for rows, cols in [(1, m), (37, 23 * m), (4096, 4096), (4100, 16384), (70000, 12288), (140000, 12288)]:
+    for rows, cols in [(1, m), (37, 23 * m), (4096, 4096), (4100, 16384), (70000, 12288)]:
         groups = rows * cols // m
-        below, words = -(-(-(-groups // P)) // bt), 0
+        below, words = -(-(-(-groups // P)) // 256), 0
         while below > 1:
             below = -(-below // 64)
             words += 2 * below
@@ -274,7 +273,7 @@ def test_static_monitor_refuses_shapes_past_its_scratch_size():
     """nm_mask_forward_monitor_static checks its fixed array's size on the host, before any HIP
     call: the fake aligned pointers below are never used."""
     L = S.lib()
-    rows, cols = 140000, 12288  # 2:4, two groups per thread, 512 per block: 420,000 blocks, a tree of 106 KB
+    rows, cols = 70000, 12288  # 2:4, two groups per thread: 420,000 blocks, a tree of 106 KB
     sh = S._shape(rows, cols, 2, 4, S.NM_BF16)
     assert L.nm_monitor_workspace_bytes(ctypes.byref(sh)) > S.MONITOR_SCRATCH_BYTES
     st = L.nm_mask_forward_monitor_static(ctypes.byref(sh), ctypes.byref(S._sample(100.0, 4.0, 1, 1)), FAKE, FAKE,

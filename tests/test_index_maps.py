@@ -15,8 +15,7 @@ import math
 import numpy as np
 import pytest
 
-THREADS = 256  # threads per block (kThreads)
-WIDE = 512     # kThreadsWide: the forward of groups of four and the 2:4 / 1:4 byte kernels
+THREADS = 256
 SUPPORTED = [(n, 4) for n in (1, 2, 3)] + [(n, 8) for n in range(1, 8)]
 
 
@@ -28,13 +27,8 @@ def bits_of(m):
     return (m - 1).bit_length()
 
 
-def grid_for(threads, bt=THREADS):
-    return (threads + bt - 1) // bt
-
-
-def fwd_threads(m):
-    """Threads per block of the forward kernels (fwd_threads in nm_layer.hpp)."""
-    return WIDE if m == 4 else THREADS
+def grid_for(threads):
+    return (threads + THREADS - 1) // THREADS
 
 
 class Buf:
@@ -120,14 +114,14 @@ def model_pack_bytes(b, rows, cols, n, wb):
     gpr = cols // m
     groups = rows * gpr
     U = 8 // (2 * n)
-    t = np.arange(grid_for(groups // U, WIDE) * WIDE, dtype=np.int64)
+    t = np.arange(grid_for(groups // U) * THREADS, dtype=np.int64)
     g0 = t * U
     t, g0 = t[g0 < groups], g0[g0 < groups]
-    blk, tid = t // WIDE, t % WIDE
-    staged = (blk + 1) * WIDE * U <= groups
+    blk, tid = t // THREADS, t % THREADS
+    staged = (blk + 1) * THREADS * U <= groups
     per = U * K // 4
     for i in range(per):  # a staged block's logits: consecutive lanes on consecutive float4
-        b["logits"].add((blk[staged] * WIDE * U * K) * 4 + (tid[staged] + i * WIDE) * 16, 16)
+        b["logits"].add((blk[staged] * THREADS * U * K) * 4 + (tid[staged] + i * THREADS) * 16, 16)
     b["logits"].add(g0[~staged] * K * 4, U * K * 4)
     b["w"].add(g0 * m * wb, U * m * wb)
     b["values"].add(g0 * n * wb, U * n * wb)
@@ -138,7 +132,7 @@ def model_pack_bytes(b, rows, cols, n, wb):
 def model_unpack_bytes(b, rows, cols, wb):
     n, m, U = 2, 4, 2
     groups = rows * (cols // m)
-    t = np.arange(grid_for(groups // U, WIDE) * WIDE, dtype=np.int64)
+    t = np.arange(grid_for(groups // U) * THREADS, dtype=np.int64)
     g0 = t * U
     t, g0 = t[g0 < groups], g0[g0 < groups]
     b["indices"].add(t, 1)
@@ -167,14 +161,13 @@ def sample_tiling(n, m):
     return K, P, PK, lalign, PK * 4 > lalign
 
 
-def add_logit_span(buf, n, m, groups, blk, tid, g0, nvalid, bt=THREADS):
-    """Logit (or logit-gradient) accesses of the sampling kernels with blocks of bt threads: a
-    staged block moves its span as consecutive vectors, other threads access their own nvalid
-    groups directly."""
+def add_logit_span(buf, n, m, groups, blk, tid, g0, nvalid):
+    """Logit (or logit-gradient) accesses of the sampling kernels: a staged block moves its span
+    as consecutive vectors, other threads access their own nvalid groups directly."""
     K, P, PK, lalign, stage = sample_tiling(n, m)
-    staged = ((blk + 1) * bt * P <= groups) if stage else np.zeros(blk.shape, bool)
+    staged = ((blk + 1) * THREADS * P <= groups) if stage else np.zeros(blk.shape, bool)
     for i in range(PK * 4 // lalign):
-        buf.add(blk[staged] * bt * PK * 4 + (tid[staged] + i * bt) * lalign, lalign)
+        buf.add(blk[staged] * THREADS * PK * 4 + (tid[staged] + i * THREADS) * lalign, lalign)
     buf.add(g0[~staged] * K * 4, nvalid[~staged] * K * 4)
 
 
@@ -286,40 +279,30 @@ def thread_slot(tid, n, m):
     return 2 * ((tid & 63) + 64 * ((tid >> 6) & 1)) + (tid >> 7)
 
 
-def sampling_threads(n, m, groups, bt):
-    """(block, place in the block's tile, first group, groups owned) of every live thread of a
-    sampling kernel launched with blocks of bt threads."""
-    K, P, PK, lalign, stage = sample_tiling(n, m)
-    t = np.arange(grid_for((groups + P - 1) // P, bt) * bt, dtype=np.int64)
-    blk, tid = t // bt, t % bt
-    q = thread_slot(tid, n, m)
-    g0 = (blk * bt + q) * P
-    live = g0 < groups
-    blk, q, g0 = blk[live], q[live], g0[live]
-    if (P * K) % 4 != 0:  # every wave's groups share a parity, so the noise phase is wave-uniform
-        assert bt == 256
-        wave = (blk * bt + t[live] % bt) // 64
-        par = g0 % 2
-        assert all(len(set(par[wave == wv])) == 1 for wv in np.unique(wave)[:512])
-    return blk, q, g0, np.minimum(groups - g0, P)
-
-
 def model_forward_backward(rows, cols, n, m, wb):
     gpr = cols // m
     groups = rows * gpr
-    K = sample_tiling(n, m)[0]
+    K, P, PK, lalign, stage = sample_tiling(n, m)
+    t = np.arange(grid_for((groups + P - 1) // P) * THREADS, dtype=np.int64)
+    blk, tid = t // THREADS, t % THREADS
+    q = thread_slot(tid, n, m)
+    g0 = (blk * THREADS + q) * P
+    live = g0 < groups
+    blk, tid, g0 = blk[live], q[live], g0[live]
+    if (P * K) % 4 != 0:  # every wave's groups share a parity, so the noise phase is wave-uniform
+        wave = (blk * THREADS + t[live] % THREADS) // 64
+        par = g0 % 2
+        assert all(len(set(par[wave == wv])) == 1 for wv in np.unique(wave)[:512])
+    nvalid = np.minimum(groups - g0, P)
     fwd = dict(w=Buf(rows * cols * wb), logits=Buf(groups * K * 4), out=Buf(rows * cols * wb))
     bwd = dict(w=Buf(rows * cols * wb), grad=Buf(rows * cols * wb), logits=Buf(groups * K * 4),
                dlogits=Buf(groups * K * 4))
-    for d, bt in ((fwd, fwd_threads(m)), (bwd, THREADS)):
-        blk, tid, g0, nvalid = sampling_threads(n, m, groups, bt)
-        add_logit_span(d["logits"], n, m, groups, blk, tid, g0, nvalid, bt)
+    for d in (fwd, bwd):
+        add_logit_span(d["logits"], n, m, groups, blk, tid, g0, nvalid)
         d["w"].add(g0 * m * wb, nvalid * m * wb)
-        if d is fwd:
-            fwd["out"].add(g0 * m * wb, nvalid * m * wb)
-        else:
-            bwd["grad"].add(g0 * m * wb, nvalid * m * wb)
-            add_logit_span(bwd["dlogits"], n, m, groups, blk, tid, g0, nvalid, bt)
+    fwd["out"].add(g0 * m * wb, nvalid * m * wb)
+    bwd["grad"].add(g0 * m * wb, nvalid * m * wb)
+    add_logit_span(bwd["dlogits"], n, m, groups, blk, tid, g0, nvalid)
     return fwd, bwd
 
 
@@ -424,7 +407,7 @@ ONE = 1 << 57
 def monitor_layout(n, m, groups):
     """(blocks of the launch, nodes per tree level, words, bytes, F)."""
     P = sample_tiling(n, m)[1]
-    blocks = grid_for(-(-groups // P), fwd_threads(m))
+    blocks = grid_for(-(-groups // P))
     levels, below = [], blocks
     while below > 1:
         below = -(-below // 64)
@@ -471,7 +454,7 @@ def test_monitor_sums_protocol(n, m, rows, cols):
     blocks, levels, words, size, frac = monitor_layout(n, m, groups)
     assert groups * 2 ** frac < 2 ** 56 and frac >= 16
     rng = np.random.default_rng(blocks)
-    per_block = fwd_threads(m) * sample_tiling(n, m)[1]
+    per_block = THREADS * sample_tiling(n, m)[1]
     # the largest sums a block can hold: every p_max 1 (rounded up by 1/2), every l1 2n
     contrib = [(g * 2 ** frac + 1, g * 2 * n) for g in
                (min(per_block, groups - b * per_block) for b in range(blocks))]
