@@ -251,9 +251,10 @@ def test_config3_annealed_sweep_sampled(layer, step):
 
 def test_config4_nemotron15b_every_matrix_round_trip():
     """Every matrix of the Nemotron-shaped model: the hard mask is the first argmax of the
-    logits, and unpack(pack) keeps exactly the selected weights with +0.0 elsewhere, from
-    poisoned outputs; the oracle checks the first and last rows of a square and a rectangular
-    matrix per layer."""
+    logits (torch.argmax, which returns the first maximal index), and unpack(pack) keeps exactly
+    the selected weights with +0.0 elsewhere, from poisoned outputs; the oracle checks the packed
+    values, index words and hard indices of 16 rows of every matrix (the first, the last and 14
+    drawn from a generator seeded by the layer and matrix)."""
     global _PREV_POINTERS
     n, m = 2, 4
     total = 0
@@ -290,11 +291,12 @@ def test_config4_nemotron15b_every_matrix_round_trip():
                                                             ("dense", dense))}
             assert hard_ok and trip_ok
             assert int(keep.view(-1, m).sum(1).min()) == n == int(keep.view(-1, m).sum(1).max())
-            if i in (0, 4):  # the oracle on sampled rows of a square and a rectangular matrix
-                for r in (0, rows - 1):
-                    rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
-                    assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri)
-                    assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16))
+            drawn = np.random.default_rng(seed).choice(np.arange(1, rows - 1), 14, replace=False)
+            for r in [0, rows - 1, *sorted(int(x) for x in drawn)]:  # rows are independent
+                rv, ri, rh = oracle.pack(w[r:r + 1].cpu(), L[r:r + 1].cpu(), n, m)
+                assert np.array_equal(indices[r:r + 1].cpu().numpy().view(np.uint32), ri), f"{name} row {r}"
+                assert np.array_equal(_bits(values[r:r + 1]).cpu().numpy(), rv.view(np.int16)), f"{name} row {r}"
+                assert np.array_equal(hard[r:r + 1].cpu().numpy(), rh), f"{name} row {r}"
             total += rows * cols
             del w, L, values, indices, hard, dense, keep, want
         if layer % 8 == 7:
