@@ -8,8 +8,9 @@ Inputs are synthetic, seeded, generated on the GPU and resident in HBM before ti
 
 Prints one JSON line.  `value` is the metric: masked weights per second of the forward and
 backward passes, timed with HIP events inside each of the K whole-path steps (ms_per_step is the
-whole step).  Alongside: the per-pass breakdown, the roofline of the dominant kernel (HIP-event
-timing, algorithmic bytes), the 32-layer annealed sweep (32 such layers x 10 steps of forward,
+whole step).  Alongside: the per-pass breakdown (each pass timed on its own, and each pass's
+share of the timed steps), the roofline of the dominant kernel (HIP-event timing, algorithmic
+bytes), the 32-layer annealed sweep (32 such layers x 10 steps of forward,
 backward and harden/pack, tau 4 -> 0.05, kappa 100 -> 500), and the oracle's CPU baseline on a
 bounded sample on every host core available.
 
@@ -111,15 +112,16 @@ PASSES = ("fwd", "bwd", "harden_pack", "unpack")
 def step_all(S, mats, step, marks=None):
     # pass-major, as in a training step (all forwards, then all backwards, ...): each pass moves
     # >= 2 GB across the seven matrices, so no pass finds a matrix's data left in the 256 MB
-    # last-level cache by the previous pass over the same matrix.  `marks`: a pair of events
-    # recorded on the launch stream before the forward pass and after the backward pass.
-    for p in PASSES:
-        if marks is not None and p == "fwd":
-            marks[0].record()
+    # last-level cache by the previous pass over the same matrix.  `marks`: len(PASSES) + 1
+    # events recorded on the launch stream at the pass boundaries (before the forward, after
+    # each pass).
+    if marks is not None:
+        marks[0].record()
+    for i, p in enumerate(PASSES):
         for mt in mats:
             run_pass(S, mt, p, step)
-        if marks is not None and p == "bwd":
-            marks[1].record()
+        if marks is not None:
+            marks[i + 1].record()
 
 
 def host_cores():
@@ -781,7 +783,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PASSES) + 1)] for _ in range(args.steps)]
     e0.record()
     for s in range(args.steps):
         step_all(S, mats, args.warmup + s, marks[s])
@@ -792,7 +794,11 @@ def main():
     step_ms_wall = wall * 1e3 / args.steps
     ms_per_step = max(step_ms, step_ms_wall)
     # the metric: forward + backward of every matrix, timed inside each of the K whole-path steps
-    fb_ms_per_step = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    fb_ms_per_step = sum(m[0].elapsed_time(m[PASSES.index("bwd") + 1]) for m in marks) / args.steps
+    # each pass inside the timed steps, per launch (the passes below time each pass on its own,
+    # one kernel launched over and over)
+    in_step_us = {p: round(sum(m[i].elapsed_time(m[i + 1]) for m in marks) / args.steps * 1e3 / len(mats), 2)
+                  for i, p in enumerate(PASSES)}
 
     # per-kernel timing: each pass over the seven matrices, HIP events on the launch stream
     passes = {}
@@ -862,6 +868,7 @@ def main():
         "fwd_bwd": fwd_bwd,
         "fwd_bwd_pack": fwd_bwd_pack,
         "passes": passes,
+        "passes_in_step_avg_launch_us": in_step_us,
         "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
