@@ -155,7 +155,8 @@ def backward_check(gpu, ref, y, d, c, tol, dy=None, n=None, m=None, dd=None):
         + c y_k (dd_k + sum_i y_i dd_i)                        an error of d itself (optional),
         + e c y_k (|d_k| + sum_i y_i |d_i|)                    rounding of the sums over N kept
     products, the K-term dot product with y, c = fl(kappa / tau) from fp32 kappa and tau, and
-    the last products: e = (N + K + 12) u."""
+    the last products: e = (N + K + 12) u.  Plus fp32's subnormal spacing: an absolute
+    2^-147 (1 + max |d|)."""
     gpu = np.asarray(gpu, np.float64)
     ad = np.abs(d)
     sy = (y * ad).sum(-1, keepdims=True)
@@ -169,6 +170,11 @@ def backward_check(gpu, ref, y, d, c, tol, dy=None, n=None, m=None, dd=None):
             derived = derived + c * y * (dd + (y * dd).sum(-1, keepdims=True))
         bound = np.maximum(bound, derived)
     floor = c * 1e-36 * ad.max(-1, keepdims=True)  # probabilities near the fp32 underflow
+    # fp32 itself: below 2^-126 its values are multiples of 2^-149, so each product of the
+    # kernel's last steps (c / S, times e_k, times d_k - s) may be off by 2^-150 absolute there,
+    # scaled by the factors that follow it (at most |d_k| + |s| <= 2 max |d|); a gradient below
+    # 2^-149 (a tiny kappa / tau) can only come out as 0 or 2^-149
+    floor = floor + 2.0**-147 * (1.0 + ad.max(-1, keepdims=True))
     return _verdict(_diff(gpu, ref), bound + floor)
 
 

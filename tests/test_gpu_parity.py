@@ -81,9 +81,11 @@ def test_gumbel_transform_over_all_2_23_uniforms():
 # ---------------------------------------------------------------------------------------------
 # soft mask, forward, backward
 
-# (kappa, tau): the annealing schedule's ends (100, 4) and (500, 0.05), and points between
+# (kappa, tau): the annealing schedule's ends (100, 4) and (500, 0.05), points between, and two
+# settings far outside it that the entry points also accept: nearly hard samples (2000, 0.002:
+# the noise exponent's fp32 rounding is amplified 500 times) and nearly uniform ones (0.5, 50)
 SAMPLES = [(100.0, 4.0), (100.0, 1.0), (1.0, 1.0), (0.0, 2.0), (30.0, 0.5), (5.0, 0.1), (3.0, 0.05),
-           (500.0, 0.05)]
+           (500.0, 0.05), (2000.0, 0.002), (0.5, 50.0)]
 
 
 @pytest.mark.parametrize("n,m", SUPPORTED)

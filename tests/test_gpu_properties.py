@@ -1,6 +1,6 @@
 """GPU property tests: for every N:M pattern hypothesis draws the shape (rows, groups per row), the
-weight type and scale, the logit scale, (kappa, tau) across the annealing range, and the seed and
-offset over their whole 64-bit ranges; every pass of the path (forward, backward, harden+pack,
+weight type and scale, the logit scale, (kappa, tau) across the annealing range and far outside it
+(kappa up to 5000, tau from 0.001 to 100), and the seed and offset over their whole 64-bit ranges; every pass of the path (forward, backward, harden+pack,
 unpack, the monitored forward) runs through the C ABI and is compared with the oracle:
   * forward and backward within the larger of the stated 1e-5 relative bound and the derived
     fp32 bound (tests/parity.py), as the fixed parity tests;
@@ -47,8 +47,8 @@ PARAMS = st.fixed_dictionaries({
     "bf16": st.booleans(),
     "w_std": st.sampled_from([0.02, 0.5, 2.0]),
     "l_std": st.sampled_from([0.05, 1.0, 3.0]),
-    "kappa": st.one_of(st.sampled_from([0.0, 100.0, 500.0]), st.floats(0.0, 500.0)),
-    "tau": st.one_of(st.sampled_from([0.05, 4.0]), st.floats(0.05, 4.0)),
+    "kappa": st.one_of(st.sampled_from([0.0, 100.0, 500.0]), st.floats(0.0, 500.0), st.floats(500.0, 5000.0)),
+    "tau": st.one_of(st.sampled_from([0.05, 4.0]), st.floats(0.05, 4.0), st.floats(0.001, 0.05), st.floats(4.0, 100.0)),
     "seed": WIDE,
     "offset": WIDE,
     "data": st.integers(0, 2**31 - 1),
