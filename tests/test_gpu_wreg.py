@@ -1,12 +1,15 @@
 """GPU parity of the backward with the weight regulariser (nm_mask_backward_wreg) against the
 oracle: every supported n:m, both weight types, ragged shapes, with and without a task
-gradient, over sample parameters, at the full size of LLaMA-7B-shaped matrices, and through the
-autograd function.  Every call goes through the C ABI."""
+gradient, over sample parameters, over drawn shapes, parameters and lambdas (hypothesis,
+derandomized), at the full size of LLaMA-7B-shaped matrices, and through the autograd
+function.  Every call goes through the C ABI."""
 import sys
 
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
 
 import nm_synth
 import oracle
@@ -112,3 +115,38 @@ def test_backward_wreg_llama7b_matrix_sampled_rows(i, with_task):
         a = a + (G.float() * w.float()).abs().view(-1, m).sum(1)
     s = dl.view(-1, dl.shape[-1]).double().sum(1).abs()
     assert bool((s <= 1e-5 * (kappa / tau) * a.double() + 1e-30).all())
+
+
+WREG = st.fixed_dictionaries({
+    "rows": st.integers(1, 24),
+    "gpr": st.integers(1, 48),
+    "bf16": st.booleans(),
+    "w_std": st.sampled_from([0.02, 0.5, 2.0]),
+    "kappa": st.one_of(st.sampled_from([0.0, 100.0, 500.0]), st.floats(0.0, 2000.0)),
+    "tau": st.one_of(st.sampled_from([0.05, 4.0]), st.floats(0.002, 50.0)),
+    "lam": st.one_of(st.sampled_from([0.0, 1e-4, -3.0]), st.floats(-10.0, 10.0)),
+    "with_task": st.booleans(),
+    "seed": st.integers(0, 2**64 - 1),
+    "offset": st.integers(0, 2**64 - 1),
+    "data": st.integers(0, 2**31 - 1),
+})
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (3, 4), (2, 8), (4, 8), (7, 8)])
+@settings(max_examples=10, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(p=WREG)
+def test_backward_wreg_properties(n, m, p):
+    """Drawn shapes, weight types and scales, (kappa, tau), lambda (zero, tiny, negative), with
+    and without a task gradient, over the whole 64-bit seed and offset ranges."""
+    f32 = lambda x: float(np.float32(x))  # noqa: E731  the values the C ABI carries
+    kappa, tau, lam = f32(p["kappa"]), f32(p["tau"]), f32(p["lam"])
+    _say("wreg props", n, m, p["rows"], p["gpr"], p["bf16"], kappa, tau, lam, p["with_task"], p["seed"],
+         p["offset"], p["data"])
+    wtype = torch.bfloat16 if p["bf16"] else torch.float32
+    w, L, G = nm_synth.matrix_inputs(p["rows"], p["gpr"] * m, n, m, wtype, p["w_std"], p["data"])
+    G = G if p["with_task"] else None
+    got = to_f64(S.nm_mask_backward_wreg(w.to(DEV), L.to(DEV), None if G is None else G.to(DEV), n, m, kappa, tau,
+                                         p["seed"], p["offset"], lam))
+    rel, bad = _check(got, w, L, G, n, m, kappa, tau, p["seed"], p["offset"], lam, TOL_FP32)
+    assert bad == 0, f"{bad} over the bound, worst {rel}"
