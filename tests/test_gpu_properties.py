@@ -7,7 +7,9 @@ unpack, the monitored forward) runs through the C ABI and is compared with the o
   * packed values, index words, hard indices and the unpacked weights bit for bit;
   * the monitored forward's sampled candidates equal the oracle's except on fp32 near-ties,
     where the choice must be among the tied ones, its L1 sum is exact for its samples and its
-    max-probability sum within 1e-5.
+    max-probability sum within 1e-5;
+  * the magnitude prior (tied magnitudes, NaN, infinities and signed zeros at drawn places) and
+    the one-call forward + pack, bit for bit.
 The draws are derandomized (a fixed sequence, no example database), so a failure reproduces by
 running the test again; each example prints its parameters before its GPU calls."""
 import sys
@@ -155,3 +157,78 @@ def test_sparse_product_is_exact_on_small_integers(p):
     want = torch.from_numpy(ref).to(torch.float32).to(ytype)
     tb = torch.int16 if p["bf16_out"] else torch.int32
     assert torch.equal(y.cpu().view(tb), want.view(tb))
+
+
+PRIOR = st.fixed_dictionaries({
+    "rows": st.integers(1, 40),
+    "gpr": st.integers(1, 72),
+    "bf16": st.booleans(),
+    "ints": st.booleans(),  # small-integer weights: many tied magnitudes
+    "alpha": st.one_of(st.sampled_from([0.0, 3.0, -2.75]), st.floats(-1e6, 1e6)),
+    "specials": st.lists(st.tuples(st.integers(0, 2**31 - 1),
+                                   st.sampled_from([float("nan"), float("inf"), float("-inf"), 0.0, -0.0])),
+                         max_size=6),
+    "data": st.integers(0, 2**31 - 1),
+})
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@SETTINGS
+@given(p=PRIOR)
+def test_prior_init_matches_the_oracle(n, m, p):
+    """The magnitude prior over drawn shapes, types and alphas, with tied magnitudes (small
+    integers) and NaN, infinities and signed zeros at drawn places: logits and prior indices
+    bit for bit."""
+    rows, gpr = p["rows"], p["gpr"]
+    alpha = _f32(p["alpha"])
+    _say("props prior", n, m, rows, gpr, p["bf16"], p["ints"], alpha, len(p["specials"]), p["data"])
+    wtype = torch.bfloat16 if p["bf16"] else torch.float32
+    if p["ints"]:
+        w = nm_synth.small_integers((rows, gpr * m), 3, p["data"], dtype=wtype)
+    else:
+        w = nm_synth.normal((rows, gpr * m), 0.02, p["data"], wtype)
+    flat = w.view(-1)
+    for where, value in p["specials"]:
+        flat[where % flat.numel()] = value
+    logits, idx = S.nm_prior_init(w.to(DEV), n, m, alpha, with_idx=True)
+    rl, ri = oracle.prior_init(w, n, m, alpha=alpha)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(logits.cpu().numpy().view(np.uint32), rl.view(np.uint32))
+
+
+FWD_PACK = st.fixed_dictionaries({
+    "rows": st.integers(1, 40),
+    "gpr": st.one_of(st.integers(1, 8).map(lambda v: 8 * v), st.integers(1, 70)),
+    "bf16": st.booleans(),
+    "kappa": st.one_of(st.sampled_from([0.0, 100.0, 500.0]), st.floats(0.0, 500.0)),
+    "tau": st.one_of(st.sampled_from([0.05, 4.0]), st.floats(0.05, 4.0)),
+    "with_hard": st.booleans(),
+    "seed": WIDE,
+    "offset": WIDE,
+    "data": st.integers(0, 2**31 - 1),
+})
+
+
+@SETTINGS
+@given(p=FWD_PACK)
+def test_forward_pack_equals_the_two_calls(p):
+    """The one-call forward + pack at 2:4 over drawn shapes (the one-pass kernel where cols / 4
+    is a multiple of 8, the two calls elsewhere): its outputs equal nm_mask_forward's and
+    nm_mask_harden_pack's bit for bit, and the packed form equals the oracle's."""
+    n, m, rows, gpr = 2, 4, p["rows"], p["gpr"]
+    kappa, tau = _f32(p["kappa"]), _f32(p["tau"])
+    _say("props fwd+pack", rows, gpr, p["bf16"], kappa, tau, p["with_hard"], p["seed"], p["offset"], p["data"])
+    w, L, _ = _inputs({**p, "w_std": 0.5, "l_std": 1.0}, n, m)
+    wd, Ld = w.to(DEV), L.to(DEV)
+    tb = torch.int16 if p["bf16"] else torch.int32
+    fused = S.nm_mask_forward_pack(wd, Ld, n, m, kappa, tau, p["seed"], p["offset"], with_hard=p["with_hard"])
+    assert torch.equal(fused[0].view(tb), S.nm_mask_forward(wd, Ld, n, m, kappa, tau, p["seed"], p["offset"]).view(tb))
+    sep = S.nm_mask_harden_pack(wd, Ld, n, m, with_hard=p["with_hard"])
+    assert torch.equal(fused[1].view(tb), sep[0].view(tb))
+    assert torch.equal(fused[2], sep[1])
+    rv, ri, rh = oracle.pack(w, L, n, m)
+    np.testing.assert_array_equal(fused[2].cpu().numpy().view(np.uint32), ri)
+    np.testing.assert_array_equal(fused[1].view(tb).cpu().numpy(), oracle._np(rv).view(np.int16 if p["bf16"] else np.int32))
+    if p["with_hard"]:
+        assert torch.equal(fused[3], sep[2])
+        np.testing.assert_array_equal(fused[3].cpu().numpy(), rh)
