@@ -43,8 +43,9 @@
  * m = 8); wtype NM_F32 or NM_BF16; all arithmetic is fp32.
  *
  * Ownership and execution: every pointer is device memory owned by the caller (a torch tensor,
- * a hipMalloc buffer).  The library allocates nothing, keeps no mutable global state and may be
- * called from several host threads.  Calls are asynchronous and ordered on `stream` (a
+ * a hipMalloc buffer).  An output must not overlap an input or another output.  The library
+ * allocates nothing, keeps no mutable global state other than the fixed device array of
+ * nm_mask_forward_monitor_static, and may be called from several host threads.  Calls are asynchronous and ordered on `stream` (a
  * hipStream_t passed as void*; NULL is the default stream).  The return value reports argument
  * validation and launch only; execution errors surface at the caller's next synchronisation.
  * Calls can be captured into a HIP graph on `stream` (none allocates, synchronises or records a
