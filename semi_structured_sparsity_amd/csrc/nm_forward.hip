@@ -354,29 +354,59 @@ __device__ __forceinline__ int prior_candidate(const float* w) {
     return kstar;
 }
 
+// A thread finds the prior candidates of its P consecutive groups from its weights (one
+// coalesced load) and leaves them in LDS (one byte per group).  After one barrier the block
+// writes its groups' logits as one contiguous span, consecutive threads on consecutive 16-byte
+// vectors, so no logit tile is staged.  A vector holds floats of at most two groups (K >= 4);
+// a float is alpha where it is its group's prior candidate, +0 elsewhere.  The group of a
+// thread's next vector follows from the previous one by a constant step, so there is one
+// division per thread.
 template <int N, int M, typename T>
 __global__ __launch_bounds__(kThreads) void k_prior(PriorArgs a) {
     using S = Sample<N, M>;
-    constexpr int K = S::K, P = S::P, PK = S::PK;
-    const ThreadGroup<N, M> tg = thread_group<N, M>();
-    const int64_t g0 = tg.g0;
-    if (g0 >= a.groups) return;
-    const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
-    const bool full = nvalid == P;
-
-    __shared__ typename StageTile<N, M>::vec tile[StageTile<N, M>::VEC];
-    const bool staged = block_full<N, M>(a.groups);  // uniform over the block
-    float w[P * M];
-    load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, full, nvalid * M, w);
-    float l[PK];
+    constexpr int K = S::K, P = S::P, BG = kThreads * P;
+    static_assert(K >= 4, "a 16-byte vector holds floats of at most two groups");
+    __shared__ uint8_t ks[BG];
+    const int64_t bg0 = (int64_t)blockIdx.x * BG;  // the block's first group (< groups)
+    const int64_t g0 = bg0 + (int64_t)threadIdx.x * P;
+    if (g0 < a.groups) {
+        const int nvalid = (int)(a.groups - g0 < P ? a.groups - g0 : P);
+        float w[P * M];
+        load_as_float<T, P * M>(reinterpret_cast<const typename T::storage*>(a.w) + g0 * M, nvalid == P,
+                                nvalid * M, w);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int kstar = prior_candidate<N, M>(w + p * M);
-#pragma unroll
-        for (int k = 0; k < K; ++k) l[p * K + k] = k == kstar ? a.alpha : 0.0f;
-        if (a.idx && p < nvalid) a.idx[g0 + p] = (uint8_t)kstar;
+        for (int p = 0; p < P; ++p) {
+            const int kstar = prior_candidate<N, M>(w + p * M);
+            ks[threadIdx.x * P + p] = (uint8_t)kstar;
+            if (a.idx && p < nvalid) a.idx[g0 + p] = (uint8_t)kstar;
+        }
     }
-    store_dlogits<N, M>(a.logits, g0, tg.q, full, nvalid, staged, tile, l);
+    __syncthreads();
+    const int ng = a.groups - bg0 < BG ? (int)(a.groups - bg0) : BG;
+    float* dst = a.logits + bg0 * K;  // 16-byte aligned: bg0 * K * 4 is a multiple of 1024
+    const int nf = ng * K, nv = nf / 4;
+    constexpr int STEP = 4 * kThreads, SQ = STEP / K, SR = STEP % K;
+    int f = 4 * (int)threadIdx.x, qa = f / K, ra = f - qa * K;  // group of the vector's first float
+    for (int v = threadIdx.x; v < nv; v += kThreads) {
+        const int qb = qa + (ra + 3 >= K ? 1 : 0);  // group of its last float
+        const int pa = qa * K + ks[qa], pb = qb * K + ks[qb];
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (f + e == pa || f + e == pb) ? a.alpha : 0.0f;
+        nt_store(dst + f, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                                     __float_as_uint(x[3])));
+        f += STEP;
+        qa += SQ;
+        ra += SR;
+        if (ra >= K) {
+            ra -= K;
+            ++qa;
+        }
+    }
+    for (int t = 4 * nv + (int)threadIdx.x; t < nf; t += kThreads) {  // a span that ends inside a vector
+        const int gt = t / K;
+        dst[t] = t == gt * K + ks[gt] ? a.alpha : 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -421,10 +451,30 @@ hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a,
     NM_DISPATCH(monitor_nmt, n, m, wtype, a, s);
 }
 
+// The prior writes K floats of logits per group from M weights: nearly a pure write stream, of a
+// contiguous span of kThreads * P * K * 4 bytes per block.  Measured on 4096 x 11008 (bf16),
+// the write rate falls once a CU holds more than about 200 KB of such spans at a time: 2:8
+// (28 KB per block) ran at 69.6% of 8 TB/s with 8 blocks per CU and 75.3% with 7, 4:8 (70 KB)
+// at 61.5% with 8 and 75.9% with 3, while 2:4 (12 KB) is best at 8.  So a block whose span
+// is large reserves LDS it does not use, which caps the blocks a CU holds at
+// 210 KB / span (160 KB of LDS per CU, reserved in whole KB).
+constexpr int kLdsPerCu = 160 * 1024;
+template <int N, int M>
+constexpr size_t prior_lds_reserve() {
+    constexpr int span = kThreads * Sample<N, M>::P * Sample<N, M>::K * 4;
+    constexpr int cap = 210 * 1024 / span;
+    if constexpr (cap >= 8) {
+        return 0;
+    } else {
+        constexpr int blocks = cap < 1 ? 1 : cap;
+        return (size_t)(kLdsPerCu / blocks / 1024 * 1024 - kThreads * Sample<N, M>::P);  // minus ks[]
+    }
+}
+
 template <int N, int M, typename T>
 static hipError_t prior_nmt(const PriorArgs& a, hipStream_t s) {
     const int64_t threads = (a.groups + Sample<N, M>::P - 1) / Sample<N, M>::P;
-    k_prior<N, M, T><<<grid_for(threads), kThreads, 0, s>>>(a);
+    k_prior<N, M, T><<<grid_for(threads), kThreads, prior_lds_reserve<N, M>(), s>>>(a);
     return hipGetLastError();
 }
 hipError_t launch_prior(int n, int m, int wtype, const PriorArgs& a, hipStream_t s) {

@@ -390,6 +390,56 @@ def test_model_catches_a_read_past_the_end():
         w.assert_in_bounds("old k_pack w")
 
 
+def model_prior(rows, cols, n, m, wb):
+    """k_prior (nm_forward.hip): a thread reads its P groups' weights and writes their prior
+    indices; each block writes its kThreads*P groups' logits as consecutive 16-byte vectors,
+    thread t taking vectors t, t + kThreads, ..., then the floats past the last whole vector one
+    by one.  Each vector's two groups come from the thread's running (group, remainder) pair,
+    which is checked against the division it replaces."""
+    K, P = sample_tiling(n, m)[:2]
+    groups = rows * (cols // m)
+    b = dict(w=Buf(rows * cols * wb), logits=Buf(groups * K * 4), idx=Buf(groups))
+    nblocks = grid_for(-(-groups // P))
+    t = np.arange(nblocks * THREADS, dtype=np.int64)
+    g0 = t * P
+    live = g0 < groups
+    nvalid = np.minimum(groups - g0[live], P)
+    b["w"].add(g0[live] * m * wb, nvalid * m * wb)
+    for p in range(P):
+        sel = p < nvalid
+        b["idx"].add(g0[live][sel] + p, 1)
+    bg0 = np.arange(nblocks, dtype=np.int64) * THREADS * P
+    ng = np.minimum(groups - bg0, THREADS * P)
+    nf = ng * K
+    nv = nf // 4
+    step, sq, sr = 4 * THREADS, (4 * THREADS) // K, (4 * THREADS) % K
+    for tid in range(THREADS):
+        f = 4 * tid
+        qa, ra = f // K, f - (f // K) * K
+        for v in range(tid, int(nv.max(initial=0)), THREADS):
+            assert qa == f // K and ra == f % K
+            sel = v < nv
+            qb = qa + (1 if ra + 3 >= K else 0)
+            assert (ng[sel] > qb).all()  # the ks entries read exist
+            b["logits"].add(bg0[sel] * K * 4 + 16 * v, 16)
+            f, qa, ra = f + step, qa + sq, ra + sr
+            if ra >= K:
+                ra, qa = ra - K, qa + 1
+        for x in range(tid, 4, THREADS):  # at most three tail floats per block
+            sel = 4 * nv + x < nf
+            b["logits"].add((bg0[sel] * K + 4 * nv[sel] + x) * 4, 4)
+    return b
+
+
+@pytest.mark.parametrize("n,m", SUPPORTED)
+@pytest.mark.parametrize("rows,cols_groups", [(1, 1), (3, 5), (37, 23), (2, 129), (512, 384)])
+def test_prior_index_maps(n, m, rows, cols_groups):
+    b = model_prior(rows, cols_groups * m, n, m, 2)
+    b["logits"].assert_written_once("k_prior logits")
+    b["idx"].assert_written_once("k_prior idx")
+    b["w"].assert_in_bounds("k_prior w")
+
+
 # ---------------------------------------------------------------------------------------------
 # The monitored forward's in-launch sums (k_forward_monitor and monitor_sums in nm_forward.hip;
 # workspace layout monitor_layout): blocks finish in any order; each adds (1 << 57) + its sum to
