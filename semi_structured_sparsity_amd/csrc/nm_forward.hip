@@ -454,10 +454,11 @@ hipError_t launch_forward_monitor(int n, int m, int wtype, const MonitorArgs& a,
 // The prior writes K floats of logits per group from M weights: nearly a pure write stream, of a
 // contiguous span of kThreads * P * K * 4 bytes per block.  Measured on 4096 x 11008 (bf16),
 // the write rate falls once a CU holds more than about 200 KB of such spans at a time: 2:8
-// (28 KB per block) ran at 69.6% of 8 TB/s with 8 blocks per CU and 75.3% with 7, 4:8 (70 KB)
-// at 61.5% with 8 and 75.9% with 3, while 2:4 (12 KB) is best at 8.  So a block whose span
-// is large reserves LDS it does not use, which caps the blocks a CU holds at
-// 210 KB / span (160 KB of LDS per CU, reserved in whole KB).
+// (28 KB per block) ran at 70.1% of 8 TB/s with 8 blocks per CU and 75.1% with 7, 4:8 (70 KB)
+// at 60.8% with 8, 71.1% with 4 and 75.6% with 3, while 2:4 (12 KB) is best at 8.  So a block
+// whose span is large reserves LDS it does not use, capping the blocks a CU holds (160 KB of
+// LDS per CU) at 210 KB / span; the reservation is rounded down to whole KB and leaves 1 KB
+// per block for the hardware's allocation granularity, so that the cap is met exactly.
 constexpr int kLdsPerCu = 160 * 1024;
 template <int N, int M>
 constexpr size_t prior_lds_reserve() {
@@ -467,7 +468,8 @@ constexpr size_t prior_lds_reserve() {
         return 0;
     } else {
         constexpr int blocks = cap < 1 ? 1 : cap;
-        return (size_t)(kLdsPerCu / blocks / 1024 * 1024 - kThreads * Sample<N, M>::P);  // minus ks[]
+        constexpr int total = (kLdsPerCu / blocks - 1024) / 1024 * 1024;
+        return (size_t)(total - kThreads * Sample<N, M>::P);  // less the static ks[]
     }
 }
 
