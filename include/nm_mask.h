@@ -280,8 +280,8 @@ int64_t nm_packed_value_elems(const nm_shape *shape);
 int64_t nm_index_words_per_row(const nm_shape *shape);
 /* rows * nm_index_words_per_row, or -1. */
 int64_t nm_packed_index_words(const nm_shape *shape);
-/* Workspace bytes nm_mask_forward_monitor needs for this shape (8 per block of its grid), or -1
- * for an invalid shape. */
+/* Workspace bytes nm_mask_forward_monitor needs for this shape (two 8-byte words per node of a
+ * 64-ary tree over the blocks of its grid, at least 16), or -1 for an invalid shape. */
 int64_t nm_monitor_workspace_bytes(const nm_shape *shape);
 /* Static description of a status code; any other value gives "unknown status".  The argument
  * is a plain int32_t so that a value outside the enumeration is well defined on both sides. */
