@@ -668,10 +668,13 @@ def workload_spmm(args):
         for mt in mats:
             mt["xd"] = nm_synth.normal((tk, mt["cols"]), 1.0, 11 + tk, torch.bfloat16, device=dev)
             mt["yd"] = torch.empty((tk, mt["rows"]), dtype=torch.bfloat16, device=dev)
+        # one workspace for the split k ranges of mid-size batches, allocated outside the timing
+        need = max(S.sparse_matmul_workspace_bytes(mt["rows"], mt["cols"], tk) for mt in mats)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
-        def sparse_d(r):
+        def sparse_d(r, split=True):
             for mt in mats:
-                S.nm_sparse_matmul(mt["values"], mt["indices"], mt["xd"], out=mt["yd"])
+                S.nm_sparse_matmul(mt["values"], mt["indices"], mt["xd"], out=mt["yd"], workspace=ws, split=split)
 
         def dense_d(r):
             for mt in mats:
@@ -684,6 +687,10 @@ def workload_spmm(args):
                                    "sparse_useful_TFLOPs": round(u / (ts * 1e-3) / 1e12, 1),
                                    "sparse_weight_GBps": round(1.125 * weights / (ts * 1e-3) / 1e9, 1),
                                    "speedup_vs_dense": round(td / ts, 3)}
+        if need > 0:  # the same batch on the tiles alone (nm_sparse_matmul, no k split)
+            tn = _elapsed_ms(lambda r: sparse_d(r, split=False), reps=reps)
+            batches[f"{tk}_tokens"]["sparse_no_split_ms_per_layer"] = round(tn, 4)
+            batches[f"{tk}_tokens"]["split_speedup"] = round(tn / ts, 3)
     res["batches"] = batches
     return {"metric": "2:4 sparse x dense product on the packed weights vs dense bf16 GEMM", "unit": "TFLOP/s",
             "config": {"workload": "LLaMA-2-7B-shaped layer (7 matrices) packed 2:4, X 4096 tokens bf16, "

@@ -269,6 +269,36 @@ nm_status nm_prior_init(const nm_shape *shape, float alpha, const void *w, float
 nm_status nm_sparse_matmul(const nm_shape *w_shape, const void *values, const uint32_t *indices,
                            const void *x, int64_t tokens, void *y, int32_t ytype, void *stream);
 
+/* nm_sparse_matmul with a caller-provided workspace, which lets the product split each tile's k
+ * range into 2, 4 or 8 parts run by separate blocks where that is estimated faster (batches too
+ * small to give every compute unit enough tiles, long k): each part's fp32 sums go to the
+ * workspace, and a second kernel adds the parts in part order and rounds once to ytype
+ * (deterministic; the sum order differs from an unsplit product's, so results may differ from
+ * nm_sparse_matmul's by rounding).  Same result otherwise.
+ *   workspace        device memory, 16-byte aligned, of at least
+ *                    nm_sparse_matmul_workspace_bytes(w_shape, tokens) bytes (may be NULL when
+ *                    that is 0); its contents on entry do not matter and are left unspecified.
+ *                    Calls whose executions overlap must not share one.
+ *   workspace_bytes  its size (NM_EINVAL if short)
+ *   other arguments  as nm_sparse_matmul */
+nm_status nm_sparse_matmul_ws(const nm_shape *w_shape, const void *values, const uint32_t *indices,
+                              const void *x, int64_t tokens, void *y, int32_t ytype, void *workspace,
+                              int64_t workspace_bytes, void *stream);
+/* Workspace bytes nm_sparse_matmul_ws needs for these sizes on the calling thread's current
+ * device (whose compute-unit count the plan depends on; 256 if it cannot be asked): 0 when
+ * the product is not split, else 4 * parts * tokens * out; -1 for sizes nm_sparse_matmul
+ * rejects. */
+int64_t nm_sparse_matmul_workspace_bytes(const nm_shape *w_shape, int64_t tokens);
+/* The kernel these sizes run on, on the calling thread's current device (host only, no device
+ * work): *tile = 0 for the row-streaming kernel (1 to 4 tokens whose X fits in 48 KB), 16 for
+ * the kernel of 16-row blocks, 64, 128 or 256 for the tiles of that many W rows x tokens per
+ * block; *parts = the parts the k range is split into (1 unless with_workspace is non-zero, as
+ * for nm_sparse_matmul_ws).  The choice is the cheapest under a cost model of the candidates
+ * fitted to MI355X measurements.  Empty products give *tile = -1, *parts = 0.  NM_EINVAL for
+ * NULL outputs, otherwise the size checks of nm_sparse_matmul. */
+nm_status nm_sparse_matmul_plan(const nm_shape *w_shape, int64_t tokens, int32_t with_workspace, int32_t *tile,
+                                int32_t *parts);
+
 /* ---- host-only helpers (no device work, no HIP call) ---------------------------------- */
 /* K = C(m, n) for a supported (n, m), else -1. */
 int32_t nm_num_candidates(int32_t n, int32_t m);

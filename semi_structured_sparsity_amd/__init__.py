@@ -70,6 +70,9 @@ _SIGNATURES = {
     "nm_mask_forward_monitor_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nm_monitor_workspace_bytes": (ctypes.c_int64, [_P]),
     "nm_sparse_matmul": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, _P]),
+    "nm_sparse_matmul_ws": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, _P, ctypes.c_int64, _P]),
+    "nm_sparse_matmul_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int64]),
+    "nm_sparse_matmul_plan": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
     "nm_num_candidates": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nm_candidate_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P]),
     "nm_packed_value_elems": (ctypes.c_int64, [_P]),
@@ -384,10 +387,30 @@ def nm_prior_init(w, n, m, alpha, with_idx=False, out=None):
     return (logits, idx) if with_idx else logits
 
 
-def nm_sparse_matmul(values, indices, x, out_dtype=torch.bfloat16, out=None):
+def sparse_matmul_workspace_bytes(out, inn, tokens):
+    """Workspace bytes nm_sparse_matmul needs for W [out, inn] and `tokens` tokens on the current
+    device (0 when the product does not split its k range)."""
+    return lib().nm_sparse_matmul_workspace_bytes(ctypes.byref(_shape(out, inn, 2, 4, NM_BF16)), int(tokens))
+
+
+def sparse_matmul_plan(out, inn, tokens, split=True):
+    """(tile, parts) nm_sparse_matmul runs W [out, inn] at `tokens` tokens with on the current
+    device: tile 0 row streaming, 16 the 16-row kernel, 64/128/256 the tiles; parts of the k
+    range (1 without split); (-1, 0) for an empty product."""
+    tile, parts = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().nm_sparse_matmul_plan(ctypes.byref(_shape(out, inn, 2, 4, NM_BF16)), int(tokens), int(bool(split)),
+                                     ctypes.byref(tile), ctypes.byref(parts))
+    _check(st, "nm_sparse_matmul_plan")
+    return tile.value, parts.value
+
+
+def nm_sparse_matmul(values, indices, x, out_dtype=torch.bfloat16, out=None, workspace=None, split=True):
     """Y [tokens, out] = X [tokens, in] times the transpose of the 2:4 weights W [out, in] held in
     nm_mask_harden_pack's packed form (values [out, in/2] bf16, indices [out, in/32]), on the
-    sparse matrix cores ("Accelerating Sparse Deep Neural Networks" summary page, 3.1-3.2)."""
+    sparse matrix cores ("Accelerating Sparse Deep Neural Networks" summary page, 3.1-3.2).
+    With `split`, mid-size batches split the k range over a workspace (nm_sparse_matmul_ws):
+    `workspace`, a uint8 device tensor of at least sparse_matmul_workspace_bytes bytes, or one
+    allocated here; split=False calls nm_sparse_matmul, which never splits."""
     rows, half = values.shape
     tokens, cols = x.shape
     if cols != 2 * half:
@@ -395,10 +418,24 @@ def nm_sparse_matmul(values, indices, x, out_dtype=torch.bfloat16, out=None):
     sh = _shape(rows, cols, 2, 4, _wtype(values.dtype))
     ytype = _wtype(out_dtype)
     y = torch.empty((tokens, rows), dtype=out_dtype, device=x.device) if out is None else out
-    st = lib().nm_sparse_matmul(ctypes.byref(sh), _dev(values, "values"),
-                                _dev(indices, "indices", torch.int32, (rows, cols // 32)),
-                                _dev(x, "x", torch.bfloat16), tokens,
-                                _dev(y, "y", out_dtype, (tokens, rows)), ytype, _stream(x.device))
+    if not split:
+        st = lib().nm_sparse_matmul(ctypes.byref(sh), _dev(values, "values"),
+                                    _dev(indices, "indices", torch.int32, (rows, cols // 32)),
+                                    _dev(x, "x", torch.bfloat16), tokens,
+                                    _dev(y, "y", out_dtype, (tokens, rows)), ytype, _stream(x.device))
+        _check(st, "nm_sparse_matmul")
+        return y
+    need = lib().nm_sparse_matmul_workspace_bytes(ctypes.byref(sh), tokens)
+    if need < 0:
+        raise NMError(NM_EUNSUPPORTED, "nm_sparse_matmul")
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws = None if need == 0 else _dev(workspace, "workspace", torch.uint8)
+    st = lib().nm_sparse_matmul_ws(ctypes.byref(sh), _dev(values, "values"),
+                                   _dev(indices, "indices", torch.int32, (rows, cols // 32)),
+                                   _dev(x, "x", torch.bfloat16), tokens,
+                                   _dev(y, "y", out_dtype, (tokens, rows)), ytype, ws,
+                                   0 if workspace is None else workspace.numel(), _stream(x.device))
     _check(st, "nm_sparse_matmul")
     return y
 
@@ -488,6 +525,8 @@ def packed_bytes(rows, cols, n, m, elem_bytes):
 __all__ = ["nm_mask_forward", "nm_mask_backward", "nm_mask_backward_wreg", "nm_mask_harden_pack",
            "nm_mask_forward_pack", "nm_unpack",
            "nm_prior_init", "nm_mask_forward_monitor", "monitor_workspace_bytes", "nm_debug_noise",
-           "nm_debug_copy", "nm_sparse_matmul", "nm_debug_gumbel_log2", "nm_debug_soft_mask", "mask", "NMMask",
+           "nm_debug_copy", "nm_sparse_matmul", "sparse_matmul_workspace_bytes", "sparse_matmul_plan",
+           "nm_debug_gumbel_log2",
+           "nm_debug_soft_mask", "mask", "NMMask",
            "num_candidates", "candidate_table", "index_words_per_row", "packed_bytes", "lib",
            "NMError", "EXPORTS", "library_path"]

@@ -394,24 +394,89 @@ nm_status nm_prior_init(const nm_shape* shape, float alpha, const void* w, float
     return launched(nm::launch_prior(shape->n, shape->m, shape->wtype, a, (hipStream_t)stream));
 }
 
-nm_status nm_sparse_matmul(const nm_shape* w_shape, const void* values, const uint32_t* indices,
-                           const void* x, int64_t tokens, void* y, int32_t ytype, void* stream) {
+namespace {
+
+// Size checks of the product without pointers: NM_OK and *empty when nothing is to be done.
+nm_status spmm_sizes(const nm_shape* w_shape, int64_t tokens, bool* empty) {
     int64_t groups;
     int32_t K;
-    nm_status st = check_shape(w_shape, &groups, &K);
+    const nm_status st = check_shape(w_shape, &groups, &K);
     if (st != NM_OK) return st;
-    if (tokens < 0 || (ytype != NM_F32 && ytype != NM_BF16)) return NM_EINVAL;
+    if (tokens < 0) return NM_EINVAL;
     if (w_shape->n != 2 || w_shape->m != 4 || w_shape->wtype != NM_BF16) return NM_EUNSUPPORTED;
     const int64_t out = w_shape->rows, in = w_shape->cols;
-    if (out == 0 || tokens == 0) return NM_OK;
+    *empty = out == 0 || tokens == 0;
+    if (*empty) return NM_OK;
     if (in == 0 || in % 64 != 0 || out % 4 != 0) return NM_EUNSUPPORTED;
     if (tokens > INT64_MAX / 4 / (in > out ? in : out)) return NM_EINVAL;
+    return NM_OK;
+}
+
+// Checks of the product's sizes and pointers shared by its two entry points; on success *a is
+// filled (and the call launches nothing if *empty).
+nm_status spmm_args(const nm_shape* w_shape, const void* values, const uint32_t* indices, const void* x,
+                    int64_t tokens, void* y, int32_t ytype, nm::SpmmArgs* a, bool* empty) {
+    nm_status st = spmm_sizes(w_shape, tokens, empty);
+    if (st != NM_OK) return st;
+    if (ytype != NM_F32 && ytype != NM_BF16) return NM_EINVAL;
+    if (*empty) return NM_OK;
+    const int64_t out = w_shape->rows, in = w_shape->cols;
     if (((out + 255) / 256 + 8) * ((tokens + 255) / 256 + 4) > (int64_t)INT32_MAX) return NM_EINVAL;  // one block per tile
     if (!values || !indices || !x || !y) return NM_EINVAL;
     if (!aligned16(values) || !aligned16(indices) || !aligned16(x) || !aligned16(y)) return NM_EALIGN;
-    nm::SpmmArgs a{static_cast<const uint16_t*>(values), indices, static_cast<const uint16_t*>(x), y,
-                   out, in, tokens, in / 2, in / 32, in, out, ytype == NM_F32 ? 0 : 1};
-    return launched(nm::launch_spmm24(a, (hipStream_t)stream));
+    *a = nm::SpmmArgs{static_cast<const uint16_t*>(values), indices, static_cast<const uint16_t*>(x), y,
+                      out, in, tokens, in / 2, in / 32, in, out, ytype == NM_F32 ? 0 : 1};
+    return NM_OK;
+}
+
+}  // namespace
+
+nm_status nm_sparse_matmul(const nm_shape* w_shape, const void* values, const uint32_t* indices,
+                           const void* x, int64_t tokens, void* y, int32_t ytype, void* stream) {
+    nm::SpmmArgs a;
+    bool empty = false;
+    const nm_status st = spmm_args(w_shape, values, indices, x, tokens, y, ytype, &a, &empty);
+    if (st != NM_OK || empty) return st;
+    return launched(nm::launch_spmm24(a, nullptr, 0, (hipStream_t)stream));
+}
+
+int64_t nm_sparse_matmul_workspace_bytes(const nm_shape* w_shape, int64_t tokens) {
+    bool empty = false;
+    if (spmm_sizes(w_shape, tokens, &empty) != NM_OK) return -1;
+    return empty ? 0 : nm::spmm_workspace_bytes(w_shape->rows, w_shape->cols, tokens);
+}
+
+nm_status nm_sparse_matmul_plan(const nm_shape* w_shape, int64_t tokens, int32_t with_workspace, int32_t* tile,
+                                int32_t* parts) {
+    if (!tile || !parts) return NM_EINVAL;
+    bool empty = false;
+    const nm_status st = spmm_sizes(w_shape, tokens, &empty);
+    if (st != NM_OK) return st;
+    if (empty) {
+        *tile = -1;
+        *parts = 0;
+        return NM_OK;
+    }
+    const nm::SpmmPlan pl = nm::spmm_plan(w_shape->rows, w_shape->cols, tokens, nm::spmm_cus(), with_workspace != 0);
+    *tile = pl.tile;
+    *parts = pl.parts;
+    return NM_OK;
+}
+
+nm_status nm_sparse_matmul_ws(const nm_shape* w_shape, const void* values, const uint32_t* indices,
+                              const void* x, int64_t tokens, void* y, int32_t ytype, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+    nm::SpmmArgs a;
+    bool empty = false;
+    const nm_status st = spmm_args(w_shape, values, indices, x, tokens, y, ytype, &a, &empty);
+    if (st != NM_OK || empty) return st;
+    const int64_t need = nm::spmm_workspace_bytes(a.out, a.in, tokens);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return NM_EINVAL;
+        if (!aligned16(workspace)) return NM_EALIGN;
+    }
+    return launched(nm::launch_spmm24(a, need > 0 ? static_cast<float*>(workspace) : nullptr, workspace_bytes,
+                                      (hipStream_t)stream));
 }
 
 nm_status nm_debug_noise(const nm_shape* shape, const nm_sample* sample, uint32_t* words, void* stream) {

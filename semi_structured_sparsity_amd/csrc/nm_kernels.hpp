@@ -119,7 +119,17 @@ struct SpmmArgs {
     int32_t ytype;
 };
 
-hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s);
+// Product plan: the kernel (tile 0: row streaming, 1-4 tokens; 16: the 16-row kernel; 64, 128
+// or 256: the tile of W rows x tokens per block) and the parts its k range is split into.
+struct SpmmPlan {
+    int tile, parts;
+};
+SpmmPlan spmm_plan(int64_t out, int64_t in, int64_t tokens, int cus, bool allow_split);
+int spmm_cus();  // compute units of the current device (256 if it cannot be asked)
+// fp32 workspace the product needs on the current device: 4 * parts * tokens * out, or 0
+int64_t spmm_workspace_bytes(int64_t out, int64_t in, int64_t tokens);
+// ws may be null (no k split); otherwise ws_bytes of 16-byte aligned device memory
+hipError_t launch_spmm24(const SpmmArgs& a, float* ws, int64_t ws_bytes, hipStream_t s);
 
 hipError_t launch_forward(int n, int m, int wtype, const FwdArgs& a, bool soft_mask, hipStream_t s);
 // 2:4 only, rows whose index bits fill whole words (cols/4 a multiple of 8)

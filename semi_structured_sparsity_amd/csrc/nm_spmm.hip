@@ -71,8 +71,12 @@ struct SpTile {
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_x(int t) { return (t ^ (t >> 3)) & 7; }
 
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
+// SPLIT > 1: the k range is split into SPLIT consecutive parts, part sp taken by blocks
+// sp * base .. sp * base + base - 1 (so a block's XCD, its id mod 8, is that of its tile), and
+// each part's fp32 tile goes to its own slice of `ws` ([SPLIT][tokens][out]) for
+// k_spmm_combine to add in part order.
+template <int WAVES, int SPLIT>
+__global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a, int64_t base, float* ws) {
     using TL = SpTile<WAVES>;
     constexpr int T = TL::T, TI = TL::TI, TJ = TL::TJ;
     constexpr int SP_ABYTES = TL::ABYTES, SP_XBYTES = TL::XBYTES, SP_STAGE = TL::STAGE;
@@ -82,7 +86,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
     const int64_t ntok = (a.tokens + T - 1) / T, nout = (a.out + T - 1) / T;
     const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
     const int64_t rt = (ntok + C - 1) / C, ro = (nout + R - 1) / R;   // region size in tiles
-    const int64_t x = blockIdx.x % 8, p = blockIdx.x / 8;
+    const int64_t bx = SPLIT > 1 ? (int64_t)blockIdx.x % base : (int64_t)blockIdx.x;
+    const int sp = SPLIT > 1 ? (int)((int64_t)blockIdx.x / base) : 0;
+    const int64_t x = bx % 8, p = bx / 8;
     const int64_t ot = (x / C) * ro + p / rt, tt = (x % C) * rt + p % rt;
     if (p >= ro * rt || ot >= nout || tt >= ntok) return;  // whole block
     const int64_t bo = ot * T, bt = tt * T;
@@ -104,13 +110,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
         return a.x + trow(s >> 3) * a.xstride + (((s & 7) ^ swz_x(s >> 3)) << 3);
     };
     const int sa = wv * 128 + lane, sx = wv * 256 + lane, si = wv * 64 + lane;
-    const uint16_t* ga0 = asrc(sa);
-    const uint16_t* ga1 = asrc(sa + 64);
-    const uint16_t* gx0 = xsrc(sx);
-    const uint16_t* gx1 = xsrc(sx + 64);
-    const uint16_t* gx2 = xsrc(sx + 128);
-    const uint16_t* gx3 = xsrc(sx + 192);
-    const uint32_t* gi = a.indices + orow(si >> 1) * a.istride + (si & 1);  // word slot = row * 2 + word
+    // this part's stages (64 dense k each): k0 .. k0 + nk - 1 (the whole row without a split)
+    const int64_t nall = a.in / 64, k0 = sp * nall / SPLIT, nk = (sp + 1) * nall / SPLIT - k0;
+    const uint16_t* ga0 = asrc(sa) + k0 * 32;
+    const uint16_t* ga1 = asrc(sa + 64) + k0 * 32;
+    const uint16_t* gx0 = xsrc(sx) + k0 * 64;
+    const uint16_t* gx1 = xsrc(sx + 64) + k0 * 64;
+    const uint16_t* gx2 = xsrc(sx + 128) + k0 * 64;
+    const uint16_t* gx3 = xsrc(sx + 192) + k0 * 64;
+    const uint32_t* gi = a.indices + orow(si >> 1) * a.istride + (si & 1) + k0 * 2;  // word slot = row * 2 + word
 
     // LDS destinations of this wave's pieces, relative to a stage
     const int da = wv * 2048, dx = SP_ABYTES + wv * 4096, di = SP_ABYTES + SP_XBYTES + wv * 256;
@@ -185,7 +193,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
     // no fence (a fence would wait for every outstanding DMA load, the later stages' too): each
     // wave waits explicitly for its own loads of stage s + 1 (7 per stage; those of stage s + 2
     // may stay in flight) and for its own LDS reads, then all waves meet.
-    const int64_t nk = a.in / 64;
     NM_SP_DMA(0, 0);
     if (nk > 1) NM_SP_DMA(1, 1);
     if (nk > 2) NM_SP_DMA(2, 2);
@@ -248,7 +255,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_spmm24(SpmmArgs a) {
                 const int64_t o = bo + wo + i * 32 + q * 8 + kg * 4;  // out % 4 == 0: o..o+3 all in or out
                 if (o >= a.out) continue;
                 const f32x16_t v = acc[i][j];
-                if (ytype == 0) {
+                if constexpr (SPLIT > 1) {
+                    *reinterpret_cast<float4*>(ws + ((int64_t)sp * a.tokens + t) * a.out + o) =
+                        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+                } else if (ytype == 0) {
                     *reinterpret_cast<float4*>(static_cast<float*>(yp) + t * ystride + o) =
                         make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
                 } else {
@@ -460,32 +470,150 @@ __global__ __launch_bounds__(512) void k_spmv24(SpmmArgs a, int64_t rows_per_blo
     }
 }
 
-template <int WAVES>
-static hipError_t launch_tile(const SpmmArgs& a, hipStream_t s) {
+// The parts of a split k range, added in part order: y[t, o] = ws[0][t][o] + ws[1][t][o] + ...,
+// rounded once to the output type.  One thread per four consecutive outputs.
+template <int SPLIT>
+__global__ __launch_bounds__(256) void k_spmm_combine(SpmmArgs a, const float* __restrict__ ws) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.tokens * (a.out / 4)) return;
+    const int64_t t = i / (a.out / 4), o = (i % (a.out / 4)) * 4;
+    const int64_t slice = a.tokens * a.out;
+    float4 v = *reinterpret_cast<const float4*>(ws + t * a.out + o);
+#pragma unroll
+    for (int sp = 1; sp < SPLIT; ++sp) {
+        const float4 u = *reinterpret_cast<const float4*>(ws + sp * slice + t * a.out + o);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+    }
+    if (a.ytype == 0) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.y) + t * a.ystride + o) = v;
+    } else {
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.x) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.z) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + t * a.ystride + o) = make_uint2(lo, hi);
+    }
+}
+
+template <int WAVES, int SPLIT>
+static hipError_t launch_tile(const SpmmArgs& a, float* ws, hipStream_t s) {
     using TL = SpTile<WAVES>;
     // the 150 KB of the largest tile are above the default dynamic LDS limit: allow the size
-    const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24<WAVES>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_spmm24<WAVES, SPLIT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::SMEM);
     if (e != hipSuccess) return e;
     const int64_t ntok = (a.tokens + TL::T - 1) / TL::T, nout = (a.out + TL::T - 1) / TL::T;
     const int64_t C = ntok % 4 == 0 ? 4 : (ntok % 2 == 0 ? 2 : 1), R = 8 / C;
     const int64_t grid = 8 * ((ntok + C - 1) / C) * ((nout + R - 1) / R);
-    k_spmm24<WAVES><<<dim3((unsigned)grid), 64 * WAVES, TL::SMEM, s>>>(a);
+    k_spmm24<WAVES, SPLIT><<<dim3((unsigned)(grid * SPLIT)), 64 * WAVES, TL::SMEM, s>>>(a, grid, ws);
+    if constexpr (SPLIT > 1) {
+        const int64_t quads = a.tokens * (a.out / 4);
+        k_spmm_combine<SPLIT><<<dim3((unsigned)((quads + 255) / 256)), 256, 0, s>>>(a, ws);
+    }
     return hipGetLastError();
 }
 
-// Up to this many tokens the skinny kernel runs; above it the tiles.
+// Up to this many tokens the 16-row kernel can run (its J = 4 variant holds 64 tokens).
 constexpr int64_t SP_SKINNY_MAX_TOKENS = 64;
 
 // Up to this many bf16 of X (all tokens, 48 KB) the row-streaming kernel stages X in LDS.
 constexpr int64_t SP_SPMV_MAX_X = 24576;
 
-hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
+int spmm_cus() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
         cus = 256;  // MI355X
-    if (a.tokens <= 4 && a.tokens * a.in <= SP_SPMV_MAX_X) {
+    }
+    return cus;
+}
+
+namespace {
+
+// Cost model of the tiled kernel, in microseconds.  A CU moves its blocks' stages from L2 into
+// LDS at about 35 KB per microsecond with one block resident, 10% faster per further resident
+// block (up to the blocks whose three stages fit in 160 KB of LDS: 1, 2 or 4 for the 256, 128
+// and 64 tiles), plus 4 us per round of resident blocks (filling the pipeline from HBM); the CU
+// with the most blocks sets the time.  A split adds the combine pass: 2 us plus 0.5 us per MB
+// of fp32 parts (written by the product and read back).  The constants were fitted to the
+// measured time of every (tile, parts) candidate on q/o (4096 x 4096), gate (11008 x 4096) and
+// down (4096 x 11008) weights at 5 to 4096 tokens, each call reading its weights from HBM (a
+// rotation of copies larger than the 256 MB last-level cache, as a model's layers run); on
+// seven other shapes (1024 x 4096 to 24576 x 6144, 5 to 2048 tokens) the plan it picks was
+// 1.1% slower than the fastest candidate on average and 12% at worst, where taking the largest
+// tile that fills the CUs was 47% slower on average.
+template <int WAVES>
+double tile_cost_us(int64_t out, int64_t in, int64_t tokens, int cus, int parts) {
+    using TL = SpTile<WAVES>;
+    constexpr int64_t occ = (160 * 1024) / (int64_t)TL::SMEM;
+    const int64_t blocks = ((out + TL::T - 1) / TL::T) * ((tokens + TL::T - 1) / TL::T) * parts;
+    const int64_t per_cu = (blocks + cus - 1) / cus;
+    const int64_t resident = per_cu < occ ? per_cu : occ;
+    const int64_t rounds = (per_cu + resident - 1) / resident;
+    const int64_t stages = (in / 64 + parts - 1) / parts;
+    const double stage_kb = (double)TL::STAGE / 1024.0;
+    double t = (double)rounds * (4.0 + (double)(resident * stages) * stage_kb / (35.0 * (1.0 + 0.1 * (double)(resident - 1))));
+    if (parts > 1) t += 2.0 + 0.5 * (double)parts * (double)tokens * (double)out * 4e-6;
+    return t;
+}
+
+// The 16-row kernel (blocks of 16 W rows reading W once, X from L2): 2.9 us plus a cost per
+// weight of the busiest CU that grows with the tokens; fitted to the same measurements.
+double skinny_cost_us(int64_t out, int64_t in, int64_t tokens, int cus) {
+    const int64_t blocks = (out + 15) / 16;
+    const double w = (double)((blocks + cus - 1) / cus) * 16.0 * (double)in * (double)cus * 1e-6;
+    return 2.945 + w * (0.2469 + 0.01329 * (double)tokens);
+}
+
+}  // namespace
+
+// The kernel of a product.  One to four tokens whose X fits in LDS stream rows (tile 0); else
+// every candidate is costed: the 16-row kernel (tile 16, up to 64 tokens) and the 256, 128 and
+// 64 tiles with the k range whole or split into 2, 4 or 8 parts (8 not for the 256 tile), the
+// parts only with a workspace and at least one 64-wide k stage each.  The cheapest is taken; on
+// a tie, the larger tile and the fewer parts.  Candidates whose grid would pass 2^31 - 1 blocks
+// are skipped (the entry points admit only sizes whose 256 tiles stay below it), and so are
+// splits of outputs above 2^41 elements (their workspace size and combine grid).
+SpmmPlan spmm_plan(int64_t out, int64_t in, int64_t tokens, int cus, bool allow_split) {
+    if (tokens <= 4 && tokens * in <= SP_SPMV_MAX_X) return {0, 1};
+    SpmmPlan best{256, 1};
+    double cost = 0.0;
+    bool have = false;
+    for (int tile : {256, 128, 64}) {
+        for (int parts : {1, 2, 4, 8}) {
+            if (parts > 1 && (!allow_split || in / 64 < parts || (tile == 256 && parts == 8))) continue;
+            if (parts > 1 && tokens > ((int64_t)1 << 41) / out) continue;
+            if (((out + tile - 1) / tile + 8) * ((tokens + tile - 1) / tile + 4) > (int64_t)INT32_MAX / parts) continue;
+            const double c = tile == 256   ? tile_cost_us<8>(out, in, tokens, cus, parts)
+                             : tile == 128 ? tile_cost_us<4>(out, in, tokens, cus, parts)
+                                           : tile_cost_us<2>(out, in, tokens, cus, parts);
+            if (!have || c < cost) {
+                best = {tile, parts};
+                cost = c;
+                have = true;
+            }
+        }
+    }
+    if (tokens <= SP_SKINNY_MAX_TOKENS && skinny_cost_us(out, in, tokens, cus) < cost) best = {16, 1};
+    return best;
+}
+
+int64_t spmm_workspace_bytes(int64_t out, int64_t in, int64_t tokens) {
+    const SpmmPlan pl = spmm_plan(out, in, tokens, spmm_cus(), true);
+    return pl.parts > 1 ? 4 * pl.parts * tokens * out : 0;
+}
+
+hipError_t launch_spmm24(const SpmmArgs& a, float* ws, int64_t ws_bytes, hipStream_t s) {
+    const int cus = spmm_cus();
+    // A split needs the caller's workspace; without it (or with too little) the best plan
+    // without one runs.
+    SpmmPlan pl = spmm_plan(a.out, a.in, a.tokens, cus, ws != nullptr);
+    if (pl.parts > 1 && ws_bytes < 4 * pl.parts * a.tokens * a.out) pl = spmm_plan(a.out, a.in, a.tokens, cus, false);
+    if (pl.tile == 0) {
         // about two blocks of eight waves per CU; every wave ends its row loop, then the block
         const int64_t target = 2 * (int64_t)cus;
         const int64_t rpb = (a.out + target - 1) / target;
@@ -499,7 +627,7 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
             k_spmv24<4><<<dim3((unsigned)grid), 512, smem, s>>>(a, rpb);
         return hipGetLastError();
     }
-    if (a.tokens <= SP_SKINNY_MAX_TOKENS) {
+    if (pl.tile == 16) {
         const unsigned gx = (unsigned)((a.out + 15) / 16);
         if (a.tokens <= 16)
             k_spmm24_skinny<1, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
@@ -509,15 +637,22 @@ hipError_t launch_spmm24(const SpmmArgs& a, hipStream_t s) {
             k_spmm24_skinny<4, 8, 4><<<dim3(gx, 1), 512, 0, s>>>(a);
         return hipGetLastError();
     }
-    // Tile size.  Each CU moves its blocks' stages from L2 into LDS at a roughly fixed rate, so a
-    // product takes about (bytes a CU stages) / (that rate): the largest tile that still gives
-    // every CU a block is taken (256 x 256, 128 x 128 or 64 x 64).  With 256 x 256 tiles only,
-    // mid-size batches would leave most CUs idle (16 blocks for 4096 W rows at 256 tokens).
     // Deeper pipelines (6 or 9 stages per block instead of 3) were measured no faster.
-    auto tiles = [&](int64_t t) { return ((a.out + t - 1) / t) * ((a.tokens + t - 1) / t); };
-    if (tiles(256) >= cus) return launch_tile<8>(a, s);
-    if (tiles(128) >= cus) return launch_tile<4>(a, s);
-    return launch_tile<2>(a, s);
+    if (pl.tile == 256) {
+        if (pl.parts == 2) return launch_tile<8, 2>(a, ws, s);
+        if (pl.parts == 4) return launch_tile<8, 4>(a, ws, s);
+        return launch_tile<8, 1>(a, nullptr, s);
+    }
+    if (pl.tile == 128) {
+        if (pl.parts == 2) return launch_tile<4, 2>(a, ws, s);
+        if (pl.parts == 4) return launch_tile<4, 4>(a, ws, s);
+        if (pl.parts == 8) return launch_tile<4, 8>(a, ws, s);
+        return launch_tile<4, 1>(a, nullptr, s);
+    }
+    if (pl.parts == 2) return launch_tile<2, 2>(a, ws, s);
+    if (pl.parts == 4) return launch_tile<2, 4>(a, ws, s);
+    if (pl.parts == 8) return launch_tile<2, 8>(a, ws, s);
+    return launch_tile<2, 1>(a, nullptr, s);
 }
 
 }  // namespace nm

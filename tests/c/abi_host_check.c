@@ -88,6 +88,20 @@ int main(void) {
     CHECK(nm_sparse_matmul(&w24_tall, fake, fake, fake, 1LL << 45, fake, NM_F32, NULL) == NM_EINVAL);
     nm_shape w24_odd = {4094, 4096, 2, 4, NM_BF16};
     CHECK(nm_sparse_matmul(&w24_odd, fake, fake, fake, 8, fake, NM_F32, NULL) == NM_EUNSUPPORTED);
+    CHECK(nm_sparse_matmul_workspace_bytes(&w24, INT64_MAX) == -1);
+    CHECK(nm_sparse_matmul_workspace_bytes(&w24_tall, 1LL << 45) == -1);  /* offsets past int64 */
+    CHECK(nm_sparse_matmul_workspace_bytes(&w24_odd, 8) == -1);
+    CHECK(nm_sparse_matmul_workspace_bytes(NULL, 8) == -1);
+    for (size_t i = 0; i < sizeof huge / sizeof huge[0]; ++i)
+        CHECK(nm_sparse_matmul_workspace_bytes(&huge[i], INT64_MAX) == -1);
+    CHECK(nm_sparse_matmul_ws(&w24, fake, fake, fake, INT64_MAX, fake, NM_F32, fake, 64, NULL) == NM_EINVAL);
+    CHECK(nm_sparse_matmul_ws(&w24_tall, fake, fake, fake, 1LL << 45, fake, NM_F32, fake, 64, NULL) == NM_EINVAL);
+    CHECK(nm_sparse_matmul_ws(&w24, fake, fake, fake, 64, fake, NM_F32, NULL, 0, NULL) == NM_EINVAL); /* split, no workspace */
+    int32_t tile = 0, parts = 0;
+    CHECK(nm_sparse_matmul_plan(&w24, 64, 1, &tile, &parts) == NM_OK && tile == 64 && parts == 4);
+    CHECK(nm_sparse_matmul_plan(&w24, 64, 1, NULL, &parts) == NM_EINVAL);
+    CHECK(nm_sparse_matmul_plan(&w24_odd, 64, 1, &tile, &parts) == NM_EUNSUPPORTED);
+    CHECK(nm_sparse_matmul_plan(&w24, INT64_MAX, 1, &tile, &parts) == NM_EINVAL);
     /* samples whose kappa*log2(e)/tau or 1/tau leave fp32's range, or are not numbers */
     const nm_sample bad_samples[] = {{3.0e38f, 1.0e-3f, 0, 0}, {1.0f, 1.0e-45f, 0, 0}, {1.0f, -1.0f, 0, 0},
                                      {-1.0f, 1.0f, 0, 0},      {INFINITY, 1.0f, 0, 0},   {NAN, 1.0f, 0, 0},

@@ -200,6 +200,62 @@ def test_sparse_matmul_is_validated_on_the_host():
     assert ok(_shape(rows=0, cols=64, n=2, m=4, wtype=1), y=None) == NM_OK
 
 
+# Plans of the product on 256 compute units (the count taken when no GPU can be asked, and
+# MI355X's): each is the candidate measured fastest for that shape on MI355X (graph replays of
+# every tile x parts candidate, the weights read from HBM at every call).
+PLANS = [
+    ((4096, 4096, 1), True, (0, 1)), ((4096, 11008, 4), True, (16, 1)), ((4096, 4096, 16), False, (16, 1)),
+    ((11008, 4096, 16), True, (64, 4)), ((4096, 11008, 16), True, (64, 8)), ((4096, 4096, 64), True, (64, 4)),
+    ((11008, 4096, 128), True, (128, 2)), ((4096, 11008, 128), True, (128, 8)), ((4096, 4096, 512), True, (128, 2)),
+    ((4096, 4096, 768), True, (128, 1)), ((11008, 4096, 1024), True, (256, 1)), ((4096, 11008, 1024), True, (256, 4)),
+    ((4096, 11008, 2048), True, (256, 2)), ((4096, 4096, 4096), True, (256, 1)), ((1024, 4096, 64), True, (64, 8)),
+    ((4096, 4096, 64), False, (16, 1)), ((4096, 11008, 2048), False, (128, 1)), ((4096, 4096, 256), True, (128, 4)),
+    ((4096, 4096, 16), True, (16, 1)),
+]
+
+
+@pytest.mark.parametrize("shape,split,plan", PLANS)
+def test_sparse_matmul_plan_and_workspace(shape, split, plan):
+    """Without a GPU the plan takes 256 compute units; the workspace is one fp32 [tokens, out]
+    slice per part of a split k range, none without a split."""
+    out, inn, tokens = shape
+    assert S.sparse_matmul_plan(out, inn, tokens, split=split) == plan
+    if split:
+        parts = plan[1]
+        assert S.sparse_matmul_workspace_bytes(out, inn, tokens) == (4 * parts * tokens * out if parts > 1 else 0)
+
+
+def test_sparse_matmul_plan_bounds():
+    """Parts never exceed k's 64-wide stages, no split without a workspace, and a huge product
+    still gets a plan whose grid fits (its 256 tiles: what the entry points admit)."""
+    for out, inn, tokens in [(4, 64, 100), (4, 128, 100), (260, 192, 300), (8, 24640, 1), (4, 512, 60_000_000_000)]:
+        tile, parts = S.sparse_matmul_plan(out, inn, tokens)
+        assert tile in (0, 16, 64, 128, 256) and parts in (1, 2, 4, 8) and parts <= inn // 64
+        assert S.sparse_matmul_plan(out, inn, tokens, split=False)[1] == 1
+    assert S.sparse_matmul_plan(4, 512, 60_000_000_000)[1] == 1          # no split of a 2^41+ output
+    assert S.sparse_matmul_plan(256, 64, 0) == (-1, 0)
+
+
+def test_sparse_matmul_ws_is_validated_on_the_host():
+    L = S.lib()
+    sh = _shape(rows=4096, cols=4096, n=2, m=4, wtype=1)
+    need = L.nm_sparse_matmul_workspace_bytes(sh, 64)
+    assert need == 4 * 4 * 64 * 4096                      # 64 tokens: 64 tiles in 4 parts
+    call = lambda ws, nbytes, tokens=64, shp=sh: L.nm_sparse_matmul_ws(shp, FAKE, FAKE, FAKE, tokens, FAKE, 1,
+                                                                        ws, nbytes, None)
+    assert call(None, 0) == NM_EINVAL                     # a split needs the workspace
+    assert call(FAKE, need - 16) == NM_EINVAL             # short
+    assert call(ODD, need) == NM_EALIGN
+    assert call(None, 0, tokens=-1) == NM_EINVAL
+    assert call(None, 0, tokens=0) == NM_OK               # empty: nothing to do, no workspace
+    assert call(None, 0, shp=_shape(rows=130, cols=64, n=2, m=4, wtype=1)) == NM_EUNSUPPORTED
+    assert L.nm_sparse_matmul_workspace_bytes(_shape(rows=130, cols=64, n=2, m=4, wtype=1), 256) == -1
+    assert L.nm_sparse_matmul_workspace_bytes(_shape(rows=256, cols=64, n=2, m=4, wtype=0), 256) == -1
+    assert L.nm_sparse_matmul_workspace_bytes(sh, -1) == -1
+    assert L.nm_sparse_matmul_workspace_bytes(sh, 0) == 0
+    assert L.nm_sparse_matmul_workspace_bytes(_shape(rows=0, cols=64, n=2, m=4, wtype=1), 256) == 0
+
+
 def test_unsupported_helpers():
     assert S.num_candidates(2, 6) == -1 and S.num_candidates(4, 4) == -1
     assert S.lib().nm_candidate_table(2, 6, None) == NM_EUNSUPPORTED
