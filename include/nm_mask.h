@@ -278,7 +278,8 @@ nm_status nm_sparse_matmul(const nm_shape *w_shape, const void *values, const ui
  *   workspace        device memory, 16-byte aligned, of at least
  *                    nm_sparse_matmul_workspace_bytes(w_shape, tokens) bytes (may be NULL when
  *                    that is 0); its contents on entry do not matter and are left unspecified.
- *                    Calls whose executions overlap must not share one.
+ *                    It must not overlap values, indices, x or y, and calls whose executions
+ *                    overlap must not share one.
  *   workspace_bytes  its size (NM_EINVAL if short)
  *   other arguments  as nm_sparse_matmul */
 nm_status nm_sparse_matmul_ws(const nm_shape *w_shape, const void *values, const uint32_t *indices,
