@@ -387,6 +387,22 @@ def nm_prior_init(w, n, m, alpha, with_idx=False, out=None):
     return (logits, idx) if with_idx else logits
 
 
+# Workspace sizes of the product by (device, out, in, weight type, tokens): the plan depends
+# only on these (and on the device's compute units), so the binding asks the library once.
+_SPMM_NEED = {}
+
+
+def _spmm_need(sh, device, tokens):
+    key = (device.index, sh.rows, sh.cols, sh.wtype, tokens)
+    need = _SPMM_NEED.get(key)
+    if need is None:
+        need = lib().nm_sparse_matmul_workspace_bytes(ctypes.byref(sh), tokens)
+        if len(_SPMM_NEED) > 4096:
+            _SPMM_NEED.clear()
+        _SPMM_NEED[key] = need
+    return need
+
+
 def sparse_matmul_workspace_bytes(out, inn, tokens):
     """Workspace bytes nm_sparse_matmul needs for W [out, inn] and `tokens` tokens on the current
     device (0 when the product does not split its k range)."""
@@ -425,7 +441,7 @@ def nm_sparse_matmul(values, indices, x, out_dtype=torch.bfloat16, out=None, wor
                                     _dev(y, "y", out_dtype, (tokens, rows)), ytype, _stream(x.device))
         _check(st, "nm_sparse_matmul")
         return y
-    need = lib().nm_sparse_matmul_workspace_bytes(ctypes.byref(sh), tokens)
+    need = _spmm_need(sh, x.device, tokens)
     if need < 0:
         raise NMError(NM_EUNSUPPORTED, "nm_sparse_matmul")
     if need > 0 and workspace is None:
