@@ -2,8 +2,8 @@
 function of the arguments, and each call's scratch is its caller's workspace), so the same calls
 issued alternately on two non-default streams, with nothing ordering one stream against the
 other, give the outputs of the same calls made one after another on the default stream, bit for
-bit; monitored forwards with one workspace per stream give the same samples and stats.  Every
-call goes through the C ABI."""
+bit; monitored forwards and split products with one workspace per stream give the same samples,
+stats and products.  Every call goes through the C ABI."""
 import sys
 
 import pytest
@@ -78,3 +78,33 @@ def test_monitored_forwards_on_two_streams_with_their_own_workspaces():
             assert torch.equal(got[1], ref[1]), f"rep {rep} matrix {i} samples"
             assert torch.equal(got[2], ref[2]), f"rep {rep} matrix {i} stats"
     assert not any(bool(s.any()) for s in spaces)  # every call left its workspace zero
+
+
+def test_split_products_on_two_streams():
+    """Products whose plans split k (LLaMA-7B-shaped weights at 64 to 256 tokens), issued
+    alternately on two streams: with one workspace per stream, given by the caller, and with the
+    binding's own per-call workspaces, every output equals that of the same call made alone."""
+    _say("streams spmm")
+    cases = [(4096, 4096, 64), (11008, 4096, 128), (4096, 11008, 256), (4096, 4096, 256)]
+    mats = []
+    for i, (out, inn, tokens) in enumerate(cases):
+        assert S.sparse_matmul_plan(out, inn, tokens)[1] > 1
+        w, L, _ = nm_synth.matrix_inputs(out, inn, 2, 4, torch.bfloat16, 0.02, 80 + i, with_grad=False, device=DEV)
+        values, indices = S.nm_mask_harden_pack(w, L, 2, 4)
+        x = nm_synth.normal((tokens, inn), 1.0, 90 + i, torch.bfloat16, device=DEV)
+        mats.append((values, indices, x))
+    refs = [S.nm_sparse_matmul(v, ix, x) for v, ix, x in mats]
+    torch.cuda.synchronize()
+    need = max(S.sparse_matmul_workspace_bytes(out, inn, tokens) for out, inn, tokens in cases)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    spaces = [torch.empty(need, dtype=torch.uint8, device=DEV) for _ in streams]
+    torch.cuda.synchronize()
+    for own in (True, False):
+        for rep in range(3):
+            outs = []
+            for i, (v, ix, x) in enumerate(mats):
+                with torch.cuda.stream(streams[i % 2]):
+                    outs.append(S.nm_sparse_matmul(v, ix, x, workspace=spaces[i % 2] if own else None))
+            torch.cuda.synchronize()
+            for i, (got, ref) in enumerate(zip(outs, refs)):
+                assert torch.equal(_bits(got), _bits(ref)), f"own workspace {own} rep {rep} product {i}"
