@@ -576,8 +576,9 @@ double skinny_cost_us(int64_t out, int64_t in, int64_t tokens, int cus) {
 // 64 tiles with the k range whole or split into 2, 4 or 8 parts (8 not for the 256 tile), the
 // parts only with a workspace and at least one 64-wide k stage each.  The cheapest is taken; on
 // a tie, the larger tile and the fewer parts.  Candidates whose grid would pass 2^31 - 1 blocks
-// are skipped (the entry points admit only sizes whose 256 tiles stay below it), and so are
-// splits of outputs above 2^41 elements (their workspace size and combine grid).
+// are skipped (the entry points admit only sizes whose 256 tiles stay below it; the 16-row
+// kernel has one block per 16 W rows), and so are splits of outputs above 2^41 elements (their
+// workspace size and combine grid).
 SpmmPlan spmm_plan(int64_t out, int64_t in, int64_t tokens, int cus, bool allow_split) {
     if (tokens <= 4 && tokens * in <= SP_SPMV_MAX_X) return {0, 1};
     SpmmPlan best{256, 1};
@@ -598,7 +599,9 @@ SpmmPlan spmm_plan(int64_t out, int64_t in, int64_t tokens, int cus, bool allow_
             }
         }
     }
-    if (tokens <= SP_SKINNY_MAX_TOKENS && skinny_cost_us(out, in, tokens, cus) < cost) best = {16, 1};
+    if (tokens <= SP_SKINNY_MAX_TOKENS && (out + 15) / 16 <= (int64_t)INT32_MAX &&
+        skinny_cost_us(out, in, tokens, cus) < cost)
+        best = {16, 1};
     return best;
 }
 

@@ -234,6 +234,11 @@ def test_sparse_matmul_plan_bounds():
         assert S.sparse_matmul_plan(out, inn, tokens, split=False)[1] == 1
     assert S.sparse_matmul_plan(4, 512, 60_000_000_000)[1] == 1          # no split of a 2^41+ output
     assert S.sparse_matmul_plan(256, 64, 0) == (-1, 0)
+    # the tallest weight the checks admit (2^35 - 16 rows of 64 columns) still gets a plan; the
+    # 16-row kernel's grid is then exactly 2^31 - 1 blocks
+    tall = (1 << 35) - 16
+    tile, _ = S.sparse_matmul_plan(tall, 64, 64)
+    assert tile != 16 or (tall + 15) // 16 <= 2**31 - 1
 
 
 def test_sparse_matmul_ws_is_validated_on_the_host():
