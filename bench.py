@@ -389,7 +389,9 @@ def workload_sweep32(args):
 
 
 def workload_general_nm(args):
-    """4096x11008 bf16, 1:4 / 2:8 / 4:8, kappa 100, tau 1: every pass timed on its own."""
+    """4096x11008 bf16, 1:4 / 2:8 / 4:8, kappa 100, tau 1: every pass timed on its own.  Each
+    pass cycles through copies of its inputs and outputs that together exceed 600 MB, so that
+    every call reads and writes HBM rather than the 256 MB last-level cache."""
     import torch
 
     import nm_synth
@@ -407,17 +409,30 @@ def workload_general_nm(args):
         idx = torch.empty((rows, wpr), dtype=torch.int32, device=dev)
         dense = torch.empty_like(w)
         bpw = bytes_per_weight(2, n, m, k)
-        calls = {"fwd": lambda r: S.nm_mask_forward(w, L, n, m, 100.0, 1.0, seed, r, out=out),
-                 "bwd": lambda r: S.nm_mask_backward(w, L, G, n, m, 100.0, 1.0, seed, r, out=dl),
-                 "harden_pack": lambda r: S.nm_mask_harden_pack(w, L, n, m, out=(values, idx, None)),
-                 "unpack": lambda r: S.nm_unpack(values, idx, cols, n, m, out=dense)}
+        S.nm_mask_harden_pack(w, L, n, m, out=(values, idx, None))  # unpack's input
+        base = {"fwd": (w, L, out), "bwd": (w, L, G, dl), "harden_pack": (w, L, values, idx),
+                "unpack": (values, idx, dense)}
         entry = {}
-        for p, fn in calls.items():
-            fn(0)
-            us = _elapsed_ms(fn, reps=args.kernel_reps) * 1e3
+        for p in ("fwd", "bwd", "harden_pack", "unpack"):
+            ncopy = -(-600_000_000 // int(bpw[p] * rows * cols))
+            sets = [base[p]] + [tuple(t.clone() for t in base[p]) for _ in range(ncopy - 1)]
+            if p == "fwd":
+                fn = lambda r: (lambda a: S.nm_mask_forward(a[0], a[1], n, m, 100.0, 1.0, seed, r, out=a[2]))(sets[r % ncopy])
+            elif p == "bwd":
+                fn = lambda r: (lambda a: S.nm_mask_backward(a[0], a[1], a[2], n, m, 100.0, 1.0, seed, r, out=a[3]))(sets[r % ncopy])
+            elif p == "harden_pack":
+                fn = lambda r: (lambda a: S.nm_mask_harden_pack(a[0], a[1], n, m, out=(a[2], a[3], None)))(sets[r % ncopy])
+            else:
+                fn = lambda r: (lambda a: S.nm_unpack(a[0], a[1], cols, n, m, out=a[2]))(sets[r % ncopy])
+            for r in range(ncopy):
+                fn(r)
+            us = _elapsed_ms(fn, reps=max(args.kernel_reps, 2 * ncopy)) * 1e3
             gbps = bpw[p] * rows * cols / (us * 1e-6) / 1e9
             entry[p] = {"avg_launch_us": round(us, 2), "bytes_per_weight": round(bpw[p], 4),
-                        "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+                        "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+                        "copies": ncopy}
+            del sets
+            torch.cuda.empty_cache()
         fb = entry["fwd"]["avg_launch_us"] + entry["bwd"]["avg_launch_us"]
         entry["fwd_bwd_weights_per_s"] = rows * cols / (fb * 1e-6)
         res[f"{n}:{m}"] = entry
